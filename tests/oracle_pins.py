@@ -1,0 +1,395 @@
+"""Pins of the float64 oracle to things other than itself.
+
+Each ``check_*`` function takes a loaded oracle build and raises
+AssertionError when the build disagrees with what the pages or the
+mathematics fix.  ``tests/test_oracle_pins.py`` runs them on the real build;
+``tests/test_oracle_mutations.py`` runs them on builds with planted mistakes
+and expects at least one to fail for every mistake.
+
+The brute-force definitions below are written independently of the oracle:
+no sort and no cumulative sum, just the order-free rule counted directly.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+import subprocess
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_examples.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _logits_of(case):
+    if "logits" in case:
+        return np.asarray(case["logits"], dtype=np.float32)
+    spec = case["logits_spec"]
+    if spec.startswith("peaked"):
+        return np.asarray([8.0, 3.0, 2.0, 1.0] + [0.0] * 96, dtype=np.float32)
+    if spec.startswith("sloped"):
+        return np.linspace(1.0, 0.0, 100).astype(np.float32)
+    raise ValueError(spec)
+
+
+def run_row(O, row, T, p, k=0, mp=0.0, seed=7, step=0, probs=True):
+    lg = np.asarray(row, dtype=np.float32)[None, :]
+    r, pr = O.sample(lg, [T], [p], [k], [mp], seed=seed, step=step, want_probs=probs)
+    return r[0], (pr[0] if probs else None)
+
+
+# --------------------------------------------------------------------------
+# Brute force from the definitions (independent of the oracle's code)
+# --------------------------------------------------------------------------
+def brute_row(x, T, p, k, mp):
+    """Order-free definitions, O(V^2), no sort.
+
+    Returns (keep mask, A (mass strictly above each token among survivors,
+    normalised), probs of the kept set) for T > 0 rows with a finite logit.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    fin = x > -np.inf
+    m = x[fin].max()
+    e = np.where(fin, np.exp(np.where(fin, x - m, 0.0) / T), 0.0)
+    prob = e / e.sum()
+    surv = fin.copy()
+    if mp > 0:
+        surv &= ~(prob < min(mp, 1.0) * prob.max())
+    if k > 0:
+        greater = ((x[None, :] > x[:, None]) & surv[None, :]).sum(axis=1)
+        surv &= greater < k
+    q = np.where(surv, e, 0.0)
+    q = q / q.sum()
+    A = ((x[None, :] > x[:, None]) * q[None, :]).sum(axis=1)
+    if p >= 1.0:
+        keep = surv.copy()
+    else:
+        keep = surv & (A < p)
+        top = x[surv].max()
+        keep |= surv & (x == top)  # the most probable level is always kept
+    ek = np.where(keep, e, 0.0)
+    return keep, A, ek / ek.sum()
+
+
+def exhaustive_keep(q, p):
+    """Keep set by exhaustive subset search (n <= 12): take the smallest
+    cardinality c of any subset whose mass reaches p (at least 1); the
+    heaviest subset of that size is the top-c tokens; keep every token at
+    least as probable as its lightest member (so ties share a fate)."""
+    n = len(q)
+    if p >= 1.0:
+        return np.ones(n, bool), None
+    best = None
+    for c in range(1, n + 1):
+        heaviest = None
+        for sub in itertools.combinations(range(n), c):
+            mass = sum(q[i] for i in sub)
+            if heaviest is None or mass > heaviest[0]:
+                heaviest = (mass, sub)
+        if heaviest[0] >= p:
+            best = heaviest
+            break
+    tau = min(q[i] for i in best[1])
+    return np.asarray([qi >= tau for qi in q]), best
+
+
+# --------------------------------------------------------------------------
+# Checks
+# --------------------------------------------------------------------------
+def check_worked_examples(O):
+    for case in golden()["cases"]:
+        if "probs" in case:
+            q = np.asarray(case["probs"], dtype=np.float64)
+            keep, a, m = O.topp_levels(q, q, case["p"])
+            assert keep.sum() == case["keep_count"], (case["id"], keep)
+            if "renormalized" in case:
+                got = q[keep] / q[keep].sum()
+                assert np.allclose(got, case["renormalized"], atol=case["tol"]), (case["id"], got)
+            if "kept_mass" in case:
+                assert abs(q[keep].sum() - case["kept_mass"]) <= 1e-12, case["id"]
+            # The same example through the full sampler, as logits ln(q).
+            if case["id"] != "descending_prefix_boundary":
+                r, pr = run_row(O, np.log(q).astype(np.float32), 1.0, case["p"])
+                assert r["keep_count"] == case["keep_count"], (case["id"], r)
+            continue
+        x = _logits_of(case)
+        r, pr = run_row(O, x, case["T"], case["p"])
+        assert r["status"] == 0 and r["keep_count"] == case["keep_count"], (case["id"], r)
+        kept = pr[pr > 0]
+        if "renormalized" in case:
+            got = pr[: len(case["renormalized"])]
+            assert np.allclose(got, case["renormalized"], atol=case["tol"]), (case["id"], got)
+            assert abs(kept.sum() - 1.0) < 1e-12
+        if "kept_mass" in case:
+            assert abs(r["s_keep"] / r["s_surv"] - case["kept_mass"]) <= case["tol"], (case["id"], r)
+        if "tempered" in case:
+            r1, p1 = run_row(O, x, case["T"], 1.0)  # p = 1: the plain tempered softmax
+            assert np.allclose(p1, case["tempered"], atol=case["tempered_tol"]), (case["id"], p1)
+
+
+def check_order_counterexample(O):
+    """Temperature does not commute with top-p: at T = 1.5 applying top-p to
+    the untempered distribution keeps 4 tokens, after temperature 5 (the
+    temperature/top-k/top-p page, 'A strong answer').  The chain applies
+    temperature first."""
+    x = [3.0, 2.5, 2.0, 1.0, 0.5, 0.0]
+    before, _ = run_row(O, x, 1.0, 0.9)
+    after, pr = run_row(O, x, 1.5, 0.9)
+    assert before["keep_count"] == 4 and after["keep_count"] == 5
+    assert pr[4] > 0.05  # the fifth token gets a real share of the mass
+
+
+def check_special_cases(O):
+    # Greedy: T <= 0 is argmax with the lowest index on ties.
+    r, pr = run_row(O, [1.0, 5.0, 2.0, 5.0], 0.0, 0.9)
+    assert r["token"] == 1 and r["keep_count"] == 1 and pr[1] == 1.0 and pr.sum() == 1.0
+    r, _ = run_row(O, [1.0, 5.0, 2.0, 5.0], -1.0, 0.9)
+    assert r["token"] == 1
+    # p >= 1 keeps every finite token; -inf tokens get probability 0.
+    row = [0.5, -np.inf, 0.25, 3.0, -np.inf]
+    r, pr = run_row(O, row, 1.0, 1.0)
+    assert r["keep_count"] == 3 and pr[1] == 0.0 and pr[4] == 0.0
+    r, _ = run_row(O, row, 1.0, 2.5)
+    assert r["keep_count"] == 3
+    # Very small and non-positive p keep the top level only (and all its ties).
+    r, _ = run_row(O, [1.0, 2.0, 2.0, 0.0], 1.0, 1e-6)
+    assert r["keep_count"] == 2
+    r, _ = run_row(O, [1.0, 2.0, 2.0, 0.0], 1.0, 0.0)
+    assert r["keep_count"] == 2
+    # top_k = 1 with two equal maxima keeps both.
+    r, _ = run_row(O, [4.0, 1.0, 4.0, 3.9], 1.0, 1.0, k=1)
+    assert r["keep_count"] == 2
+    # top_k keeps exactly k tokens when the values are distinct.
+    r, _ = run_row(O, [4.0, 1.0, 3.0, 2.0], 1.0, 1.0, k=2)
+    assert r["keep_count"] == 2
+    # top_k >= V and top_k <= 0 are no-ops.
+    for k in (0, -3, 4, 100):
+        r, _ = run_row(O, [4.0, 1.0, 4.0, 3.9], 1.0, 1.0, k=k)
+        assert r["keep_count"] == 4
+    # min-p drops p_i < min_p * p_max; min_p > 1 behaves as 1.
+    x = np.log(np.asarray([0.5, 0.25, 0.125, 0.0625, 0.0625]))
+    r, _ = run_row(O, x, 1.0, 1.0, mp=0.3)
+    assert r["keep_count"] == 2
+    r, _ = run_row(O, x, 1.0, 1.0, mp=5.0)
+    assert r["keep_count"] == 1
+    # Row errors: NaN, +inf, no finite logit, NaN parameters.
+    for row, T, p, mp in (([1.0, np.nan], 1.0, 0.9, 0.0), ([1.0, np.inf], 1.0, 0.9, 0.0),
+                          ([-np.inf, -np.inf], 1.0, 0.9, 0.0), ([1.0, 2.0], np.nan, 0.9, 0.0),
+                          ([1.0, 2.0], 1.0, np.nan, 0.0), ([1.0, 2.0], 1.0, 0.9, np.nan),
+                          ([1.0, np.nan], 0.0, 0.9, 0.0)):
+        r, pr = run_row(O, row, T, p, mp=mp)
+        assert r["status"] == 1 and r["token"] == -1 and r["keep_count"] == 0 and not pr.any()
+    # Empty batch: nothing to do, no error.
+    out, _ = O.sample(np.zeros((0, 7), np.float32), np.zeros(0), np.zeros(0))
+    assert out.shape == (0,)
+    # -0.0 and +0.0 are one level.
+    r, _ = run_row(O, [0.0, -0.0, -1.0], 1.0, 0.3)
+    assert r["keep_count"] == 2
+
+
+def check_bruteforce_protocol(O, batches=3000, seed=1234, extras=False):
+    """Random batches of 4 rows against the order-free definition: vocabularies
+    of 1 to 39 tokens, temperatures 0, 0.5, 1 and 2, p from 0.05 to 1.0, a third
+    of the batches drawn from a five-value integer set so that ties are common
+    (the protocol of 'Implement batched top-p sampling with temperature',
+    closing paragraph of 'Why each line is there').  Tokens whose mass above
+    lies within 1e-9 of p are excluded, as there.  With ``extras`` the rows
+    also carry random top-k and min-p."""
+    rng = np.random.default_rng(seed)
+    rows_checked = boundary = 0
+    for _ in range(batches):
+        V = int(rng.integers(1, 40))
+        if rng.random() < 1 / 3:
+            L = rng.integers(-2, 3, (4, V)).astype(np.float32)
+        else:
+            L = rng.normal(0.0, 2.0, (4, V)).astype(np.float32)
+        T = rng.choice([0.0, 0.5, 1.0, 2.0], 4).astype(np.float32)
+        P = np.where(rng.random(4) < 0.1, 1.0, rng.uniform(0.05, 1.0, 4)).astype(np.float32)
+        K = np.where(rng.random(4) < 0.5, rng.integers(1, V + 2, 4), 0).astype(np.int32) if extras else np.zeros(4, np.int32)
+        MP = np.where(rng.random(4) < 0.5, rng.uniform(0.0, 0.6, 4), 0.0).astype(np.float32) if extras else np.zeros(4, np.float32)
+        out, pr = O.sample(L, T, P, K, MP, seed=99, want_probs=True)
+        for b in range(4):
+            x = L[b].astype(np.float64)
+            if T[b] <= 0:
+                assert out[b]["token"] == int(np.argmax(x)), (L[b], out[b])
+                continue
+            keep, A, probs = brute_row(x, float(T[b]), float(P[b]), int(K[b]), float(MP[b]))
+            near = np.abs(A - P[b]) <= 1e-9
+            if P[b] < 1.0 and near.any():
+                boundary += int(near.sum())
+                sel = ~near
+            else:
+                sel = np.ones(V, bool)
+            got = pr[b] > 0
+            assert np.array_equal(got[sel], keep[sel]), (x, T[b], P[b], K[b], MP[b], got, keep)
+            if sel.all():
+                assert np.abs(pr[b] - probs).max() <= 1e-12
+                assert out[b]["keep_count"] == keep.sum()
+                assert keep[out[b]["token"]]
+            rows_checked += 1
+    return rows_checked, boundary
+
+
+def check_exhaustive_subsets(O, trials=400, seed=77):
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        n = int(rng.integers(1, 13))
+        if rng.random() < 0.4:
+            x = rng.integers(-2, 3, n).astype(np.float32)
+        else:
+            x = rng.normal(0.0, 1.5, n).astype(np.float32)
+        p = float(rng.uniform(0.05, 1.0))
+        e = np.exp(x.astype(np.float64) - x.max())
+        q = e / e.sum()
+        masses = [sum(q[list(s)]) for c in range(1, n + 1) for s in itertools.combinations(range(n), c)]
+        if min(abs(m - p) for m in masses) <= 1e-9:
+            continue  # on the boundary: floating point decides
+        want, _ = exhaustive_keep(q, p)
+        r, pr = run_row(O, x, 1.0, p)
+        assert np.array_equal(pr > 0, want), (x, p, pr, want)
+
+
+def check_invariants(O, trials=300, seed=5):
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        V = int(rng.integers(2, 300))
+        x = rng.normal(0, 2, V).astype(np.float32)
+        if rng.random() < 0.5:
+            x[rng.integers(0, V, V // 4)] = x[0]  # plant ties
+        if rng.random() < 0.3:
+            x[rng.integers(0, V, V // 5)] = -np.inf
+            x[0] = 1.0
+        T = float(rng.choice([0.3, 1.0, 2.0]))
+        p = float(rng.uniform(0.05, 0.999))
+        r, pr = run_row(O, x, T, p)
+        keep = pr > 0
+        top = x.max()
+        assert keep[x == top].all()                                      # the argmax is kept
+        for v in np.unique(x[np.isfinite(x)]):
+            lvl = keep[x == v]
+            assert lvl.all() or not lvl.any()                          # ties share a fate
+        assert r["s_keep"] / r["s_surv"] >= p - 1e-12                  # kept mass reaches p
+        assert abs(pr.sum() - 1.0) < 1e-12                             # renormalised
+        assert not keep[~np.isfinite(x)].any()                          # -inf never kept
+        assert keep[r["token"]]                                         # the draw is kept
+        assert r["min_kept_logit"] == x[keep].min()
+        # Temperature commutes with top-k: the kept set of top-k alone is the same at any T > 0.
+        k = int(rng.integers(1, V + 1))
+        a, pa = run_row(O, x, 0.5, 1.0, k=k)
+        b, pb = run_row(O, x, 3.0, 1.0, k=k)
+        assert np.array_equal(pa > 0, pb > 0)
+        assert (pa > 0).sum() >= min(k, np.isfinite(x).sum())
+
+
+def check_large_rows(O):
+    """A 128,256-token row at p = 0.9 keeps far fewer than all tokens; p = 1
+    keeps all of them ('Implement batched top-p sampling ...', TL;DR and
+    'Why each line is there' item 3; 'Top-p (Nucleus) Sampling, in depth',
+    'What to do next' item 2)."""
+    V = 128256
+    rng = np.random.default_rng(3)
+    x = (-1.1 * np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V)).astype(np.float32)
+    r, _ = run_row(O, x, 1.0, 0.9, probs=False)
+    assert 1 <= r["keep_count"] < V // 2
+    r, _ = run_row(O, x, 1.0, 1.0, probs=False)
+    assert r["keep_count"] == V
+
+
+def _draw_freqs(O, case, n, seed=2024, step=0):
+    x = np.asarray(case["logits"], dtype=np.float32)
+    L = np.tile(x, (n, 1))
+    out, _ = O.sample(L, np.full(n, case["T"]), np.full(n, case["p"]), seed=seed, step=step)
+    return np.bincount(out["token"], minlength=len(x)) / n
+
+
+def check_race_frequencies(O):
+    """The exponential race draws from the renormalised nucleus: frequencies of
+    the pages' sampled examples.  Each row of a batch has its own Philox
+    counter, so a batch of n identical rows is n independent draws."""
+    for case in golden()["draws"]:
+        n = case["n"]
+        f = _draw_freqs(O, case, n)
+        k = len(case["target"])
+        assert f[k:].sum() == 0.0, f                       # nothing outside the nucleus
+        for got, want in zip(f[:k], case["target"]):
+            sigma = math.sqrt(want * (1 - want) / n)
+            assert abs(got - want) <= 5 * sigma + 1e-3, (case["id"], f)
+
+
+def check_race_chisquare(O):
+    """400,000 draws from a filtered 5-token distribution: chi-square at a fixed
+    seed, and no filtered-out token ever drawn ('Implement batched top-p
+    sampling ...', closing paragraph of 'Why each line is there')."""
+    q = np.asarray([0.30, 0.25, 0.25, 0.12, 0.08])
+    x = np.log(q).astype(np.float32)
+    n = 400_000
+    out, pr = O.sample(np.tile(x, (n, 1)), np.ones(n), np.full(n, 0.6), seed=31337, step=5)
+    target = np.asarray([0.375, 0.3125, 0.3125, 0.0, 0.0])
+    cnt = np.bincount(out["token"], minlength=5)
+    assert cnt[3] == 0 and cnt[4] == 0
+    exp = target[:3] * n
+    chi2 = float(((cnt[:3] - exp) ** 2 / exp).sum())
+    assert chi2 < 18.4, (cnt, chi2)  # chi-square with 2 dof: p-value 1e-4
+    tv = 0.5 * np.abs(cnt / n - target).sum()
+    assert tv < 0.005, tv
+
+
+def check_race_reproducible(O):
+    x = np.random.default_rng(8).normal(0, 1, (64, 500)).astype(np.float32)
+    T = np.ones(64, np.float32)
+    P = np.full(64, 0.95, np.float32)
+    a, _ = O.sample(x, T, P, seed=11, step=3)
+    b, _ = O.sample(x, T, P, seed=11, step=3)
+    c, _ = O.sample(x, T, P, seed=11, step=4)
+    d, _ = O.sample(x, T, P, seed=12, step=3)
+    assert np.array_equal(a["token"], b["token"])
+    assert (a["token"] != c["token"]).sum() > 32
+    assert (a["token"] != d["token"]).sum() > 32
+
+
+_ROCRAND_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "rocrand_philox_words.cpp")
+
+
+def rocrand_words(tuples, workdir):
+    """Philox4x32-10 words from rocRAND's engine (host build) for
+    (seed, step, row, token) tuples."""
+    exe = os.path.join(workdir, "rocrand_philox_words")
+    if not os.path.exists(exe):
+        subprocess.run(["hipcc", "-O1", "--offload-arch=gfx950", "-o", exe, _ROCRAND_SRC], check=True,
+                       cwd=workdir)
+    text = "".join(f"{s} {t} {r} {i}\n" for s, t, r, i in tuples)
+    res = subprocess.run([exe], input=text, capture_output=True, text=True, check=True)
+    return [int(v) for v in res.stdout.split()]
+
+
+def philox_tuples(n=3000, seed=9):
+    rng = np.random.default_rng(seed)
+    # rocRAND addresses words by a 64-bit offset = 4 * counter(words 0,1), so the
+    # row (counter word 1) stays below 2**30 here.
+    tuples = [(0, 0, 0, 0), (1, 0, 0, 0), (2**64 - 1, 2**64 - 1, 2**30 - 1, 2**31 - 1)]
+    for _ in range(n):
+        tuples.append((int(rng.integers(0, 2**63)) * 2 + int(rng.integers(0, 2)), int(rng.integers(0, 2**63)),
+                       int(rng.integers(0, 2**30)), int(rng.integers(0, 2**31))))
+    return tuples
+
+
+def check_philox_against(O, tuples, words):
+    for (s, t, r, i), w in zip(tuples, words):
+        assert O.noise_word(s, t, r, i) == w, (s, t, r, i)
+
+
+def check_exp1(O):
+    """u = (r + 1/2)/2^32 and E = -ln u, at the extremes and midpoint."""
+    assert abs(O.exp1(0) - (-math.log(0.5 / 2**32))) < 1e-12
+    assert abs(O.exp1(2**32 - 1) - (-math.log1p(-0.5 / 2**32))) < 1e-20
+    assert abs(O.exp1(2**31) - (-math.log((2**31 + 0.5) / 2**32))) < 1e-15
+
+
+ALL_FAST_CHECKS = [check_worked_examples, check_order_counterexample, check_special_cases, check_invariants,
+                   check_exp1, check_race_reproducible]
