@@ -1,0 +1,204 @@
+"""Throughput of batched nucleus sampling on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+
+A step is one nucleus_sample call over one batch: validate, max, min-p,
+top-k, top-p cut, renormalise and the exponential race for every row.  The
+default workload is B = 256 rows of V = 128256 fp32 Zipf-shaped logits
+(workloads.py, workload 3).  Inputs sit in HBM before timing starts; the
+timed steps rotate over enough copies of the batch (> 512 MB in total) that
+the 256 MB last-level cache cannot serve a repeat read.
+
+Prints one JSON line: rows/s for the whole job, the dominant kernel's
+achieved HBM bandwidth against the 8 TB/s peak (per-launch HIP events on the
+stream the kernel runs on), the same buffers read by a pure streaming kernel
+for comparison, and the float64 oracle timed on the host's cores over a
+bounded sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "sampled rows/sec and logits HBM GB/s (% of peak) at B=256, V=128256 fp32"
+KERNEL_SOURCES = ["nucleus_sampling_amd/csrc/nucleus.hip", "nucleus_sampling_amd/csrc/row_kernel.h",
+                  "nucleus_sampling_amd/csrc/common.h", "nucleus_sampling_amd/csrc/params.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        p = os.path.join(ROOT, rel)
+        if os.path.exists(p):
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name: str, bytes_per_launch: float):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float, threads: int):
+    import oracle
+
+    t0 = time.perf_counter()
+    rows = 0
+    passes = 0
+    while True:
+        oracle.sample(w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], seed=w["seed"],
+                      threads=threads)
+        rows += w["B"]
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} pass(es) over the {w['B']} rows of the benchmark batch ({rows} rows, {dt:.1f} s, "
+                      f"float64 stable-sort oracle, {threads} threads, one row per task)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--buffers", type=int, default=0, help="input copies to rotate (default: > 512 MB total)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--profile-steps", action="store_true", help="only run the timed loop (for rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); rows are independent, so a batch "
+              "shards across GPUs with no communication, but this build measures one GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nucleus_sampling_amd as ns
+    import workloads
+
+    ns.lib()  # fails loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    w = workloads.make(args.workload)
+    B, V = w["B"], w["V"]
+    esz = 2 if w["dtype"] == "bf16" else 4
+    batch_bytes = B * V * esz
+    nbuf = args.buffers or max(2, -(-(512 * 2**20 + 1) // batch_bytes) + 1)
+    if w["dtype"] == "bf16":
+        host = torch.from_numpy(w["logits"].view(np.int16)).view(torch.bfloat16)
+    else:
+        host = torch.from_numpy(w["logits"])
+    bufs = [host.to(dev) for _ in range(nbuf)]
+    T = torch.from_numpy(w["temperature"]).to(dev)
+    P = torch.from_numpy(w["top_p"]).to(dev)
+    K = torch.from_numpy(w["top_k"]).to(dev)
+    MP = torch.from_numpy(w["min_p"]).to(dev)
+    out = ns.SampleResult(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                          None, None)
+    ws = None
+    need = ns.workspace_bytes(B, V, host.dtype)
+    if need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        ns.sample(bufs[i % nbuf], T, P, K, MP, seed=w["seed"], step=i, out=out, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    span_ms = starts[0].elapsed_time(ends[-1])
+    if args.profile_steps:
+        print(json.dumps({"profile_steps": args.steps, "span_ms": span_ms}), flush=True)
+        return
+
+    # Pure streaming read of the same buffers: the practical read ceiling.
+    sink = torch.zeros(256, dtype=torch.int64, device=dev)
+    for i in range(5):
+        ns.stream_read(bufs[i % nbuf], sink, stream)
+    torch.cuda.synchronize()
+    rs = [torch.cuda.Event(enable_timing=True) for _ in range(50)]
+    re_ = [torch.cuda.Event(enable_timing=True) for _ in range(50)]
+    for i in range(50):
+        rs[i].record(stream)
+        ns.stream_read(bufs[i % nbuf], sink, stream)
+        re_[i].record(stream)
+    torch.cuda.synchronize()
+    read_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(rs, re_)]))
+
+    avg_ms = float(np.mean(per_launch_ms))
+    med_ms = float(np.median(per_launch_ms))
+    achieved = batch_bytes / (avg_ms * 1e-3) / 1e9
+    stream_gbps = batch_bytes / (read_ms * 1e-3) / 1e9
+    ms_per_step = span_ms / args.steps
+    value = B * args.steps / (span_ms * 1e-3)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w["dtype"] == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w['name']}: B={B}, V={V} {w['dtype']} logits, per-row T/top_p/top_k/min_p",
+                   "B": B, "V": V, "logit_dtype": w["dtype"], "input_buffers": nbuf,
+                   "input_bytes_per_step": batch_bytes},
+        "logits_gbps": achieved,
+        "pct_of_hbm_peak": 100.0 * achieved / PEAK_HBM_GBPS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic_from_profile(w["name"], batch_bytes),
+                     "kernel": "row_sample_kernel", "avg_launch_ms": avg_ms, "median_launch_ms": med_ms,
+                     "algorithmic_bytes_per_launch": batch_bytes},
+        "stream_read": {"gbps": stream_gbps, "avg_ms": read_ms, "frac_of_peak": stream_gbps / PEAK_HBM_GBPS,
+                        "sampler_vs_stream": achieved / stream_gbps},
+        "wall_s": wall,
+        "kernel_hash": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, threads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

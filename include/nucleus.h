@@ -1,0 +1,141 @@
+/*
+ * nucleus.h -- C ABI of libnucleus, batched top-p (nucleus) sampling over
+ * full-vocabulary logits on AMD Instinct MI355X (gfx950).
+ *
+ * One call samples one token for each of B rows of logits.  Each row carries
+ * its own temperature T, min-p, top-k and top-p, applied as one chain:
+ *
+ *   temperature -> min-p -> top-k -> top-p -> renormalise -> sample
+ *
+ * (the order named in "What do temperature, top-k and top-p each do to the
+ * next-token distribution, and in what order does a serving engine apply
+ * them?", TL;DR and reference sampler).  Per row b with logits x:
+ *
+ *  - Temperature divides the logits before the softmax: p_i is proportional
+ *    to exp((x_i - max x)/T) (the tempered-softmax equation of that page).
+ *    T <= 0 is greedy: the lowest index among the maximal logits ("Implement
+ *    batched top-p sampling with temperature", "A strong answer" and "Why
+ *    each line is there", item 4).
+ *  - min-p drops token i iff p_i < min_p * max_j p_j (reference sampler of the
+ *    order page).  min_p <= 0 is off; min_p > 1 acts as 1.
+ *  - top-k keeps the tokens whose logit is >= the k-th largest remaining
+ *    logit; ties at the k-th value survive (order page, reference sampler and
+ *    its edge-case note).  k <= 0 is off; k >= the number of remaining tokens
+ *    is a no-op.
+ *  - top-p keeps token i iff the probability mass of the remaining tokens
+ *    strictly more probable than i is < p, measured on the distribution left
+ *    by min-p and top-k, renormalised.  Tokens tied at the cut share a fate,
+ *    the most probable level is always kept, p >= 1 keeps every remaining
+ *    token and p <= 0 keeps only the most probable level ("Top-p (Nucleus)
+ *    Sampling, in depth", "Batched top-p with a different p per request" and
+ *    "Boundaries and ties"; "Implement batched top-p sampling ...", "How to
+ *    approach it").
+ *  - The kept set is renormalised and one token is drawn by the exponential
+ *    race argmax_i p_i / E_i, E_i ~ Exp(1) (order page, "A strong answer",
+ *    last paragraph), lowest index on exact ties.  E_i = -ln u_i,
+ *    u_i = (r_i + 1/2) / 2^32, where r_i is word (i mod 4) of
+ *    Philox4x32-10 (Salmon et al., SC'11) with key (seed low 32 bits, seed
+ *    high 32 bits) and counter (i / 4, b, step low 32 bits, step high
+ *    32 bits).  The draw of row b depends only on (seed, step, b) and row b's
+ *    own inputs.
+ *  - A row with a NaN or +inf logit, no finite logit, or a NaN T / top-p /
+ *    min-p is a row error ("Top-p (Nucleus) Sampling, in depth", "Failure
+ *    modes": check for NaN and fail the request).  -inf logits are masked
+ *    tokens: probability 0, never kept.
+ *
+ * Threading: calls are asynchronous on the given stream and never
+ * synchronise the device.  Calls on different streams need distinct
+ * workspaces.  The library keeps no pointer after a call returns.
+ */
+#ifndef NUCLEUS_H
+#define NUCLEUS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes.  Argument errors are detected on the host before anything is
+ * launched; nothing is written in that case. */
+#define NUCLEUS_OK 0
+#define NUCLEUS_EINVAL (-1)     /* null required pointer, B < 0, V < 1, V >= 2^31, bad dtype,
+                                   stride < V, or a pointer not aligned to its element size */
+#define NUCLEUS_EWORKSPACE (-2) /* workspace missing or smaller than nucleus_workspace_bytes() */
+#define NUCLEUS_ELAUNCH (-3)    /* the HIP runtime refused a launch */
+#define NUCLEUS_EDEVICE (-4)    /* no usable gfx950 device for the current HIP context */
+
+/* Logit element types. */
+#define NUCLEUS_F32 0
+#define NUCLEUS_BF16 1
+
+typedef struct nucleus_options {
+    int32_t dtype;               /* NUCLEUS_F32 (default) or NUCLEUS_BF16 */
+    int32_t flags;               /* reserved: pass 0 */
+    void* stream;                /* hipStream_t to launch on; NULL = the null stream */
+    int64_t row_stride;          /* elements between row starts; 0 means V */
+    void* workspace;             /* device scratch of >= nucleus_workspace_bytes(B, V, dtype) bytes,
+                                    owned by the caller; may be NULL when that size is 0 */
+    size_t workspace_bytes;      /* size of workspace */
+    float* out_min_kept_logit;   /* optional device [B]: the smallest kept logit (NaN on a row
+                                    error).  For T > 0 rows the kept set is exactly
+                                    {i : x_i finite and x_i >= out_min_kept_logit[b]};
+                                    for greedy rows it is {out_token[b]}. */
+} nucleus_options;
+
+/*
+ * Sample one token per row.
+ *
+ * logits          device, [B, row_stride] elements of dtype, row-major; read only.
+ *                 fp32 rows must start on 16-byte boundaries or the call uses the
+ *                 (slower) unaligned path; bf16 rows are widened exactly to fp32.
+ * B, V            batch rows and vocabulary size: B >= 0, 1 <= V < 2^31.
+ *                 B == 0 returns NUCLEUS_OK and launches nothing.
+ * temperature     device [B] float, required.
+ * top_p           device [B] float, required.
+ * top_k           device [B] int32, or NULL (top-k off for every row).
+ * min_p           device [B] float, or NULL (min-p off for every row).
+ * seed, step      Philox key and the high counter words; reusing them reproduces
+ *                 the draws exactly.
+ * out_token       device [B] int32: the sampled id, or -1 on a row error.
+ * out_keep_count  device [B] int32: size of the kept set (1 for greedy rows,
+ *                 0 on a row error).
+ * out_probs       device [B, V] float, or NULL: the renormalised kept
+ *                 distribution (one-hot for greedy rows, zeros on a row error).
+ * opt             NULL for all defaults (fp32, null stream, no stride, no workspace).
+ *
+ * Returns NUCLEUS_OK or a negative code; the outputs are complete once the
+ * stream reaches the call.  All device buffers are owned by the caller and
+ * must stay valid until then.
+ */
+int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temperature,
+                   const float* top_p, const int32_t* top_k, const float* min_p, uint64_t seed,
+                   uint64_t step, int32_t* out_token, int32_t* out_keep_count, float* out_probs,
+                   const nucleus_options* opt);
+
+/* Device workspace, in bytes, that nucleus_sample needs for a batch of this
+ * shape and dtype (0 if none).  Returns 0 for invalid shapes. */
+size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype);
+
+/* Static description of a return code. */
+const char* nucleus_strerror(int code);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int nucleus_version(void);
+
+/*
+ * Read `bytes` bytes of device memory at `buf` once with 16-byte loads and
+ * fold them into device `sink`, an array of 256 uint64 words (XOR-updated,
+ * not cleared).  This is the HBM read ceiling the sampler's achieved
+ * bandwidth is compared with.  `buf` must be 16-byte aligned.  Asynchronous
+ * on `stream` (a hipStream_t, NULL = null stream).  Returns NUCLEUS_OK or a
+ * negative code.
+ */
+int nucleus_stream_read(const void* buf, size_t bytes, uint64_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NUCLEUS_H */

@@ -1,0 +1,177 @@
+"""Python binding of libnucleus: batched top-p (nucleus) sampling on MI355X.
+
+Argument marshalling only.  Every step of the sampler runs in the HIP
+kernels of ``libnucleus.so`` (built in-tree by ``nucleus_sampling_amd.build``);
+PyTorch supplies device memory and the stream.  There is no CPU fallback:
+if the library is missing or the device is not a gfx950, calls raise.
+
+    tok, cnt = nucleus_sampling_amd.sample(logits, temperature, top_p,
+                                           top_k=None, min_p=None,
+                                           seed=0, step=0)[:2]
+
+The C ABI, with the semantics of every argument, is ``include/nucleus.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+__all__ = ["sample", "workspace_bytes", "strerror", "version", "stream_read", "NucleusError", "lib", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnucleus.so")
+
+NUCLEUS_F32 = 0
+NUCLEUS_BF16 = 1
+
+
+class NucleusError(RuntimeError):
+    pass
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("stream", ctypes.c_void_p),
+        ("row_stride", ctypes.c_int64),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("out_min_kept_logit", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libnucleus.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise NucleusError(f"{LIB_PATH} is missing: build it with `python -m nucleus_sampling_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64
+        L.nucleus_sample.argtypes = [vp, i64, i64, vp, vp, vp, vp, u64, u64, vp, vp, vp, ctypes.POINTER(_Options)]
+        L.nucleus_sample.restype = ctypes.c_int
+        L.nucleus_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32]
+        L.nucleus_workspace_bytes.restype = ctypes.c_size_t
+        L.nucleus_strerror.argtypes = [ctypes.c_int]
+        L.nucleus_strerror.restype = ctypes.c_char_p
+        L.nucleus_version.argtypes = []
+        L.nucleus_version.restype = ctypes.c_int
+        L.nucleus_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.nucleus_stream_read.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().nucleus_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return int(lib().nucleus_version())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return NUCLEUS_F32
+    if t.dtype == torch.bfloat16:
+        return NUCLEUS_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def workspace_bytes(B: int, V: int, dtype: torch.dtype = torch.float32) -> int:
+    code = NUCLEUS_BF16 if dtype == torch.bfloat16 else NUCLEUS_F32
+    return int(lib().nucleus_workspace_bytes(int(B), int(V), code))
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise NucleusError(f"{what}: {strerror(code)} ({code})")
+
+
+def _vec(t, B, dtype, name, dev):
+    if t is None:
+        return None
+    if not torch.is_tensor(t):
+        t = torch.as_tensor(t, dtype=dtype)
+    if t.device != dev:
+        t = t.to(dev)
+    t = t.to(dtype).contiguous()
+    if t.numel() != B:
+        raise ValueError(f"{name} must have {B} elements")
+    return t
+
+
+class SampleResult(NamedTuple):
+    token: torch.Tensor          # int32 [B]; -1 on a row error
+    keep_count: torch.Tensor     # int32 [B]
+    probs: Optional[torch.Tensor]     # float32 [B, V] or None
+    min_kept_logit: Optional[torch.Tensor]  # float32 [B] or None
+
+
+def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, seed: int = 0, step: int = 0, *,
+           want_probs: bool = False, want_min_kept: bool = False, out: Optional[SampleResult] = None,
+           workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> SampleResult:
+    """Sample one token per row of ``logits`` [B, V] (float32 or bfloat16 on a
+    gfx950 device; rows may be strided, the last dimension must be dense).
+
+    Launches on ``stream`` (default: the current stream) and returns without
+    synchronising.  ``out`` may supply preallocated outputs; ``workspace`` a
+    preallocated byte tensor of at least ``workspace_bytes(B, V, dtype)``.
+    """
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    if not logits.is_cuda:
+        raise NucleusError("logits must be on the GPU: this library has no CPU path")
+    B, V = logits.shape
+    if V > 1 and logits.stride(1) != 1:
+        raise ValueError("the vocabulary dimension of logits must be contiguous")
+    dev = logits.device
+    code = _dtype_code(logits)
+    T = _vec(temperature, B, torch.float32, "temperature", dev)
+    P = _vec(top_p, B, torch.float32, "top_p", dev)
+    K = _vec(top_k, B, torch.int32, "top_k", dev)
+    MP = _vec(min_p, B, torch.float32, "min_p", dev)
+    if out is None:
+        out = SampleResult(
+            torch.empty(B, dtype=torch.int32, device=dev),
+            torch.empty(B, dtype=torch.int32, device=dev),
+            torch.empty((B, V), dtype=torch.float32, device=dev) if want_probs else None,
+            torch.empty(B, dtype=torch.float32, device=dev) if want_min_kept else None,
+        )
+    need = workspace_bytes(B, V, logits.dtype)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    opt = _Options()
+    opt.dtype = code
+    opt.flags = 0
+    opt.stream = s.cuda_stream
+    opt.row_stride = logits.stride(0) if B > 1 else V
+    opt.workspace = workspace.data_ptr() if (workspace is not None and need) else None
+    opt.workspace_bytes = (workspace.numel() * workspace.element_size()) if (workspace is not None and need) else 0
+    opt.out_min_kept_logit = out.min_kept_logit.data_ptr() if out.min_kept_logit is not None else None
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    rc = lib().nucleus_sample(ptr(logits), B, V, ptr(T), ptr(P), ptr(K), ptr(MP), ctypes.c_uint64(seed),
+                              ctypes.c_uint64(step), ptr(out.token), ptr(out.keep_count), ptr(out.probs),
+                              ctypes.byref(opt))
+    _check(rc, "nucleus_sample")
+    return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+    """Read every byte of ``buf`` once (the HBM read ceiling); ``sink`` is a
+    device tensor of 256 int64 words that receives an XOR checksum."""
+    if sink.numel() * sink.element_size() < 256 * 8:
+        raise ValueError("sink must hold 256 uint64 words")
+    s = stream if stream is not None else torch.cuda.current_stream(buf.device)
+    rc = lib().nucleus_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), s.cuda_stream)
+    _check(rc, "nucleus_stream_read")

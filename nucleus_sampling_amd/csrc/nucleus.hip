@@ -1,0 +1,141 @@
+// nucleus.hip -- the C ABI of libnucleus (declared in include/nucleus.h):
+// argument validation, launch-shape choice and launches on the caller's
+// stream.  No call synchronises the device or allocates memory.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "nucleus.h"
+#include "common.h"
+#include "params.h"
+#include "row_kernel.h"
+#include "stream_read.h"
+
+using namespace nucleus;
+
+namespace {
+
+// The library is built for gfx950 only; refuse other devices up front rather
+// than fail inside a launch.
+int check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return NUCLEUS_EDEVICE;
+    static std::mutex mu;
+    static int known[64] = {0};  // 0 unknown, 1 ok, -1 unsupported
+    if (dev < 0 || dev >= 64) return NUCLEUS_EDEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (known[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NUCLEUS_EDEVICE;
+        known[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    }
+    return known[dev] == 1 ? NUCLEUS_OK : NUCLEUS_EDEVICE;
+}
+
+int ceil_log2(int64_t v)
+{
+    int r = 0;
+    while ((int64_t(1) << r) < v) ++r;
+    return r;
+}
+
+// Fixed-point scale of token weights: each weight is < 2^shift + 1 and a row
+// sums at most V of them, so V * 2^shift must stay below 2^63.
+int mass_shift_for(int64_t V)
+{
+    const int s = 62 - ceil_log2(V);
+    return s < 40 ? s : 40;
+}
+
+template <class T>
+bool aligned(const T* p)
+{
+    return ((uintptr_t)p % alignof(T)) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nucleus_version(void) { return 100; }
+
+const char* nucleus_strerror(int code)
+{
+    switch (code) {
+    case NUCLEUS_OK: return "ok";
+    case NUCLEUS_EINVAL: return "invalid argument";
+    case NUCLEUS_EWORKSPACE: return "workspace missing or too small";
+    case NUCLEUS_ELAUNCH: return "kernel launch failed";
+    case NUCLEUS_EDEVICE: return "no usable gfx950 device";
+    default: return "unknown error";
+    }
+}
+
+size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype)
+{
+    if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16)) return 0;
+    return 0;
+}
+
+int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temperature, const float* top_p,
+                   const int32_t* top_k, const float* min_p, uint64_t seed, uint64_t step, int32_t* out_token,
+                   int32_t* out_keep_count, float* out_probs, const nucleus_options* opt)
+{
+    const int32_t dtype = opt ? opt->dtype : NUCLEUS_F32;
+    const int64_t stride = (opt && opt->row_stride) ? opt->row_stride : V;
+    if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || stride < V) return NUCLEUS_EINVAL;
+    if (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16) return NUCLEUS_EINVAL;
+    if (opt && opt->flags != 0) return NUCLEUS_EINVAL;
+    if (B == 0) return NUCLEUS_OK;
+    if (!logits || !temperature || !top_p || !out_token || !out_keep_count) return NUCLEUS_EINVAL;
+    const size_t esz = dtype == NUCLEUS_F32 ? 4 : 2;
+    if ((uintptr_t)logits % esz != 0 || !aligned(temperature) || !aligned(top_p) || (top_k && !aligned(top_k)) ||
+        (min_p && !aligned(min_p)) || !aligned(out_token) || !aligned(out_keep_count) ||
+        (out_probs && !aligned(out_probs)) || (opt && opt->out_min_kept_logit && !aligned(opt->out_min_kept_logit)))
+        return NUCLEUS_EINVAL;
+    const size_t need = nucleus_workspace_bytes(B, V, dtype);
+    if (need > 0 && (!opt || !opt->workspace || opt->workspace_bytes < need)) return NUCLEUS_EWORKSPACE;
+    const int dev_rc = check_device();
+    if (dev_rc != NUCLEUS_OK) return dev_rc;
+
+    Params p;
+    p.logits = logits;
+    p.B = B;
+    p.V = V;
+    p.stride = stride;
+    p.temperature = temperature;
+    p.top_p = top_p;
+    p.top_k = top_k;
+    p.min_p = min_p;
+    p.seed_lo = (uint32_t)seed;
+    p.seed_hi = (uint32_t)(seed >> 32);
+    p.step_lo = (uint32_t)step;
+    p.step_hi = (uint32_t)(step >> 32);
+    p.out_token = out_token;
+    p.out_count = out_keep_count;
+    p.out_probs = out_probs;
+    p.out_min_kept = opt ? opt->out_min_kept_logit : nullptr;
+    const size_t vec_bytes = dtype == NUCLEUS_F32 ? 16 : 8;
+    p.vec_in = ((uintptr_t)logits % vec_bytes == 0) && ((size_t)stride * esz) % vec_bytes == 0;
+    p.mass_shift = mass_shift_for(V);
+
+    hipStream_t s = opt ? (hipStream_t)opt->stream : nullptr;
+    const dim3 grid((unsigned)B), block(kRowBlock);
+    if (dtype == NUCLEUS_F32)
+        hipLaunchKernelGGL(row_sample_kernel<kF32>, grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL(row_sample_kernel<kBF16>, grid, block, 0, s, p);
+    return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
+}
+
+int nucleus_stream_read(const void* buf, size_t bytes, uint64_t* sink, void* stream)
+{
+    if (!buf || !sink || (uintptr_t)buf % 16 != 0 || !aligned(sink)) return NUCLEUS_EINVAL;
+    const int dev_rc = check_device();
+    if (dev_rc != NUCLEUS_OK) return dev_rc;
+    return launch_stream_read(buf, bytes, sink, (hipStream_t)stream) ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
+}
+
+}  // extern "C"

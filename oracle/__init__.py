@@ -93,7 +93,8 @@ class Oracle:
         ``logits`` is float32 or uint16 (bf16 bit patterns).  ``rows``
         (optional iterable of row indices) limits the work to those rows; the
         other entries of the result stay zero.  Returns (rows, probs): a
-        structured array of ROW_DTYPE of length B, and float64 [B, V] or None.
+        structured array of ROW_DTYPE of length B, and float64 probabilities
+        ([B, V], or [len(rows), V] in the order of ``rows``) or None.
         """
         logits = np.ascontiguousarray(logits)
         B, V = logits.shape
@@ -103,26 +104,31 @@ class Oracle:
         K = None if top_k is None else np.ascontiguousarray(top_k, dtype=np.int32).reshape(B)
         MP = None if min_p is None else np.ascontiguousarray(min_p, dtype=np.float32).reshape(B)
         out = np.zeros(B, dtype=ROW_DTYPE)
-        probs = np.zeros((B, V), dtype=np.float64) if want_probs else None
-        L = self.L
-
-        def run(span):
-            rc = L.oracle_sample(_ptr(logits), dt, B, V, V, _ptr(T), _ptr(P), _ptr(K), _ptr(MP),
-                                 ctypes.c_uint64(seed), ctypes.c_uint64(step), span[0], span[1],
-                                 _ptr(out), _ptr(probs))
-            if rc != 0:
-                raise ValueError("oracle_sample rejected its arguments")
-
         if rows is None:
             spans = [(b, b + 1) for b in range(B)] if threads > 1 else [(0, B)]
         else:
             spans = [(int(b), int(b) + 1) for b in rows]
+        # probs[j] belongs to spans[j][0] .. (one buffer row per span row)
+        nrows = sum(s1 - s0 for s0, s1 in spans)
+        probs = np.zeros((nrows, V), dtype=np.float64) if want_probs else None
+        starts = np.cumsum([0] + [s1 - s0 for s0, s1 in spans])
+        L = self.L
+
+        def run(j):
+            s0, s1 = spans[j]
+            pp = None if probs is None else probs[starts[j]:starts[j + 1]]
+            rc = L.oracle_sample(_ptr(logits), dt, B, V, V, _ptr(T), _ptr(P), _ptr(K), _ptr(MP),
+                                 ctypes.c_uint64(seed), ctypes.c_uint64(step), s0, s1,
+                                 _ptr(out), None if pp is None else pp.ctypes.data)
+            if rc != 0:
+                raise ValueError("oracle_sample rejected its arguments")
+
         if threads > 1 and len(spans) > 1:
             with ThreadPoolExecutor(threads) as ex:
-                list(ex.map(run, spans))
+                list(ex.map(run, range(len(spans))))
         else:
-            for s in spans:
-                run(s)
+            for j in range(len(spans)):
+                run(j)
         return out, probs
 
     def eval_cut(self, logits_row, row, temperature, top_p, top_k, min_p, seed, step, cut, want_probs=False):
@@ -173,12 +179,17 @@ class Oracle:
 _default = None
 
 
+def stale() -> bool:
+    """True when the built library is missing or older than its source."""
+    return not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC)
+
+
 def default() -> Oracle:
-    """The oracle built from this directory's source (built on first use)."""
+    """The oracle built from this directory's source (rebuilt when stale)."""
     global _default
     if _default is None:
-        if not os.path.exists(LIB_PATH):
-            build(force=False)
+        if stale():
+            build(force=True)
         _default = Oracle(LIB_PATH)
     return _default
 

@@ -1,0 +1,179 @@
+"""Row-by-row comparison of sampler outputs with the oracle.
+
+TEST INFRASTRUCTURE ONLY: used by the GPU parity tests and the smoke check.
+
+Rules, per row b (p = top_p[b]):
+
+* row error (oracle status 1): token -1, keep count 0, min kept logit NaN,
+  probabilities all zero.
+* greedy (T <= 0): token, keep count 1 and one-hot probabilities exactly.
+* otherwise, unless exempt: keep count and smallest kept logit exactly (so the
+  keep mask is exactly the oracle's), token exactly, probabilities within
+  |gpu - oracle| <= 1e-6 + 1e-5 * oracle.
+* mass-band exemption: the oracle's mass above the last kept level (A*) or
+  above the first dropped one (M*) lies within 1e-5 of p.  The row is then
+  judged by the admissible-set rule: the GPU's cut level L must satisfy
+  A(L) < p + 1e-5 and M(L) >= p - 1e-5 under the oracle's masses, and the
+  GPU's count, token and probabilities must equal the oracle's evaluation of
+  that same cut.  Exact agreement on exempt rows is counted separately.
+* race exemption: the oracle's race margin (s1 - s2)/s1 is below 1e-6.  The
+  GPU's token must then be kept and score at least s1 (1 - 1e-6) under the
+  oracle.
+* min-p boundary: a token whose p_i/(min_p p_max) lies within 1e-9 of 1 can
+  fall either way; such rows are counted and only checked for validity.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import default as _default_oracle
+
+MASS_BAND = 1e-5
+RACE_BAND = 1e-6
+MINP_BAND = 1e-9
+
+
+@dataclass
+class Report:
+    rows: int = 0
+    exact: int = 0
+    errors_ok: int = 0
+    greedy: int = 0
+    exempt_mass: int = 0
+    exempt_mass_exact: int = 0
+    exempt_race: int = 0
+    exempt_minp: int = 0
+    near_1e6: int = 0
+    near_1e7: int = 0
+    max_prob_ratio: float = 0.0
+    failures: list = field(default_factory=list)
+
+    def ok(self) -> bool:
+        return not self.failures
+
+    def summary(self) -> str:
+        return (f"rows={self.rows} exact={self.exact} greedy={self.greedy} row_errors={self.errors_ok} "
+                f"exempt_mass={self.exempt_mass} (exact {self.exempt_mass_exact}) exempt_race={self.exempt_race} "
+                f"exempt_minp={self.exempt_minp} band1e-6={self.near_1e6} band1e-7={self.near_1e7} "
+                f"max|dp|/(1e-6+1e-5p)={self.max_prob_ratio:.3g} failures={len(self.failures)}")
+
+
+def _prob_ratio(g, o):
+    return float(np.max(np.abs(g - o) / (1e-6 + 1e-5 * o))) if g.size else 0.0
+
+
+def compare(logits, temperature, top_p, top_k, min_p, seed, step, gpu_token, gpu_count, gpu_min_kept,
+            oracle_rows, gpu_probs=None, oracle_probs=None, prob_rows=None, batch_rows=None, O=None,
+            max_failures=20) -> Report:
+    """Compare GPU outputs with oracle results.
+
+    logits: host [B, V] (float32 or uint16 bf16 bits) as given to both sides.
+    gpu_*: host arrays [B]; oracle_rows: ROW_DTYPE [B].
+    gpu_probs / oracle_probs: optional [R, V] for the rows listed in prob_rows.
+    batch_rows: the Philox row index of each row (defaults to 0..B-1).
+    """
+    O = O or _default_oracle()
+    B = logits.shape[0]
+    T = np.asarray(temperature, np.float32)
+    P = np.asarray(top_p, np.float32)
+    K = np.zeros(B, np.int32) if top_k is None else np.asarray(top_k, np.int32)
+    MP = np.zeros(B, np.float32) if min_p is None else np.asarray(min_p, np.float32)
+    rid = np.arange(B) if batch_rows is None else np.asarray(batch_rows)
+    prob_index = {} if prob_rows is None else {int(b): j for j, b in enumerate(prob_rows)}
+    rep = Report()
+
+    def fail(b, why):
+        if len(rep.failures) < max_failures:
+            rep.failures.append((int(b), why))
+        else:
+            rep.failures.append((int(b), "..."))
+
+    for b in range(B):
+        rep.rows += 1
+        o = oracle_rows[b]
+        gt, gc, gm = int(gpu_token[b]), int(gpu_count[b]), float(gpu_min_kept[b]) if gpu_min_kept is not None else None
+        j = prob_index.get(b)
+        gp = gpu_probs[j] if (j is not None and gpu_probs is not None) else None
+        op = oracle_probs[j] if (j is not None and oracle_probs is not None) else None
+        if o["status"] == 1:
+            good = gt == -1 and gc == 0 and (gm is None or math.isnan(gm)) and (gp is None or not gp.any())
+            if good:
+                rep.errors_ok += 1
+            else:
+                fail(b, f"row error expected, got token={gt} count={gc} min_kept={gm}")
+            continue
+        if o["greedy"]:
+            rep.greedy += 1
+            good = gt == o["token"] and gc == 1 and (gm is None or gm == o["min_kept_logit"])
+            if gp is not None:
+                good &= gp[gt] == 1.0 and np.count_nonzero(gp) == 1
+            if good:
+                rep.exact += 1
+            else:
+                fail(b, f"greedy: token {gt} vs {o['token']}, count {gc}, min_kept {gm} vs {o['min_kept_logit']}")
+            continue
+        p = float(P[b])
+        a_s, m_s = float(o["a_star"]), float(o["m_star"])
+        if o["topp_active"]:
+            d = min(abs(a_s - p), abs(m_s - p))
+            rep.near_1e6 += d <= 1e-6
+            rep.near_1e7 += d <= 1e-7
+        exempt_mass = bool(o["topp_active"]) and (abs(a_s - p) <= MASS_BAND or abs(m_s - p) <= MASS_BAND)
+        exempt_minp = float(o["minp_nearest"]) <= MINP_BAND
+        same_set = gc == o["keep_count"] and gm is not None and gm == o["min_kept_logit"]
+        if exempt_minp:
+            rep.exempt_minp += 1
+            if not (0 <= gt < logits.shape[1] and gc >= 1):
+                fail(b, f"min-p boundary row: invalid token {gt} / count {gc}")
+            continue
+        if exempt_mass:
+            rep.exempt_mass += 1
+            if gm is None:
+                fail(b, "mass-band row needs the GPU's min kept logit")
+                continue
+            ev, eprobs = O.eval_cut(logits[b], rid[b], T[b], P[b], K[b], MP[b], seed, step, gm,
+                                    want_probs=gp is not None)
+            if not (ev["a_cut"] < p + MASS_BAND and ev["m_cut"] >= p - MASS_BAND):
+                fail(b, f"inadmissible cut {gm}: A={ev['a_cut']:.9f} M={ev['m_cut']:.9f} p={p:.9f}")
+                continue
+            if gc != ev["keep_count"]:
+                fail(b, f"count {gc} does not match the cut's {ev['keep_count']}")
+                continue
+            want_tok, s1 = int(ev["token"]), float(ev["race_s1"])
+            ref_probs = eprobs
+            if same_set:
+                rep.exempt_mass_exact += 1
+        else:
+            if not same_set:
+                fail(b, f"keep set: count {gc} vs {o['keep_count']}, min_kept {gm} vs {o['min_kept_logit']}")
+                continue
+            want_tok, s1 = int(o["token"]), float(o["race_s1"])
+            ref_probs = op
+        if gt != want_tok:
+            margin = float(o["race_margin"]) if not exempt_mass else None
+            sg = O.race_score(logits[b], rid[b], T[b], seed, step, gt) if 0 <= gt < logits.shape[1] else -1.0
+            kept_ok = 0 <= gt < logits.shape[1] and _kept(logits[b], gt, gm)
+            if kept_ok and sg >= s1 * (1.0 - RACE_BAND):
+                rep.exempt_race += 1
+            else:
+                fail(b, f"token {gt} vs {want_tok} (oracle score {sg:.9g} vs best {s1:.9g}, margin {margin})")
+                continue
+        elif not exempt_mass:
+            rep.exact += 1
+        if gp is not None and ref_probs is not None:
+            r = _prob_ratio(gp.astype(np.float64), ref_probs)
+            rep.max_prob_ratio = max(rep.max_prob_ratio, r)
+            if r > 1.0:
+                fail(b, f"probabilities off by {r:.3g} x tolerance")
+    return rep
+
+
+def _kept(row, tok, min_kept):
+    x = row[tok]
+    if row.dtype == np.uint16:
+        x = np.asarray([x], np.uint16).astype(np.uint32) << 16
+        x = x.view(np.float32)[0]
+    return bool(np.isfinite(x) and x >= min_kept)

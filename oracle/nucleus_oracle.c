@@ -342,8 +342,8 @@ static int64_t race(const row_prep* r, const uint8_t* keep, int64_t V, uint64_t 
 /*
  * Sample rows [r0, r1) of a [B, V] batch (row b starts at element b*stride).
  * rows_out[b] receives the result of row b.  probs_out, if not NULL, is a
- * [B, V] float64 array that receives the renormalised kept distribution
- * (one-hot for greedy rows, zeros for error rows).
+ * [r1 - r0, V] float64 array whose row (b - r0) receives the renormalised kept
+ * distribution of row b (one-hot for greedy rows, zeros for error rows).
  * Returns 0, or -1 on bad arguments.
  */
 int oracle_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride,
@@ -358,7 +358,7 @@ int oracle_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t s
         memset(o, 0, sizeof(*o));
         o->a_star = NAN; o->m_star = NAN; o->min_kept_logit = NAN;
         o->minp_nearest = INFINITY;
-        double* prow = probs_out ? probs_out + b * V : NULL;
+        double* prow = probs_out ? probs_out + (b - r0) * V : NULL;
         if (prow) memset(prow, 0, (size_t)V * sizeof(double));
 
         float T = temperature[b], P = top_p[b], MP = min_p ? min_p[b] : 0.0f;

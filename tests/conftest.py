@@ -16,5 +16,5 @@ def pytest_configure(config):
 def oracle_lib():
     import oracle
 
-    oracle.build(force=False)
+    oracle.default()  # builds the library if missing or stale
     return oracle

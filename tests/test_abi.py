@@ -1,0 +1,91 @@
+"""The C ABI library: it loads, exports every function include/nucleus.h
+declares, and rejects bad arguments on the host without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nucleus.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nucleus_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import nucleus_sampling_amd as ns
+
+    return ns.lib()
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ("nucleus_sample", "nucleus_workspace_bytes", "nucleus_strerror", "nucleus_version",
+              "nucleus_stream_read"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_strerror_and_version(L):
+    import nucleus_sampling_amd as ns
+
+    assert ns.strerror(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert ns.strerror(code) not in ("ok", "unknown error")
+    assert ns.version() >= 100
+
+
+def test_workspace_query(L):
+    import nucleus_sampling_amd as ns
+
+    assert L.nucleus_workspace_bytes(-1, 10, 0) == 0
+    assert L.nucleus_workspace_bytes(4, 0, 0) == 0
+    assert L.nucleus_workspace_bytes(4, 1 << 31, 0) == 0
+    assert L.nucleus_workspace_bytes(4, 10, 7) == 0
+    assert ns.workspace_bytes(256, 128256) >= 0
+
+
+def _call(L, logits=1 << 20, B=2, V=8, T=1 << 21, P=1 << 22, tok=1 << 23, cnt=1 << 24, opt=None):
+    # Fake, never-dereferenced device addresses: every case below must be
+    # rejected on the host before any launch.
+    return L.nucleus_sample(logits, B, V, T, P, None, None, ctypes.c_uint64(0), ctypes.c_uint64(0), tok, cnt, None,
+                            opt)
+
+
+def test_host_side_argument_errors(L):
+    import nucleus_sampling_amd as ns
+
+    EINVAL = -1
+    assert _call(L, logits=None) == EINVAL
+    assert _call(L, T=None) == EINVAL
+    assert _call(L, P=None) == EINVAL
+    assert _call(L, tok=None) == EINVAL
+    assert _call(L, cnt=None) == EINVAL
+    assert _call(L, B=-1) == EINVAL
+    assert _call(L, V=0) == EINVAL
+    assert _call(L, V=1 << 31) == EINVAL
+    assert _call(L, logits=(1 << 20) + 2) == EINVAL  # fp32 logits not 4-byte aligned
+    assert _call(L, T=(1 << 21) + 1) == EINVAL
+    opt = ns._Options()
+    opt.dtype = 5
+    assert _call(L, opt=ctypes.byref(opt)) == EINVAL
+    opt = ns._Options()
+    opt.row_stride = 4  # < V
+    assert _call(L, opt=ctypes.byref(opt)) == EINVAL
+    opt = ns._Options()
+    opt.flags = 1
+    assert _call(L, opt=ctypes.byref(opt)) == EINVAL
+
+
+def test_empty_batch_launches_nothing(L):
+    assert _call(L, B=0) == 0
+    assert _call(L, B=0, logits=None, T=None, P=None, tok=None, cnt=None) == 0

@@ -1,0 +1,224 @@
+"""Parity of the HIP sampler with the float64 oracle, element by element.
+
+Every test calls the library through its C ABI (via the ctypes binding) on
+cuda:0 with seeded inputs from workloads.py, and compares with the oracle
+under the rules of oracle/compare.py: exact keep sets, keep counts and
+tokens; probabilities within 1e-6 + 1e-5 p; rows within 1e-5 of a mass
+boundary or 1e-6 of a race tie judged by the admissible-set rule.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import device_logits, oracle_and_compare, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None):
+    import torch
+
+    import nucleus_sampling_amd as ns
+
+    lg = device_logits(w["logits"], w["dtype"]) if lg is None else lg
+    res = ns.sample(lg, w["temperature"], w["top_p"], w["top_k"], w["min_p"],
+                    seed=w["seed"] if seed is None else seed, step=step, want_probs=want_probs, want_min_kept=True)
+    torch.cuda.synchronize()
+    probs = None
+    if want_probs:
+        idx = torch.as_tensor(list(prob_rows), dtype=torch.long, device=lg.device)
+        probs = res.probs.index_select(0, idx).cpu().numpy()
+    return res.token.cpu().numpy(), res.keep_count.cpu().numpy(), res.min_kept_logit.cpu().numpy(), probs
+
+
+PROB_ROWS = {1: list(range(15)), 2: [0, 1, 2, 3, 17, 40, 63], 3: [0, 1, 2, 3, 100, 255], 4: [0, 1, 2, 3, 9, 200],
+             5: [0, 1, 2, 5, 9, 500, 1023]}
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_workload_parity(n):
+    say(f"workload {n} ({workloads.NAMES[n]}) shape={workloads.SHAPES[n]} {workloads.DTYPES[n]}: generating")
+    w = workloads.make(n)
+    say(f"workload {n}: sampling on cuda:0 (no probs: the benchmark's launch)")
+    tok, cnt, mk, _ = _gpu(w)
+    rep, orows = oracle_and_compare(w, tok, cnt, mk)
+    say(f"workload {n}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+    say(f"workload {n}: sampling with probabilities for rows {PROB_ROWS[n]}")
+    tok2, cnt2, mk2, probs = _gpu(w, want_probs=True, prob_rows=PROB_ROWS[n])
+    assert np.array_equal(tok, tok2) and np.array_equal(cnt, cnt2)
+    rep2, _ = oracle_and_compare(w, tok2, cnt2, mk2, gpu_probs=probs, prob_rows=PROB_ROWS[n])
+    say(f"workload {n} probs: {rep2.summary()}")
+    assert rep2.ok(), rep2.failures
+
+
+def _random_batch(rng, B, V, dtype, extras=True):
+    kind = rng.integers(0, 3, B)
+    L = np.empty((B, V), np.float32)
+    for b in range(B):
+        if kind[b] == 0:
+            L[b] = rng.normal(0, 2, V)
+        elif kind[b] == 1:
+            L[b] = rng.integers(-2, 3, V)
+        else:
+            L[b] = -1.1 * np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V)
+        if rng.random() < 0.3:
+            L[b, rng.random(V) < 0.2] = -np.inf
+            L[b, rng.integers(0, V)] = 0.5
+    T = rng.choice([0.0, 0.3, 0.7, 1.0, 1.5, 3.0], B).astype(np.float32)
+    P = np.where(rng.random(B) < 0.15, 1.0, rng.uniform(0.05, 0.999, B)).astype(np.float32)
+    K = (np.where(rng.random(B) < 0.4, rng.integers(1, V + 3, B), 0) if extras else np.zeros(B)).astype(np.int32)
+    MP = (np.where(rng.random(B) < 0.3, rng.uniform(0, 0.5, B), 0.0) if extras else np.zeros(B)).astype(np.float32)
+    logits = workloads.f32_to_bf16_bits(L) if dtype == "bf16" else L
+    return dict(logits=logits, dtype=dtype, temperature=T, top_p=P, top_k=K, min_p=MP, seed=4242, B=B, V=V)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 63, 64, 65, 1023, 4097, 9999, 40001])
+def test_small_and_ragged_shapes(V, dtype):
+    rng = np.random.default_rng(V * 7 + (dtype == "bf16"))
+    B = 9
+    w = _random_batch(rng, B, V, dtype)
+    say(f"ragged V={V} {dtype} B={B}")
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(B))
+    rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(B)))
+    say(f"ragged V={V} {dtype}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_strided_unaligned_rows(dtype):
+    """Rows whose starts are not 16-byte aligned take the scalar-load path."""
+    import torch
+
+    rng = np.random.default_rng(17)
+    B, V, pad = 6, 3001, 3
+    w = _random_batch(rng, B, V, dtype)
+    say(f"strided rows V={V} stride={V + pad} {dtype}")
+    base = device_logits(np.pad(w["logits"], ((0, 0), (0, pad))), dtype)
+    lg = base[:, :V]
+    assert lg.stride(0) == V + pad
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(B), lg=lg)
+    rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(B)))
+    assert rep.ok(), rep.failures
+    torch.cuda.synchronize()
+
+
+def _edge_batch():
+    V = 37
+    inf, nan = np.inf, np.nan
+    rows, T, P, K, MP = [], [], [], [], []
+
+    def add(row, t=1.0, p=0.9, k=0, mp=0.0):
+        r = np.full(V, -inf, np.float32)
+        r[: len(row)] = row
+        rows.append(r); T.append(t); P.append(p); K.append(k); MP.append(mp)
+
+    add([1.0, nan, 2.0])                      # NaN logit
+    add([1.0, inf, 2.0])                      # +inf logit
+    add([])                                   # no finite logit
+    add([1.0, 2.0], t=nan)                    # NaN parameters
+    add([1.0, 2.0], p=nan)
+    add([1.0, 2.0], mp=nan)
+    add([1.0, nan], t=0.0)                    # greedy rows still fail on NaN
+    add([3.0, 5.0, 5.0, 1.0], t=0.0)          # greedy, lowest index on ties
+    add([3.0, 5.0, 5.0, 1.0], t=-2.0)
+    add([0.5, 0.25, 3.0], p=1.0)              # p >= 1 keeps every finite token
+    add([0.5, 0.25, 3.0], p=7.0)
+    add([1.0, 2.0, 2.0, 0.0], p=0.0)          # p <= 0 keeps the top level
+    add([1.0, 2.0, 2.0, 0.0], p=-1.0)
+    add([1.0, 2.0, 2.0, 0.0], p=1e-8)
+    add([4.0, 1.0, 4.0, 3.9], p=1.0, k=1)     # top-k = 1 keeps tied maxima
+    add([4.0, 1.0, 3.0, 2.0], p=1.0, k=2)
+    add([4.0, 1.0, 3.0, 2.0], p=1.0, k=100)
+    add([4.0, 1.0, 3.0, 2.0], p=1.0, k=-4)
+    add(list(np.log([0.5, 0.25, 0.125, 0.0625, 0.0625])), p=1.0, mp=0.3)
+    add(list(np.log([0.5, 0.25, 0.125, 0.0625, 0.0625])), p=1.0, mp=5.0)
+    add(list(np.log([0.5, 0.25, 0.125, 0.0625, 0.0625])), p=1.0, mp=1e-30)
+    add([0.0, -0.0, -1.0], p=0.3)             # -0.0 and +0.0 are one level
+    add([2.0, 1.0, 0.0], t=np.inf, p=0.5)     # T = +inf: uniform over finite tokens
+    add([2.0, 1.0, 0.0], t=np.inf, p=1.0, mp=1.0)
+    add([2.0, 1.9999999, 0.0], t=1e-30)       # tiny T
+    add([2.0, 1.0, 0.0], t=1e-44)             # subnormal T
+    add([3e38, -3e38, 0.0], p=0.999)          # x - max overflows fp32
+    add([3e38, 3e38, -3e38], p=0.5)
+    add([1e-40, 0.0, -1e-40], t=1e-38)        # subnormal logits
+    add([7.0])                                # a single finite token
+    add(list(np.linspace(1.0, 0.0, 37)), p=0.9999999)
+    add([1.0] * 37, p=0.3)                    # one level
+    add([1.0] * 37, p=0.3, k=5)
+    return np.stack(rows), np.asarray(T, np.float32), np.asarray(P, np.float32), np.asarray(K, np.int32), \
+        np.asarray(MP, np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_edge_rows(dtype):
+    L, T, P, K, MP = _edge_batch()
+    if dtype == "bf16":
+        L = workloads.f32_to_bf16_bits(L)
+    w = dict(logits=L, dtype=dtype, temperature=T, top_p=P, top_k=K, min_p=MP, seed=1, B=len(T), V=L.shape[1])
+    say(f"edge rows ({len(T)}) {dtype}")
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(len(T)))
+    rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(len(T))))
+    say(f"edge rows {dtype}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+
+
+def test_single_column():
+    rng = np.random.default_rng(2)
+    w = _random_batch(rng, 5, 1, "f32")
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(5))
+    rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(5)))
+    assert rep.ok(), rep.failures
+
+
+def test_empty_batch():
+    import torch
+
+    import nucleus_sampling_amd as ns
+
+    say("empty batch")
+    lg = torch.zeros((0, 11), device="cuda:0")
+    res = ns.sample(lg, torch.zeros(0), torch.zeros(0))
+    torch.cuda.synchronize()
+    assert res.token.numel() == 0
+
+
+def test_determinism_step_and_row_independence():
+    rng = np.random.default_rng(99)
+    w = _random_batch(rng, 32, 5000, "f32", extras=False)
+    w["temperature"][:] = 1.0
+    w["top_p"][:] = 0.97
+    say("determinism: repeated calls")
+    a = _gpu(w)
+    b = _gpu(w)
+    assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3]))
+    say("determinism: a new step changes the draws")
+    c = _gpu(w, step=1)
+    assert (a[0] != c[0]).sum() >= 8
+    rep, _ = oracle_and_compare(w, *c[:3], step=1)
+    assert rep.ok(), rep.failures
+    say("row independence: other rows changed")
+    w2 = dict(w)
+    w2["logits"] = w["logits"].copy()
+    w2["logits"][1::2] = rng.normal(0, 1, w2["logits"][1::2].shape).astype(np.float32)
+    d = _gpu(w2)
+    assert np.array_equal(a[0][0::2], d[0][0::2]) and np.array_equal(a[1][0::2], d[1][0::2])
+
+
+def test_draws_match_oracle_on_worked_example():
+    """20,000 independent draws of the six-token example (one per row): every
+    draw equals the oracle's, so the GPU inherits the oracle's pinned
+    frequencies (0.6522 / 0.2399 / 0.1078)."""
+    n = 20000
+    x = np.full((n, 16), -np.inf, np.float32)
+    x[:, :6] = [4.0, 3.0, 2.2, 1.6, 1.0, -2.0]
+    w = dict(logits=x, dtype="f32", temperature=np.ones(n, np.float32), top_p=np.full(n, 0.9, np.float32),
+             top_k=np.zeros(n, np.int32), min_p=np.zeros(n, np.float32), seed=2024, B=n, V=16)
+    say("20,000 draws of the six-token example")
+    tok, cnt, mk, _ = _gpu(w)
+    rep, orows = oracle_and_compare(w, tok, cnt, mk)
+    assert rep.ok(), rep.failures
+    f = np.bincount(tok, minlength=16) / n
+    assert f[3:].sum() == 0
+    assert np.allclose(f[:3], [0.6522, 0.2399, 0.1078], atol=0.015)
