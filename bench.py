@@ -29,8 +29,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "sampled rows/sec and logits HBM GB/s (% of peak) at B=256, V=128256 fp32"
-KERNEL_SOURCES = ["nucleus_sampling_amd/csrc/nucleus.hip", "nucleus_sampling_amd/csrc/row_kernel.h",
-                  "nucleus_sampling_amd/csrc/common.h", "nucleus_sampling_amd/csrc/params.h"]
+KERNEL_SOURCES = ["nucleus_sampling_amd/csrc/nucleus.hip", "nucleus_sampling_amd/csrc/sampler.h",
+                  "nucleus_sampling_amd/csrc/model.h", "nucleus_sampling_amd/csrc/select.h",
+                  "nucleus_sampling_amd/csrc/workspace.h", "nucleus_sampling_amd/csrc/common.h",
+                  "nucleus_sampling_amd/csrc/params.h"]
 
 
 def kernel_hash() -> str:
@@ -116,11 +118,9 @@ def main():
     MP = torch.from_numpy(w["min_p"]).to(dev)
     out = ns.SampleResult(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                           None, None)
-    ws = None
-    need = ns.workspace_bytes(B, V, host.dtype)
-    if need:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    need = ns.workspace_bytes(B, V, host.dtype)
+    ws = ns.workspace_for(dev, stream, need) if need else None
 
     def step(i):
         ns.sample(bufs[i % nbuf], T, P, K, MP, seed=w["seed"], step=i, out=out, workspace=ws, stream=stream)
@@ -187,7 +187,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic_from_profile(w["name"], batch_bytes),
-                     "kernel": "row_sample_kernel", "avg_launch_ms": avg_ms, "median_launch_ms": med_ms,
+                     "kernel": "tile_kernel", "avg_launch_ms": avg_ms, "median_launch_ms": med_ms,
                      "algorithmic_bytes_per_launch": batch_bytes},
         "stream_read": {"gbps": stream_gbps, "avg_ms": read_ms, "frac_of_peak": stream_gbps / PEAK_HBM_GBPS,
                         "sampler_vs_stream": achieved / stream_gbps},

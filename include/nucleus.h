@@ -66,17 +66,26 @@ extern "C" {
 #define NUCLEUS_ELAUNCH (-3)    /* the HIP runtime refused a launch */
 #define NUCLEUS_EDEVICE (-4)    /* no usable gfx950 device for the current HIP context */
 
+/* Option flags. */
+#define NUCLEUS_FLAG_SINGLE_WORKGROUP 1 /* run every row on one workgroup that re-reads the row
+                                           from memory for each phase (no workspace needed).
+                                           Same results, bit for bit; slower.  For verification
+                                           and for callers that cannot provide a workspace. */
+
 /* Logit element types. */
 #define NUCLEUS_F32 0
 #define NUCLEUS_BF16 1
 
 typedef struct nucleus_options {
     int32_t dtype;               /* NUCLEUS_F32 (default) or NUCLEUS_BF16 */
-    int32_t flags;               /* reserved: pass 0 */
+    int32_t flags;               /* 0, or NUCLEUS_FLAG_SINGLE_WORKGROUP */
     void* stream;                /* hipStream_t to launch on; NULL = the null stream */
     int64_t row_stride;          /* elements between row starts; 0 means V */
     void* workspace;             /* device scratch of >= nucleus_workspace_bytes(B, V, dtype) bytes,
-                                    owned by the caller; may be NULL when that size is 0 */
+                                    256-byte aligned, owned by the caller; may be NULL when that
+                                    size is 0.  Its contents need no initial value and may be
+                                    reused by any later call.  Calls that may overlap (different
+                                    streams) need different workspaces. */
     size_t workspace_bytes;      /* size of workspace */
     float* out_min_kept_logit;   /* optional device [B]: the smallest kept logit (NaN on a row
                                     error).  For T > 0 rows the kept set is exactly
@@ -98,7 +107,9 @@ typedef struct nucleus_options {
  * min_p           device [B] float, or NULL (min-p off for every row).
  * seed, step      Philox key and the high counter words; reusing them reproduces
  *                 the draws exactly.
- * out_token       device [B] int32: the sampled id, or -1 on a row error.
+ * out_token       device [B] int32: the sampled id, or -1 on a row error (-2 if the
+ *                 workgroups of a row could not meet within seconds, e.g. because
+ *                 other work held the whole device).
  * out_keep_count  device [B] int32: size of the kept set (1 for greedy rows,
  *                 0 on a row error).
  * out_probs       device [B, V] float, or NULL: the renormalised kept
@@ -115,7 +126,8 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
                    const nucleus_options* opt);
 
 /* Device workspace, in bytes, that nucleus_sample needs for a batch of this
- * shape and dtype (0 if none).  Returns 0 for invalid shapes. */
+ * shape and dtype on its default path (0 if none: rows longer than
+ * 64 * 16384 tokens, or B == 0).  Returns 0 for invalid shapes. */
 size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype);
 
 /* Static description of a return code. */

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnucleus.
 
 NUCLEUS_F32 = 0
 NUCLEUS_BF16 = 1
+NUCLEUS_FLAG_SINGLE_WORKGROUP = 1
 
 
 class NucleusError(RuntimeError):
@@ -89,6 +90,21 @@ def workspace_bytes(B: int, V: int, dtype: torch.dtype = torch.float32) -> int:
     return int(lib().nucleus_workspace_bytes(int(B), int(V), code))
 
 
+_workspaces = {}
+
+
+def workspace_for(device: torch.device, stream: torch.cuda.Stream, nbytes: int) -> torch.Tensor:
+    """A workspace of at least ``nbytes``, cached per (device, stream): calls
+    on one stream are ordered, so they may share it (its contents need no
+    initial value)."""
+    key = (device.index, stream.cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
 def _check(code: int, what: str):
     if code != 0:
         raise NucleusError(f"{what}: {strerror(code)} ({code})")
@@ -116,13 +132,16 @@ class SampleResult(NamedTuple):
 
 def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, seed: int = 0, step: int = 0, *,
            want_probs: bool = False, want_min_kept: bool = False, out: Optional[SampleResult] = None,
-           workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> SampleResult:
+           workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
+           single_workgroup: bool = False) -> SampleResult:
     """Sample one token per row of ``logits`` [B, V] (float32 or bfloat16 on a
     gfx950 device; rows may be strided, the last dimension must be dense).
 
     Launches on ``stream`` (default: the current stream) and returns without
     synchronising.  ``out`` may supply preallocated outputs; ``workspace`` a
-    preallocated byte tensor of at least ``workspace_bytes(B, V, dtype)``.
+    byte tensor of at least ``workspace_bytes(B, V, dtype)`` (by default one
+    is cached per device and stream).  ``single_workgroup`` runs
+    every row on one workgroup that re-reads the row (same results, slower).
     """
     if logits.dim() != 2:
         raise ValueError("logits must be [B, V]")
@@ -144,13 +163,13 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
             torch.empty((B, V), dtype=torch.float32, device=dev) if want_probs else None,
             torch.empty(B, dtype=torch.float32, device=dev) if want_min_kept else None,
         )
-    need = workspace_bytes(B, V, logits.dtype)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
+    need = 0 if single_workgroup else workspace_bytes(B, V, logits.dtype)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = workspace_for(dev, s, need)
     opt = _Options()
     opt.dtype = code
-    opt.flags = 0
+    opt.flags = NUCLEUS_FLAG_SINGLE_WORKGROUP if single_workgroup else 0
     opt.stream = s.cuda_stream
     opt.row_stride = logits.stride(0) if B > 1 else V
     opt.workspace = workspace.data_ptr() if (workspace is not None and need) else None

@@ -107,14 +107,22 @@ __device__ __forceinline__ uint64_t race_pack(float score, uint32_t idx)
     return ((uint64_t)__float_as_uint(score) << 32) | (uint64_t)(~idx);
 }
 
-// floor(e * 2^shift) for e in [0, 1] and 32 <= shift <= 40, exactly.
-__device__ __forceinline__ uint64_t to_fixed(float e, int shift)
+// ---------------------------------------------------------------------------
+// Wave-uniform values (moved to scalar registers).  The argument must be the
+// same in every active lane.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform(float v) { return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v))); }
+__device__ __forceinline__ uint64_t uniform(uint64_t v)
 {
-    const float hi_f = floorf(ldexpf(e, shift - 32));       // <= 2^8, exact
-    const float frac = ldexpf(e, shift - 32) - hi_f;        // exact
-    const uint32_t lo = (uint32_t)ldexpf(frac, 32);         // truncates below 2^-shift
-    return ((uint64_t)(uint32_t)hi_f << 32) | lo;
+    // readfirstlane returns int: widen through uint32_t so the low word is not
+    // sign-extended into the high word.
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
+__device__ __forceinline__ double uniform(double v) { return __longlong_as_double((long long)uniform((uint64_t)__double_as_longlong(v))); }
 
 // ---------------------------------------------------------------------------
 // Wave and workgroup reductions (wave64 shuffles; LDS across waves).

@@ -1,0 +1,284 @@
+// model.h -- the arithmetic that decides which tokens are kept.
+//
+// Every path of the sampler (the register-resident split-row kernel, the
+// single-workgroup kernel, the last-arriving workgroup's resolver) uses these
+// functions and nothing else to weigh tokens, so they all take identical
+// decisions, bit for bit.
+//
+// Weights.  With m the row max and T > 0, token i weighs e_i = exp(-d_i),
+// d_i = (m - x_i)/T (the tempered softmax numerator, "What do temperature,
+// top-k and top-p each do ...", tempered-softmax equation).  d is cut into
+// kBins bins of width w (in d units) covering [0, D), D = min(32,
+// (m - min x)/T), so the bins adapt to the row's spread; the last bin also
+// takes every token with d >= D (each such token weighs < e^-32, so the
+// whole tail moves S by less than V e^-32 relative).  Bin j's upper edge
+// weighs exp(-j w).  Within its bin a token's weight relative to that edge,
+// exp(-f w) with f in [0, 1), is held as the integer
+//     fx = floor(2^31 * P(f)),   P = cubic Taylor polynomial of exp(-f w),
+// (w <= 1/32 keeps the truncation below 4e-8 relative; rows with wider bins
+// use exp2 instead), so a token weighs
+// exp(-j w) * fx * 2^-31 and each bin's weight is an exact integer sum:
+// associative, hence identical whatever order workgroups or lanes add in.
+//
+// Rules.  A token survives min-p iff x >= max + T ln(min_p) (rounded up to
+// fp32; p_i >= min_p * p_max is exactly that inequality).  The cut search
+// first locates the crossing bin from bin sums, then resolves the exact cut
+// level inside it over integer weights (select.h).  Only bins and the exact
+// cut level matter: the bin index is a monotone function of the logit, so
+// ties always share a bin and a fate.
+#pragma once
+
+#include "common.h"
+
+namespace nucleus {
+
+constexpr int kBins = 1024;
+constexpr double kFx = 2147483648.0;  // 2^31
+
+// Row modes decided after the row max is known.
+enum : uint32_t {
+    kModeError = 1,   // NaN/+inf logit, NaN parameter or no finite logit
+    kModeGreedy = 2,  // T <= 0: argmax, lowest index
+    kModeTop = 3,     // p <= 0 (and top-k not binding): the top level only
+    kModeAll = 4,     // p >= 1 (and top-k not binding): every survivor
+    kModeP = 5,       // top-p cut inside one crossing bin
+    kModeK = 6,       // top-k binds: every survivor in bins <= the top-k crossing bin is a candidate
+    kModeHist = 7,    // (provisional) needs the histogram to decide between the above
+};
+
+struct RowModel {
+    float m;       // row max
+    float T;
+    float invT;    // 0 for T = +inf
+    float s;       // bins per logit unit: t = (m - x) * s, bin = floor(t)
+    float tmp;     // min-p threshold: survivor iff x >= tmp; -inf when off
+    float c0, c1, c2, c3;  // 2^31 * Taylor coefficients of exp(-f w)
+    double w;      // bin width in d units (0 when every token weighs the same)
+    double q;      // exp(-w), the weight ratio of neighbouring bin edges
+    float nwlog2;  // -w * log2(e), for rows whose bins are wider than 1/32 (wide != 0)
+    uint32_t wide; // 1 when w > 1/32 (only for a saturated s): in-bin weights use exp2
+};
+
+// Build the model of a row from its max, smallest finite logit and
+// parameters (T > 0).  Pure function of its arguments.
+__device__ __forceinline__ RowModel make_model(float m, float xmin, float T, float mp)
+{
+#pragma clang fp contract(off)
+    RowModel r;
+    r.m = m;
+    r.T = T;
+    r.invT = (T == INFINITY) ? 0.0f : 1.0f / T;
+    // Window span in logit units: min(range * (1 + 2^-10), 32 T); the small
+    // margin keeps the smallest logit strictly inside the last bin.
+    const float range = (m - xmin) * 1.0009765625f;
+    const float cap = 32.0f * T;
+    const float span = fminf(range, cap);
+    float s = (span > 0.0f) ? (float)kBins / span : 0.0f;
+    if (!(s <= 3.0e38f)) s = 3.0e38f;  // span underflowed: one wide bin 0
+    r.s = s;
+    // w <= 1/32 unless s saturated (a span below 3e-36 or T below 1e-37);
+    // such rows evaluate the in-bin weight with exp2 instead of the cubic.
+    const double w = (s > 0.0f && T != INFINITY) ? 1.0 / ((double)s * (double)T) : 0.0;
+    r.w = w;
+    r.wide = w > 1.0 / 32.0 ? 1u : 0u;
+    r.nwlog2 = (float)(-w * 1.4426950408889634);
+    r.q = exp(-w);
+    r.c0 = (float)kFx;
+    r.c1 = (float)(-w * kFx);
+    r.c2 = (float)(w * w * 0.5 * kFx);
+    r.c3 = (float)(-w * w * w * (1.0 / 6.0) * kFx);
+    // min-p: e_i >= mp  <=>  x_i >= m + T ln(mp); at T = +inf every weight is 1.
+    float tmp = -INFINITY;
+    const float mpc = mp > 1.0f ? 1.0f : mp;
+    if (mpc > 0.0f && T != INFINITY) {
+        const double t = (double)m + (double)T * log((double)mpc);
+        float tf = (float)t;
+        if ((double)tf < t) tf = nextafterf(tf, INFINITY);
+        tmp = tf;
+    }
+    r.tmp = tmp;
+    return r;
+}
+
+// The model with every field in scalar registers.
+__device__ __forceinline__ RowModel uniform(const RowModel& a)
+{
+    RowModel r;
+    r.m = uniform(a.m);
+    r.T = uniform(a.T);
+    r.invT = uniform(a.invT);
+    r.s = uniform(a.s);
+    r.tmp = uniform(a.tmp);
+    r.c0 = uniform(a.c0);
+    r.c1 = uniform(a.c1);
+    r.c2 = uniform(a.c2);
+    r.c3 = uniform(a.c3);
+    r.w = uniform(a.w);
+    r.q = uniform(a.q);
+    r.nwlog2 = uniform(a.nwlog2);
+    r.wide = uniform(a.wide);
+    return r;
+}
+
+__device__ __forceinline__ bool survives(const RowModel& r, float x)
+{
+    return x > -INFINITY && x >= r.tmp;
+}
+
+// Bin position of a finite logit: t >= 0, bin = min(floor(t), kBins - 1).
+__device__ __forceinline__ float bin_pos(const RowModel& r, float x)
+{
+#pragma clang fp contract(off)
+    return (r.m - x) * r.s;
+}
+
+__device__ __forceinline__ uint32_t bin_of(float t)
+{
+    const uint32_t j = (uint32_t)t;  // saturates for huge t
+    return j < (uint32_t)(kBins - 1) ? j : (uint32_t)(kBins - 1);
+}
+
+// Integer weight of a token relative to its bin's upper edge, in (0, 2^31].
+__device__ __forceinline__ uint32_t bin_fx(const RowModel& r, float t)
+{
+#pragma clang fp contract(off)
+    const float f = __builtin_amdgcn_fractf(t);
+    if (r.wide) return (uint32_t)(__builtin_amdgcn_exp2f(f * r.nwlog2) * (float)kFx);
+    const float p = fmaf(fmaf(fmaf(r.c3, f, r.c2), f, r.c1), f, r.c0);
+    return (uint32_t)p;
+}
+
+// Weight of bin j's upper edge, exp(-w)^j by binary powering (a fixed
+// sequence of at most 20 products, so every path computes the same double;
+// relative error below 1e-13).
+__device__ __forceinline__ double edge_weight(const RowModel& r, int j)
+{
+#pragma clang fp contract(off)
+    double acc = 1.0, sq = r.q;
+    for (int k = j; k; k >>= 1) {
+        if (k & 1) acc *= sq;
+        sq *= sq;
+    }
+    return acc;
+}
+
+// Weight of a token at the common 2^-40 scale used when several bins meet
+// (the top-k mode): floor(exp(-j w) * fx * 2^9).
+__device__ __forceinline__ uint64_t fixed40(const RowModel& r, uint32_t j, uint32_t fx)
+{
+#pragma clang fp contract(off)
+    return (uint64_t)(edge_weight(r, (int)j) * (double)fx * 512.0);
+}
+
+// Result of reading a full histogram.
+struct Decision {
+    uint32_t mode;     // kModeP, kModeK, kModeAll or kModeTop
+    uint32_t cbin;     // crossing bin (P) or last candidate bin (K)
+    uint64_t tc;       // mode P: keep a level of bin cbin iff sum fx above it < tc
+    double a_above;    // mode P: weight of bins < cbin
+    double s_total;    // weight of all survivors
+};
+
+// Sum of exp(-j w) * H[j] * 2^-31 over bins [0, nb) in a fixed order: 32
+// groups of 32 bins summed sequentially, then the groups in order.  Called
+// by one wave; every lane returns the same value.
+__device__ __forceinline__ double group_sum(const RowModel& r, const uint64_t* H, int g)
+{
+#pragma clang fp contract(off)
+    double acc = 0.0;
+    for (int j = 32 * g; j < 32 * g + 32; ++j)
+        if (H[j]) acc += edge_weight(r, j) * ((double)H[j] * (1.0 / kFx));
+    return acc;
+}
+
+// Decide how a row's cut is found from its merged histogram H (weights) and
+// C (counts of survivors per bin, only when k > 0).  Must be called by all
+// threads of one workgroup; `red` is workgroup scratch of >= 64 doubles.
+// Deterministic: the summation order is fixed, whatever the block size.
+__device__ Decision decide(const RowModel& r, const uint64_t* H, const uint32_t* C, int k, float p, double* red)
+{
+#pragma clang fp contract(off)
+    __shared__ Decision dec;
+    const int t = threadIdx.x;
+    if (t < 32) {  // group sums (32 groups of 32 bins) and counts
+        red[t] = group_sum(r, H, t);
+        uint64_t gc = 0;
+        if (C)
+            for (int j = 32 * t; j < 32 * t + 32; ++j) gc += C[j];
+        red[32 + t] = (double)gc;
+    }
+    __syncthreads();
+    if (t == 0) {
+        Decision d;
+        d.mode = kModeP;
+        d.cbin = 0;
+        d.tc = 0;
+        d.a_above = 0.0;
+        double S = 0.0;
+        uint64_t total = 0;
+        for (int g = 0; g < 32; ++g) {
+            S += red[g];
+            total += (uint64_t)red[32 + g];
+        }
+        d.s_total = S;
+        bool topk = false;
+        if (C && k > 0 && total > (uint64_t)k) {
+            // top-k binds: the first bin where the running count reaches k.
+            uint64_t run = 0;
+            int g = 0;
+            while (run + (uint64_t)red[32 + g] < (uint64_t)k) {
+                run += (uint64_t)red[32 + g];
+                ++g;
+            }
+            int j = 32 * g;
+            while (run + C[j] < (uint64_t)k) {
+                run += C[j];
+                ++j;
+            }
+            d.mode = kModeK;
+            d.cbin = (uint32_t)j;
+            topk = true;
+        }
+        if (!topk) {
+            if (p >= 1.0f) {
+                d.mode = kModeAll;
+            } else if (p <= 0.0f) {
+                d.mode = kModeTop;
+            } else {
+                // top-p: the first bin whose running weight (through it) reaches
+                // p*S.  Group prefixes use the same additions as S, and bins inside
+                // a group the same additions as its group sum, so the search always
+                // stops at a non-empty bin.
+                const double thr = (double)p * S;
+                double run = 0.0;
+                int g = 0;
+                while (g < 31 && run + red[g] < thr) {
+                    run += red[g];
+                    ++g;
+                }
+                int j = 32 * g;
+                double acc = 0.0;
+                for (; j < 32 * g + 31; ++j) {
+                    const double nxt = H[j] ? acc + edge_weight(r, j) * ((double)H[j] * (1.0 / kFx)) : acc;
+                    if (run + nxt >= thr) break;
+                    acc = nxt;
+                }
+                run = run + acc;
+                d.cbin = (uint32_t)j;
+                d.a_above = run;
+                // Inside bin j: keep a level iff its fx-sum above < (thr - run) / (e_j 2^-31).
+                const double q = (thr - run) / (edge_weight(r, j) * (1.0 / kFx));
+                uint64_t tc = (q <= 1.0) ? 1 : (uint64_t)ceil(q);
+                if (!(q < 1.8e19)) tc = ~0ull;
+                d.tc = tc;
+            }
+        }
+        dec = d;
+    }
+    __syncthreads();
+    const Decision out = dec;
+    __syncthreads();
+    return out;
+}
+
+}  // namespace nucleus

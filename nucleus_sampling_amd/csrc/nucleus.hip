@@ -4,13 +4,16 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <atomic>
+#include <chrono>
 #include <mutex>
 
 #include "nucleus.h"
 #include "common.h"
 #include "params.h"
-#include "row_kernel.h"
+#include "sampler.h"
 #include "stream_read.h"
+#include "workspace.h"
 
 using namespace nucleus;
 
@@ -34,19 +37,24 @@ int check_device()
     return known[dev] == 1 ? NUCLEUS_OK : NUCLEUS_EDEVICE;
 }
 
-int ceil_log2(int64_t v)
+// Workgroups per row on the split-row path, or 0 when rows are too long for it.
+int chunks_for(int64_t V)
 {
-    int r = 0;
-    while ((int64_t(1) << r) < v) ++r;
-    return r;
+    const int64_t K = (V + kChunk - 1) / kChunk;
+    return K <= kMaxChunks ? (int)K : 0;
 }
 
-// Fixed-point scale of token weights: each weight is < 2^shift + 1 and a row
-// sums at most V of them, so V * 2^shift must stay below 2^63.
-int mass_shift_for(int64_t V)
+// A distinct 56-bit tag per call.  The sequence starts at a value derived
+// from this process (so tags of different processes rarely meet) and steps
+// by one; stale barrier words never carry the current tag.
+uint64_t next_epoch()
 {
-    const int s = 62 - ceil_log2(V);
-    return s < 40 ? s : 40;
+    static std::atomic<uint64_t> counter{0};
+    static const uint64_t base = [] {
+        const uint64_t t = (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
+        return (t * 0x9E3779B97F4A7C15ull) ^ ((uint64_t)(uintptr_t)&counter << 17);
+    }();
+    return (base + counter.fetch_add(1) + 1) & ((uint64_t(1) << 56) - 1);
 }
 
 template <class T>
@@ -59,7 +67,7 @@ bool aligned(const T* p)
 
 extern "C" {
 
-int nucleus_version(void) { return 100; }
+int nucleus_version(void) { return 200; }
 
 const char* nucleus_strerror(int code)
 {
@@ -76,7 +84,9 @@ const char* nucleus_strerror(int code)
 size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype)
 {
     if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16)) return 0;
-    return 0;
+    const int K = chunks_for(V);
+    if (B == 0 || K == 0) return 0;
+    return work_layout(B, K, kBins).total;
 }
 
 int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temperature, const float* top_p,
@@ -87,7 +97,8 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     const int64_t stride = (opt && opt->row_stride) ? opt->row_stride : V;
     if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || stride < V) return NUCLEUS_EINVAL;
     if (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16) return NUCLEUS_EINVAL;
-    if (opt && opt->flags != 0) return NUCLEUS_EINVAL;
+    if (opt && (opt->flags & ~NUCLEUS_FLAG_SINGLE_WORKGROUP) != 0) return NUCLEUS_EINVAL;
+    const bool single = opt && (opt->flags & NUCLEUS_FLAG_SINGLE_WORKGROUP);
     if (B == 0) return NUCLEUS_OK;
     if (!logits || !temperature || !top_p || !out_token || !out_keep_count) return NUCLEUS_EINVAL;
     const size_t esz = dtype == NUCLEUS_F32 ? 4 : 2;
@@ -95,8 +106,10 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
         (min_p && !aligned(min_p)) || !aligned(out_token) || !aligned(out_keep_count) ||
         (out_probs && !aligned(out_probs)) || (opt && opt->out_min_kept_logit && !aligned(opt->out_min_kept_logit)))
         return NUCLEUS_EINVAL;
-    const size_t need = nucleus_workspace_bytes(B, V, dtype);
-    if (need > 0 && (!opt || !opt->workspace || opt->workspace_bytes < need)) return NUCLEUS_EWORKSPACE;
+    const int K = single ? 0 : chunks_for(V);
+    const size_t need = K ? work_layout(B, K, kBins).total : 0;
+    if (need > 0 && (!opt || !opt->workspace || opt->workspace_bytes < need || (uintptr_t)opt->workspace % 256))
+        return NUCLEUS_EWORKSPACE;
     const int dev_rc = check_device();
     if (dev_rc != NUCLEUS_OK) return dev_rc;
 
@@ -119,14 +132,32 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     p.out_min_kept = opt ? opt->out_min_kept_logit : nullptr;
     const size_t vec_bytes = dtype == NUCLEUS_F32 ? 16 : 8;
     p.vec_in = ((uintptr_t)logits % vec_bytes == 0) && ((size_t)stride * esz) % vec_bytes == 0;
-    p.mass_shift = mass_shift_for(V);
 
     hipStream_t s = opt ? (hipStream_t)opt->stream : nullptr;
-    const dim3 grid((unsigned)B), block(kRowBlock);
-    if (dtype == NUCLEUS_F32)
-        hipLaunchKernelGGL(row_sample_kernel<kF32>, grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL(row_sample_kernel<kBF16>, grid, block, 0, s, p);
+    if (K) {
+        const WorkLayout L = work_layout(B, K, kBins);
+        char* ws = (char*)opt->workspace;
+        Work wk;
+        wk.ctl = (RowCtl*)(ws + L.ctl);
+        wk.slot_a = (uint4*)(ws + L.slot_a);
+        wk.slot_h = (uint64_t*)(ws + L.slot_h);
+        wk.slot_c = (uint32_t*)(ws + L.slot_c);
+        wk.slot_r = (RacePart*)(ws + L.slot_r);
+        wk.cand = (uint2*)(ws + L.cand);
+        wk.K = K;
+        wk.epoch = next_epoch();
+        const dim3 grid((unsigned)(padded_rows(B) * K)), block(kThreads);
+        if (dtype == NUCLEUS_F32)
+            hipLaunchKernelGGL(tile_kernel<kF32>, grid, block, 0, s, p, wk);
+        else
+            hipLaunchKernelGGL(tile_kernel<kBF16>, grid, block, 0, s, p, wk);
+    } else {
+        const dim3 grid((unsigned)B), block(kThreads);
+        if (dtype == NUCLEUS_F32)
+            hipLaunchKernelGGL(generic_kernel<kF32>, grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL(generic_kernel<kBF16>, grid, block, 0, s, p);
+    }
     return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
 }
 

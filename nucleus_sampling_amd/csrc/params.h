@@ -21,7 +21,6 @@ struct Params {
     float* out_probs;         // [B, V] or null
     float* out_min_kept;      // [B] or null
     int vec_in;               // rows start 16-byte (f32) / 8-byte (bf16) aligned
-    int mass_shift;           // token weights are summed as floor(e * 2^mass_shift)
 };
 
 }  // namespace nucleus

@@ -1,0 +1,898 @@
+// sampler.h -- the sampler's kernels.
+//
+// tile_kernel (the fast path, rows up to kMaxChunks * kChunk tokens):
+//   each row is split into K chunks of kChunk tokens; one 256-thread
+//   workgroup per chunk loads its chunk once from HBM into registers and
+//   keeps it there for every phase.  The K workgroups of a row meet at
+//   per-row barriers in the workspace; the last to arrive at each barrier
+//   merges what the others published and releases them:
+//     A  row max, smallest finite logit, error flag       -> row mode
+//     B  bin histograms of the survivors (model.h)         -> crossing bin
+//     C  race partials over the tokens surely kept, and the compacted tokens
+//        of the crossing bin -> the last arriver resolves the exact cut
+//        (select.h), races the kept candidates and writes the row's outputs.
+//   With out_probs the workgroups wait once more and write the renormalised
+//   probabilities of their chunk from registers.
+//   Workgroups of a row are consecutive in dispatch order on one XCD lane
+//   (blockIdx = ((row / 8) * K + chunk) * 8 + row % 8), and dispatch is in
+//   order, so the members of the lowest unfinished row are always resident
+//   and the barriers cannot deadlock; a bounded spin turns a violation of that
+//   assumption into a row error (token -2) instead of a hang.
+//
+// generic_kernel: one workgroup per row streaming the row from global memory
+//   for each phase, taking the same decisions with the same arithmetic.  It
+//   serves rows too long for the split path and, through the resolver, rows
+//   whose crossing bin holds more than kCap tokens.
+#pragma once
+
+#include "common.h"
+#include "model.h"
+#include "params.h"
+#include "select.h"
+#include "workspace.h"
+
+namespace nucleus {
+
+constexpr int kEPT = 32;                  // tokens per thread held in registers
+constexpr int kChunk = kThreads * kEPT;   // tokens per workgroup
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct MinF { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+struct SumU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+
+// ---------------------------------------------------------------------------
+// Loads: four consecutive tokens starting at i0 (a multiple of 4); tokens at or
+// past V read as -inf, which is never finite and never kept.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ void load4(const void* rowp, int64_t i0, int64_t V, int vec, float x[4])
+{
+    if (DT == kF32) {
+        const float* r = (const float*)rowp;
+        if (vec && i0 + 4 <= V) {
+            const f32x4 v = __builtin_nontemporal_load((const f32x4*)(r + i0));
+            x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = (i0 + j < V) ? r[i0 + j] : -INFINITY;
+        }
+    } else {
+        const uint16_t* r = (const uint16_t*)rowp;
+        if (vec && i0 + 4 <= V) {
+            const u32x2 v = __builtin_nontemporal_load((const u32x2*)(r + i0));
+            x[0] = __uint_as_float(v.x << 16);
+            x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+            x[2] = __uint_as_float(v.y << 16);
+            x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = (i0 + j < V) ? bf16_to_float(r[i0 + j]) : -INFINITY;
+        }
+    }
+}
+
+// Loads a workgroup's chunk into registers: x[4v + j] is token
+// lane0 + 1024 v + j.  Full, aligned chunks take straight-line vector loads
+// (the branch is uniform); otherwise every token is loaded from a clamped
+// address and masked, without divergent branches.
+template <int DT, int EPT>
+__device__ __forceinline__ void load_chunk(const void* rowp, uint32_t lane0, uint32_t chunk_end, uint32_t V, int vec,
+                                           float x[EPT])
+{
+    if (vec && chunk_end <= V) {
+        if (DT == kF32) {
+            const float* r = (const float*)rowp;
+#pragma unroll
+            for (int v = 0; v < EPT / 4; ++v) {
+                const f32x4 q = __builtin_nontemporal_load((const f32x4*)(r + lane0 + (uint32_t)v * (kThreads * 4)));
+                x[4 * v] = q.x; x[4 * v + 1] = q.y; x[4 * v + 2] = q.z; x[4 * v + 3] = q.w;
+            }
+        } else {
+            const uint16_t* r = (const uint16_t*)rowp;
+#pragma unroll
+            for (int v = 0; v < EPT / 4; ++v) {
+                const u32x2 q = __builtin_nontemporal_load((const u32x2*)(r + lane0 + (uint32_t)v * (kThreads * 4)));
+                x[4 * v] = __uint_as_float(q.x << 16);
+                x[4 * v + 1] = __uint_as_float(q.x & 0xFFFF0000u);
+                x[4 * v + 2] = __uint_as_float(q.y << 16);
+                x[4 * v + 3] = __uint_as_float(q.y & 0xFFFF0000u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const uint32_t i = lane0 + (uint32_t)(e >> 2) * (kThreads * 4) + (uint32_t)(e & 3);
+            const uint32_t c = i < V ? i : V - 1;
+            const float v = (DT == kF32) ? ((const float*)rowp)[c] : bf16_to_float(((const uint16_t*)rowp)[c]);
+            x[e] = i < V ? v : -INFINITY;
+        }
+    }
+}
+
+// Calls f(i0, x[4]) for every 4-token group of a row read from global memory.
+template <int DT, class F>
+__device__ __forceinline__ void row_groups(const Params& p, const void* rowp, F&& f)
+{
+    const int64_t ng = (p.V + 3) >> 2;
+    for (int64_t g = threadIdx.x; g < ng; g += kThreads) {
+        float x[4];
+        load4<DT>(rowp, g << 2, p.V, p.vec_in, x);
+        f(g << 2, x);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-row barrier in the workspace (sense-reversing: the last arrival leaves
+// the count at zero, and the last arriver bumps the generation the others
+// wait on once its merge is published).
+// ---------------------------------------------------------------------------
+struct BarrierShared {
+    uint32_t last, g0, timeout;
+};
+
+__device__ __forceinline__ bool barrier_arrive(RowCtl* c, uint32_t K, uint64_t epoch, BarrierShared& bs)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t g0 = __hip_atomic_load(&c->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // Count this arrival; a word tagged with another epoch is stale and
+        // restarts at one.  The last arrival leaves the count at zero.
+        uint64_t v = __hip_atomic_load(&c->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t n;
+        while (true) {
+            n = ((v >> 8) == epoch) ? (uint32_t)(v & 0xFFu) + 1u : 1u;
+            const uint64_t nv = (epoch << 8) | (n == K ? 0u : n);
+            if (__hip_atomic_compare_exchange_strong(&c->arrive, &v, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+                break;
+        }
+        bs.g0 = g0;
+        bs.last = (n == K) ? 1u : 0u;
+        bs.timeout = 0;
+        if (bs.last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    return bs.last != 0;
+}
+
+// Called by every thread of the last arriver once its merge is published.
+__device__ __forceinline__ void barrier_release(RowCtl* c)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(&c->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Every thread of a workgroup that arrived but was not last.  Returns false
+// if the wait timed out.
+__device__ __forceinline__ bool barrier_wait(RowCtl* c, BarrierShared& bs)
+{
+    if (threadIdx.x == 0) {
+        uint32_t n = 0;
+        while (__hip_atomic_load(&c->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == bs.g0) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++n > kSpinLimit) {
+                bs.timeout = 1;
+                break;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    return bs.timeout == 0;
+}
+
+// ---------------------------------------------------------------------------
+// Row state shared by the phases.
+// ---------------------------------------------------------------------------
+struct RowState {
+    uint32_t mode;
+    float m, xmin;
+    uint32_t cbin;
+    uint64_t tc;
+    double a_above, s_total, s_keep;
+    uint32_t token, count, cut_key;
+};
+
+// Mode of a row once its max is known (before any histogram).
+__device__ __forceinline__ uint32_t first_mode(bool bad, float m, float T, float P, float MP, int K, bool want_probs)
+{
+    if (bad || T != T || P != P || MP != MP || !(m > -INFINITY)) return kModeError;
+    if (T <= 0.0f) return kModeGreedy;
+    if (K > 0 || (P > 0.0f && P < 1.0f) || (P >= 1.0f && want_probs)) return kModeHist;
+    return P >= 1.0f ? kModeAll : kModeTop;
+}
+
+struct RowParams {
+    float T, P, MP;
+    int K;
+};
+
+__device__ __forceinline__ RowParams row_params(const Params& p, int64_t b)
+{
+    RowParams r;
+    r.T = p.temperature[b];
+    r.P = p.top_p[b];
+    r.MP = p.min_p ? p.min_p[b] : 0.0f;
+    r.K = p.top_k ? p.top_k[b] : 0;
+    return r;
+}
+
+struct RaceAcc {
+    uint64_t best;
+    uint32_t count, minkey;
+    __device__ void init() { best = 0; count = 0; minkey = 0xFFFFFFFFu; }
+};
+
+// The exact race score e_i / E_i of one token (e from the compensated
+// tempered weight, E from the token's Philox word).  Every path computes a
+// winner's score with this one function, so all paths agree bit for bit; the
+// hot loops only reach it for the few tokens that pass race_may_win.
+__device__ __forceinline__ float exact_score(float x, float m, float T, float invT, uint32_t word)
+{
+    return tempered_weight(x, m, T, invT) / exp1_from_word(word);
+}
+
+// Cheap screen before exact_score: a token can only reach the current best
+// score sstar if e_hat * (1 + 1e-4) >= sstar * w, where e_hat approximates
+// e_i to better than 3e-5 relative (|argument| <= 126 before underflow), and
+// w = 1 - u <= -ln u = E_i.  The comparison is strict in the rejecting
+// direction, so a token that could tie the best is never screened out.
+__device__ __forceinline__ bool race_may_win(float x, float m, float c_log2e, uint32_t word, float sstar)
+{
+    const float e_hat = __builtin_amdgcn_exp2f((x - m) * c_log2e);
+    const float w = ((float)(0xFFFFFFFFu - word) + 0.5f) * 0x1p-32f;
+    return !(e_hat * 1.0001f < sstar * w);
+}
+
+__device__ __forceinline__ uint32_t philox_word(const uint4& w4, uint32_t j)
+{
+    return j == 0 ? w4.x : j == 1 ? w4.y : j == 2 ? w4.z : w4.w;
+}
+
+// Race four consecutive tokens i0..i0+3 of which keep[j] are kept.  `scored`
+// is false for greedy rows, where every kept token scores 1 so that the
+// lowest index wins.  sstar is this lane's best exact score so far.
+__device__ __forceinline__ void race_group(const Params& p, int64_t b, bool scored, const RowModel& r, float c_log2e,
+                                           uint32_t i0, const float x[4], const bool keep[4], RaceAcc& acc,
+                                           float& sstar)
+{
+    if (!(keep[0] | keep[1] | keep[2] | keep[3])) return;
+    uint4 w4 = make_uint4(0, 0, 0, 0);
+    if (scored) w4 = philox4x32_10(make_uint4(i0 >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (!keep[j]) continue;
+        acc.count += 1;
+        const uint32_t k = order_key(x[j]);
+        acc.minkey = k < acc.minkey ? k : acc.minkey;
+        if (!scored) {
+            const uint64_t pk = race_pack(1.0f, i0 + j);
+            acc.best = pk > acc.best ? pk : acc.best;
+            continue;
+        }
+        const uint32_t word = philox_word(w4, j);
+        if (race_may_win(x[j], r.m, c_log2e, word, sstar)) {
+            const float s = exact_score(x[j], r.m, r.T, r.invT, word);
+            const uint64_t pk = race_pack(s, i0 + j);
+            acc.best = pk > acc.best ? pk : acc.best;
+            sstar = fmaxf(sstar, s);
+        }
+    }
+}
+
+// Race one token by index (resolver candidates).
+__device__ __forceinline__ void race_one(const Params& p, int64_t b, const RowModel& r, uint32_t key, uint32_t idx,
+                                         RaceAcc& acc)
+{
+    const uint4 w4 = philox4x32_10(make_uint4(idx >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
+    const float s = exact_score(key_value(key), r.m, r.T, r.invT, philox_word(w4, idx & 3));
+    const uint64_t pk = race_pack(s, idx);
+    acc.best = pk > acc.best ? pk : acc.best;
+    acc.count += 1;
+    acc.minkey = key < acc.minkey ? key : acc.minkey;
+}
+
+// The smallest logit whose bin is < c (c >= 1): bins fall as logits rise, so
+// this is a binary search over order keys between the lowest finite logit and
+// the row max (whose bin is 0).
+__device__ __forceinline__ float lowest_in_bins_below(const RowModel& r, uint32_t c)
+{
+    uint32_t lo = order_key(-3.4028234663852886e38f), hi = order_key(r.m);  // answer in [lo, hi]
+    if (bin_of(bin_pos(r, key_value(lo))) < c) return key_value(lo);
+    while (hi - lo > 1) {  // invariant: bin(lo) >= c, bin(hi) < c
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (bin_of(bin_pos(r, key_value(mid))) < c) hi = mid; else lo = mid;
+    }
+    return key_value(hi);
+}
+
+// Thresholds on the logit that classify the tokens of a row after its mode is
+// known: surely kept iff x >= keep_lo; candidate iff cand_lo <= x < keep_lo.
+struct Classes {
+    float keep_lo, cand_lo;
+};
+
+__device__ __forceinline__ Classes classify(const RowModel& r, const RowState& st)
+{
+    Classes c;
+    c.keep_lo = INFINITY;
+    c.cand_lo = INFINITY;
+    const float floor_ = fmaxf(r.tmp, -3.4028234663852886e38f);  // survivors: finite and >= tmp
+    switch (st.mode) {
+    case kModeGreedy:
+    case kModeTop: c.keep_lo = st.m; break;
+    case kModeAll: c.keep_lo = floor_; break;
+    case kModeP:
+        if (st.cbin > 0) c.keep_lo = fmaxf(floor_, lowest_in_bins_below(r, st.cbin));
+        c.cand_lo = (st.cbin + 1 < (uint32_t)kBins) ? fmaxf(floor_, lowest_in_bins_below(r, st.cbin + 1)) : floor_;
+        break;
+    case kModeK:
+        c.cand_lo = (st.cbin + 1 < (uint32_t)kBins) ? fmaxf(floor_, lowest_in_bins_below(r, st.cbin + 1)) : floor_;
+        break;
+    default: break;
+    }
+    return c;
+}
+
+struct ResolveShared {
+    SelectShared sel;
+    uint64_t red64[kThreads / kWave];
+    uint32_t red32[kThreads / kWave];
+};
+
+// Merge partial race accumulators of the workgroup (all threads return the merge).
+__device__ __forceinline__ RaceAcc block_race(RaceAcc a, ResolveShared& rs)
+{
+    RaceAcc o;
+    o.best = block_reduce<kThreads>(a.best, MaxU64(), rs.red64);
+    o.count = block_reduce<kThreads>(a.count, SumU32(), rs.red32);
+    o.minkey = block_reduce<kThreads>(a.minkey, MinU32(), rs.red32);
+    return o;
+}
+
+// The last step of a row: given the merged race partial of the surely kept
+// tokens (`part`) and a way to visit the candidates (`visit(fn(key, idx))`),
+// find the exact cut, race the kept candidates and fill st.token / count /
+// cut_key / s_keep.  All threads; uniform control flow.
+template <class Visit>
+__device__ void resolve_row(const Params& p, int64_t b, const RowModel& r, const RowParams& rp, RowState& st,
+                            RaceAcc part, Visit visit, ResolveShared& rs)
+{
+    if (st.mode == kModeError) {
+        st.token = 0xFFFFFFFFu;
+        st.count = 0;
+        st.cut_key = 0;
+        st.s_keep = 0.0;
+        return;
+    }
+    if (st.mode == kModeGreedy) {
+        st.token = ~(uint32_t)part.best;
+        st.count = 1;
+        st.cut_key = order_key(st.m);
+        st.s_keep = 1.0;
+        return;
+    }
+    RaceAcc acc = part;
+    if (st.mode == kModeTop) {
+        st.s_keep = (double)acc.count;  // every top-level token weighs exactly 1
+    } else if (st.mode == kModeAll) {
+        st.s_keep = st.s_total;
+    } else if (st.mode == kModeP) {
+        const uint64_t tc = st.tc;
+        const SelectResult sr = select_level(
+            [&](auto&& fn) {
+                visit([&](uint32_t key, uint32_t) { fn(key, (uint64_t)bin_fx(r, bin_pos(r, key_value(key)))); });
+            },
+            [&](uint64_t) { return tc; }, rs.sel);
+        const uint32_t cut = sr.level;
+        RaceAcc c;
+        c.init();
+        visit([&](uint32_t key, uint32_t idx) {
+            if (key >= cut) race_one(p, b, r, key, idx, c);
+        });
+        c = block_race(c, rs);
+        acc.best = c.best > acc.best ? c.best : acc.best;
+        acc.count += c.count;
+        acc.minkey = c.minkey < acc.minkey ? c.minkey : acc.minkey;
+        st.s_keep = st.a_above + edge_weight(r, (int)st.cbin) * ((double)(sr.above + sr.at) * (1.0 / kFx));
+    } else {  // kModeK: top-k binds; every candidate decision is taken here
+        const uint64_t kk = (uint64_t)rp.K;
+        const SelectResult tk = select_level(
+            [&](auto&& fn) { visit([&](uint32_t key, uint32_t) { fn(key, (uint64_t)1); }); },
+            [&](uint64_t) { return kk; }, rs.sel);
+        uint32_t cut = tk.level;
+        if (rp.P <= 0.0f) {
+            cut = order_key(st.m);
+        } else if (rp.P < 1.0f) {
+            const uint32_t vk = tk.level;
+            const float P = rp.P;
+            const SelectResult sp = select_level(
+                [&](auto&& fn) {
+                    visit([&](uint32_t key, uint32_t) {
+                        if (key >= vk) {
+                            const float t = bin_pos(r, key_value(key));
+                            fn(key, fixed40(r, bin_of(t), bin_fx(r, t)));
+                        }
+                    });
+                },
+                [&](uint64_t total) { return ceil_p_times(P, total); }, rs.sel);
+            cut = sp.level;
+        }
+        RaceAcc c;
+        c.init();
+        uint64_t kept_w = 0;
+        visit([&](uint32_t key, uint32_t idx) {
+            if (key >= cut) {
+                race_one(p, b, r, key, idx, c);
+                const float t = bin_pos(r, key_value(key));
+                kept_w += fixed40(r, bin_of(t), bin_fx(r, t));
+            }
+        });
+        c = block_race(c, rs);
+        kept_w = block_reduce<kThreads>(kept_w, SumU64(), rs.red64);
+        acc = c;
+        st.s_keep = (double)kept_w * 0x1p-40;
+    }
+    st.token = ~(uint32_t)acc.best;
+    st.count = acc.count;
+    st.cut_key = acc.minkey;
+}
+
+__device__ __forceinline__ void write_outputs(const Params& p, int64_t b, const RowState& st)
+{
+    if (threadIdx.x != 0) return;
+    if (st.mode == kModeError) {
+        p.out_token[b] = -1;
+        p.out_count[b] = 0;
+        if (p.out_min_kept) p.out_min_kept[b] = __uint_as_float(0x7FC00000u);
+        return;
+    }
+    p.out_token[b] = (int32_t)st.token;
+    p.out_count[b] = (int32_t)st.count;
+    if (p.out_min_kept) p.out_min_kept[b] = key_value(st.cut_key);
+}
+
+// Per-bin factors edge(j) * 2^-31 / S_keep for the probability pass.
+__device__ __forceinline__ void prob_factors(const RowModel& r, const RowState& st, float* factor)
+{
+    for (int j = threadIdx.x; j < kBins; j += kThreads)
+        factor[j] = (st.s_keep > 0.0) ? (float)(edge_weight(r, j) * (1.0 / kFx) / st.s_keep) : 0.0f;
+    __syncthreads();
+}
+
+__device__ __forceinline__ float prob_of(uint32_t mode, const RowModel& r, const RowState& st, const float* factor,
+                                         float x, int64_t i)
+{
+    if (mode == kModeError) return 0.0f;
+    if (mode == kModeGreedy) return (uint32_t)i == st.token ? 1.0f : 0.0f;
+    if (!(survives(r, x) && order_key(x) >= st.cut_key)) return 0.0f;
+    const float t = bin_pos(r, x);
+    return (float)bin_fx(r, t) * factor[bin_of(t)];
+}
+
+// ---------------------------------------------------------------------------
+// The split-row kernel.
+// ---------------------------------------------------------------------------
+struct TileShared {
+    union {
+        struct {
+            uint64_t hm[kBins];
+            uint32_t hc[kBins];
+        } h;
+        float factor[kBins];
+    } u;
+    ResolveShared rs;
+    double red[64];
+    float redf[kThreads / kWave];
+    int redi[kThreads / kWave];
+    uint32_t red32[kThreads / kWave];
+    BarrierShared bar;
+    RowState st;
+    uint32_t cand_base;
+};
+
+__device__ __forceinline__ RowState uniform(const RowState& a)
+{
+    RowState s;
+    s.mode = uniform(a.mode);
+    s.m = uniform(a.m);
+    s.xmin = uniform(a.xmin);
+    s.cbin = uniform(a.cbin);
+    s.tc = uniform(a.tc);
+    s.a_above = uniform(a.a_above);
+    s.s_total = uniform(a.s_total);
+    s.s_keep = uniform(a.s_keep);
+    s.token = uniform(a.token);
+    s.count = uniform(a.count);
+    s.cut_key = uniform(a.cut_key);
+    return s;
+}
+
+__device__ __forceinline__ void read_state(RowCtl* c, RowState& st)
+{
+    if (threadIdx.x == 0) {
+        st.mode = c->mode;
+        st.m = c->m;
+        st.xmin = c->xmin;
+        st.cbin = c->cbin;
+        st.tc = c->tc;
+        st.a_above = c->a_above;
+        st.s_total = c->s_total;
+        st.s_keep = c->s_keep;
+        st.token = c->token;
+        st.count = c->count;
+        st.cut_key = c->cut_key;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void timed_out(const Params& p, int64_t b)
+{
+    if (threadIdx.x == 0) p.out_token[b] = -2;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
+{
+    __shared__ TileShared sh;
+    const uint32_t K = (uint32_t)wk.K;
+    const uint32_t grp = blockIdx.x / (8u * K), rem = blockIdx.x % (8u * K);
+    const uint32_t chunk = rem >> 3;
+    const int64_t b = (int64_t)grp * 8 + (rem & 7);
+    if (b >= p.B) return;
+    const int t = threadIdx.x;
+    const int64_t esz = DT == kF32 ? 4 : 2;
+    const void* rowp = (const char*)p.logits + b * p.stride * esz;
+    const int64_t base = (int64_t)chunk * kChunk;
+    RowCtl* ctl = wk.ctl + b;
+    const int64_t wg = b * K + chunk;
+    const bool want_probs = p.out_probs != nullptr;
+
+    // ---- load the chunk into registers (token of x[4v+j]: lane0 + 1024 v + j)
+    float x[kEPT];
+    const uint32_t lane0 = (uint32_t)base + (uint32_t)t * 4u;
+    load_chunk<DT, kEPT>(rowp, lane0, (uint32_t)base + kChunk, (uint32_t)p.V, p.vec_in, x);
+
+    // ---- A: row max, smallest finite logit, NaN / +inf
+    float lmax = -INFINITY, lmin = INFINITY;
+    int bad = 0;
+#pragma unroll
+    for (int e = 0; e < kEPT; ++e) {
+        const float v = x[e];
+        bad |= (v != v) | (v == INFINITY);
+        lmax = fmaxf(lmax, v);
+        lmin = (v > -INFINITY) ? fminf(lmin, v) : lmin;
+    }
+    lmax = block_reduce<kThreads>(lmax, MaxF(), sh.redf);
+    lmin = block_reduce<kThreads>(lmin, MinF(), sh.redf);
+    bad = block_reduce<kThreads>(bad, OrI32(), sh.redi);
+    if (t == 0) wk.slot_a[wg] = make_uint4(__float_as_uint(lmax), __float_as_uint(lmin), (uint32_t)bad, 0u);
+    const RowParams rp = row_params(p, b);
+
+    if (barrier_arrive(ctl, K, wk.epoch, sh.bar)) {
+        float m = -INFINITY, mn = INFINITY;
+        int e = 0;
+        for (uint32_t k = t; k < K; k += kThreads) {
+            const uint4 a = wk.slot_a[b * K + k];
+            m = fmaxf(m, __uint_as_float(a.x));
+            mn = fminf(mn, __uint_as_float(a.y));
+            e |= (int)a.z;
+        }
+        m = block_reduce<kThreads>(m, MaxF(), sh.redf);
+        mn = block_reduce<kThreads>(mn, MinF(), sh.redf);
+        e = block_reduce<kThreads>(e, OrI32(), sh.redi);
+        if (t == 0) {
+            ctl->m = m;
+            ctl->xmin = mn;
+            ctl->mode = first_mode(e != 0, m, rp.T, rp.P, rp.MP, rp.K, want_probs);
+        }
+        barrier_release(ctl);
+    } else if (!barrier_wait(ctl, sh.bar)) {
+        timed_out(p, b);
+        return;
+    }
+    read_state(ctl, sh.st);
+    RowState st = uniform(sh.st);
+    RowModel model = {};
+    if (st.mode >= kModeTop) model = uniform(make_model(st.m, st.xmin, rp.T, rp.MP));
+
+    // ---- B: bin histogram of the survivors
+    if (st.mode == kModeHist) {
+        const bool counts = rp.K > 0;
+        for (int i = t; i < kBins; i += kThreads) {
+            sh.u.h.hm[i] = 0;
+            sh.u.h.hc[i] = 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kEPT; ++e) {
+            if (survives(model, x[e])) {
+                const float tp = bin_pos(model, x[e]);
+                const uint32_t j = bin_of(tp);
+                atomicAdd((unsigned long long*)&sh.u.h.hm[j], (unsigned long long)bin_fx(model, tp));
+                if (counts) atomicAdd(&sh.u.h.hc[j], 1u);
+            }
+        }
+        __syncthreads();
+        uint64_t* my_h = wk.slot_h + wg * kBins;
+        uint32_t* my_c = wk.slot_c + wg * kBins;
+        for (int i = t; i < kBins; i += kThreads) {
+            my_h[i] = sh.u.h.hm[i];
+            if (counts) my_c[i] = sh.u.h.hc[i];
+        }
+        if (barrier_arrive(ctl, K, wk.epoch, sh.bar)) {
+            for (int i = t; i < kBins; i += kThreads) {
+                uint64_t s = 0;
+                uint32_t c = 0;
+                for (uint32_t k = 0; k < K; ++k) {
+                    s += wk.slot_h[(b * K + k) * kBins + i];
+                    if (counts) c += wk.slot_c[(b * K + k) * kBins + i];
+                }
+                sh.u.h.hm[i] = s;
+                sh.u.h.hc[i] = c;
+            }
+            __syncthreads();
+            const Decision d = decide(model, sh.u.h.hm, counts ? sh.u.h.hc : nullptr, rp.K, rp.P, sh.red);
+            if (t == 0) {
+                ctl->cand_n = 0;  // the candidates of this call are appended after this barrier
+                ctl->mode = d.mode;
+                ctl->cbin = d.cbin;
+                ctl->tc = d.tc;
+                ctl->a_above = d.a_above;
+                ctl->s_total = d.s_total;
+            }
+            barrier_release(ctl);
+        } else if (!barrier_wait(ctl, sh.bar)) {
+            timed_out(p, b);
+            return;
+        }
+        read_state(ctl, sh.st);
+        st = uniform(sh.st);
+    }
+
+    // ---- C: race the surely kept tokens, compact the candidates
+    const Classes cl = classify(model, st);
+    const float keep_lo = uniform(cl.keep_lo), cand_lo = uniform(cl.cand_lo);
+    const bool scored = st.mode != kModeGreedy;
+    const float c_log2e = uniform(model.invT * 1.4426950408889634f);
+    RaceAcc acc;
+    acc.init();
+    float sstar = 0.0f;
+    uint32_t ncand = 0;
+    const bool has_cands = st.mode == kModeP || st.mode == kModeK;
+#pragma unroll
+    for (int v = 0; v < kEPT / 4; ++v) {
+        const uint32_t i0 = lane0 + (uint32_t)v * (kThreads * 4);
+        bool keep[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            keep[j] = x[4 * v + j] >= keep_lo;
+            ncand += (x[4 * v + j] >= cand_lo && !keep[j]) ? 1u : 0u;
+        }
+        race_group(p, b, scored, model, c_log2e, i0, &x[4 * v], keep, acc, sstar);
+        if (scored) sstar = wave_reduce(sstar, MaxF());
+    }
+    if (has_cands) {
+        const uint64_t excl = block_exclusive_sum<kThreads>((uint64_t)ncand, sh.rs.red64);
+        const uint32_t total = (uint32_t)block_reduce<kThreads>((uint64_t)ncand, SumU64(), sh.rs.red64);
+        if (t == 0) sh.cand_base = total ? atomicAdd(&ctl->cand_n, total) : 0u;
+        __syncthreads();
+        uint32_t pos = sh.cand_base + (uint32_t)excl;
+        uint2* cand = wk.cand + b * kCap;
+#pragma unroll
+        for (int e = 0; e < kEPT; ++e) {
+            if (x[e] >= cand_lo && x[e] < keep_lo) {
+                if (pos < (uint32_t)kCap)
+                    cand[pos] = make_uint2(order_key(x[e]), lane0 + (uint32_t)(e >> 2) * (kThreads * 4) + (uint32_t)(e & 3));
+                ++pos;
+            }
+        }
+    }
+    acc = block_race(acc, sh.rs);
+    if (t == 0) {
+        RacePart rpart;
+        rpart.best = acc.best;
+        rpart.count = acc.count;
+        rpart.minkey = acc.minkey;
+        wk.slot_r[wg] = rpart;
+    }
+
+    if (barrier_arrive(ctl, K, wk.epoch, sh.bar)) {
+        RaceAcc part;
+        part.init();
+        for (uint32_t k = t; k < K; k += kThreads) {
+            const RacePart q = wk.slot_r[b * K + k];
+            part.best = q.best > part.best ? q.best : part.best;
+            part.count += q.count;
+            part.minkey = q.minkey < part.minkey ? q.minkey : part.minkey;
+        }
+        part = block_race(part, sh.rs);
+        uint32_t n = 0;
+        if (has_cands) {
+            if (t == 0) sh.cand_base = __hip_atomic_load(&ctl->cand_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            n = sh.cand_base;
+        }
+        if (n <= (uint32_t)kCap) {
+            const uint2* cand = wk.cand + b * kCap;
+            resolve_row(p, b, model, rp, st,
+                        part, [&](auto&& fn) {
+                            for (uint32_t i = t; i < n; i += kThreads) {
+                                const uint2 c = cand[i];
+                                fn(c.x, c.y);
+                            }
+                        },
+                        sh.rs);
+        } else {  // the crossing bin overflowed the list: visit the row in global memory
+            resolve_row(p, b, model, rp, st,
+                        part, [&](auto&& fn) {
+                            row_groups<DT>(p, rowp, [&](int64_t i0, const float* xs) {
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), (uint32_t)(i0 + j));
+                            });
+                        },
+                        sh.rs);
+        }
+        write_outputs(p, b, st);
+        if (t == 0) {
+            ctl->token = st.token;
+            ctl->count = st.count;
+            ctl->cut_key = st.cut_key;
+            ctl->s_keep = st.s_keep;
+        }
+        barrier_release(ctl);
+        if (!want_probs) return;
+        // The resolving workgroup re-reads its chunk so that its registers are
+        // free for the resolver; the others write from registers below.
+        if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors(model, st, sh.u.factor);
+        float* prow = p.out_probs + b * p.V;
+        for (int v = 0; v < kEPT / 4; ++v) {
+            const int64_t i0 = base + ((int64_t)v * kThreads + t) * 4;
+            float xs[4];
+            load4<DT>(rowp, i0, p.V, p.vec_in, xs);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (i0 + j < p.V) prow[i0 + j] = prob_of(st.mode, model, st, sh.u.factor, xs[j], i0 + j);
+        }
+        return;
+    }
+    if (!want_probs) return;
+    if (!barrier_wait(ctl, sh.bar)) {
+        timed_out(p, b);
+        return;
+    }
+    read_state(ctl, sh.st);
+    st = uniform(sh.st);
+
+    // ---- probabilities of this chunk, from registers
+    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors(model, st, sh.u.factor);
+    float* prow = p.out_probs + b * p.V;
+#pragma unroll
+    for (int v = 0; v < kEPT / 4; ++v) {
+        const uint32_t i0 = lane0 + (uint32_t)v * (kThreads * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i0 + j < (uint32_t)p.V) prow[i0 + j] = prob_of(st.mode, model, st, sh.u.factor, x[4 * v + j], i0 + j);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per row, every phase streamed from global memory.
+// ---------------------------------------------------------------------------
+struct GenericShared {
+    union {
+        struct {
+            uint64_t hm[kBins];
+            uint32_t hc[kBins];
+        } h;
+        float factor[kBins];
+    } u;
+    ResolveShared rs;
+    double red[64];
+    float redf[kThreads / kWave];
+    int redi[kThreads / kWave];
+};
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void generic_kernel(Params p)
+{
+    __shared__ GenericShared sh;
+    const int64_t b = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t esz = DT == kF32 ? 4 : 2;
+    const void* rowp = (const char*)p.logits + b * p.stride * esz;
+    const bool want_probs = p.out_probs != nullptr;
+
+    float lmax = -INFINITY, lmin = INFINITY;
+    int bad = 0;
+    row_groups<DT>(p, rowp, [&](int64_t, const float* xs) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float v = xs[j];
+            bad |= (v != v) | (v == INFINITY);
+            lmax = fmaxf(lmax, v);
+            lmin = (v > -INFINITY) ? fminf(lmin, v) : lmin;
+        }
+    });
+    lmax = block_reduce<kThreads>(lmax, MaxF(), sh.redf);
+    lmin = block_reduce<kThreads>(lmin, MinF(), sh.redf);
+    bad = block_reduce<kThreads>(bad, OrI32(), sh.redi);
+    const RowParams rp = row_params(p, b);
+    RowState st;
+    st.mode = first_mode(bad != 0, lmax, rp.T, rp.P, rp.MP, rp.K, want_probs);
+    st.m = lmax;
+    st.xmin = lmin;
+    st.cbin = 0;
+    st.tc = 0;
+    st.a_above = st.s_total = st.s_keep = 0.0;
+    RowModel model = {};
+    if (st.mode >= kModeTop) model = make_model(st.m, st.xmin, rp.T, rp.MP);
+
+    if (st.mode == kModeHist) {
+        const bool counts = rp.K > 0;
+        for (int i = t; i < kBins; i += kThreads) {
+            sh.u.h.hm[i] = 0;
+            sh.u.h.hc[i] = 0;
+        }
+        __syncthreads();
+        row_groups<DT>(p, rowp, [&](int64_t, const float* xs) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (survives(model, xs[j])) {
+                    const float tp = bin_pos(model, xs[j]);
+                    const uint32_t jb = bin_of(tp);
+                    atomicAdd((unsigned long long*)&sh.u.h.hm[jb], (unsigned long long)bin_fx(model, tp));
+                    if (counts) atomicAdd(&sh.u.h.hc[jb], 1u);
+                }
+            }
+        });
+        __syncthreads();
+        const Decision d = decide(model, sh.u.h.hm, counts ? sh.u.h.hc : nullptr, rp.K, rp.P, sh.red);
+        st.mode = d.mode;
+        st.cbin = d.cbin;
+        st.tc = d.tc;
+        st.a_above = d.a_above;
+        st.s_total = d.s_total;
+    }
+
+    const Classes cl = classify(model, st);
+    const float keep_lo = cl.keep_lo, cand_lo = cl.cand_lo;
+    const bool scored = st.mode != kModeGreedy;
+    const float c_log2e = model.invT * 1.4426950408889634f;
+    RaceAcc acc;
+    acc.init();
+    float sstar = 0.0f;
+    row_groups<DT>(p, rowp, [&](int64_t i0, const float* xs) {
+        bool keep[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) keep[j] = xs[j] >= keep_lo;
+        race_group(p, b, scored, model, c_log2e, (uint32_t)i0, xs, keep, acc, sstar);
+    });
+    acc = block_race(acc, sh.rs);
+    resolve_row(p, b, model, rp, st, acc,
+                [&](auto&& fn) {
+                    row_groups<DT>(p, rowp, [&](int64_t i0, const float* xs) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), (uint32_t)(i0 + j));
+                    });
+                },
+                sh.rs);
+    write_outputs(p, b, st);
+    if (!want_probs) return;
+    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors(model, st, sh.u.factor);
+    float* prow = p.out_probs + b * p.V;
+    row_groups<DT>(p, rowp, [&](int64_t i0, const float* xs) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i0 + j < p.V) prow[i0 + j] = prob_of(st.mode, model, st, sh.u.factor, xs[j], i0 + j);
+    });
+}
+
+}  // namespace nucleus

@@ -1,0 +1,83 @@
+// workspace.h -- layout of the caller-owned device workspace.
+//
+// Rows are padded to a multiple of 8 (one row per XCD lane of the dispatch
+// mapping).  Everything is plain device memory and needs no initial value:
+// barrier arrivals carry the call's 56-bit epoch, so the first arrival of a
+// call resets whatever the word held (a previous call, or another layout's
+// data); generations are only compared for change; the candidate count is
+// reset by the workgroup that publishes the crossing bin.
+#pragma once
+
+#include <stdint.h>
+
+namespace nucleus {
+
+constexpr int kCap = 8192;       // candidates per row handed to the resolver
+constexpr int kMaxChunks = 64;   // split-row path limit: V <= 64 * 16384
+
+// Per-row control block: barrier state and the values published at each
+// phase.  128 bytes.
+struct RowCtl {
+    uint64_t arrive;     // (call epoch << 8) | arrivals at the current barrier
+    uint32_t gen;        // barrier generation (bumped by the last arriver)
+    uint32_t cand_n;     // candidates appended this call
+    uint32_t mode;       // row mode (model.h)
+    float m;             // row max
+    float xmin;          // smallest finite logit
+    uint32_t cbin;       // crossing bin (mode P) / last candidate bin (mode K)
+    uint32_t cut_key;    // key of the smallest kept logit (published for the probability pass)
+    uint32_t count;      // kept count
+    uint64_t tc;         // mode P threshold inside the crossing bin
+    double a_above;      // mode P: weight of the bins above the crossing bin
+    double s_total;      // weight of all survivors
+    double s_keep;       // weight of the kept set
+    uint32_t token;      // sampled token (published for the probability pass)
+    uint32_t pad[13];
+};
+static_assert(sizeof(RowCtl) == 128, "RowCtl layout");
+
+// Per-workgroup partial of the race: best packed (score, ~index), kept
+// count, smallest kept key.
+struct RacePart {
+    uint64_t best;
+    uint32_t count;
+    uint32_t minkey;
+};
+
+struct Work {
+    RowCtl* ctl;          // [rows]
+    uint4* slot_a;        // [rows * K]: max bits, min bits, error flag, 0
+    uint64_t* slot_h;     // [rows * K][kBins] bin weights
+    uint32_t* slot_c;     // [rows * K][kBins] bin counts (top-k rows)
+    RacePart* slot_r;     // [rows * K]
+    uint2* cand;          // [rows][kCap]: key, index
+    int K;                // workgroups per row
+    uint64_t epoch;       // this call's tag (56 bits), distinct for every call
+};
+
+inline int64_t padded_rows(int64_t B) { return (B + 7) / 8 * 8; }
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Byte offsets of each region for a batch of B rows with K workgroups each.
+struct WorkLayout {
+    size_t ctl, slot_a, slot_h, slot_c, slot_r, cand, total;
+};
+
+inline WorkLayout work_layout(int64_t B, int K, int bins)
+{
+    const size_t rows = (size_t)padded_rows(B);
+    const size_t wgs = rows * (size_t)K;
+    WorkLayout L;
+    size_t off = 0;
+    L.ctl = off; off = align256(off + rows * sizeof(RowCtl));
+    L.slot_a = off; off = align256(off + wgs * 16);
+    L.slot_h = off; off = align256(off + wgs * (size_t)bins * 8);
+    L.slot_c = off; off = align256(off + wgs * (size_t)bins * 4);
+    L.slot_r = off; off = align256(off + wgs * sizeof(RacePart));
+    L.cand = off; off = align256(off + rows * (size_t)kCap * 8);
+    L.total = off;
+    return L;
+}
+
+}  // namespace nucleus

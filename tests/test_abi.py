@@ -82,8 +82,11 @@ def test_host_side_argument_errors(L):
     opt.row_stride = 4  # < V
     assert _call(L, opt=ctypes.byref(opt)) == EINVAL
     opt = ns._Options()
-    opt.flags = 1
+    opt.flags = 2  # undefined flag bit
     assert _call(L, opt=ctypes.byref(opt)) == EINVAL
+    # The default path needs a workspace for these shapes.
+    opt = ns._Options()
+    assert _call(L, opt=ctypes.byref(opt)) == -2
 
 
 def test_empty_batch_launches_nothing(L):

@@ -15,14 +15,15 @@ from gpu_util import device_logits, oracle_and_compare, say
 pytestmark = pytest.mark.gpu
 
 
-def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None):
+def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None, single=False):
     import torch
 
     import nucleus_sampling_amd as ns
 
     lg = device_logits(w["logits"], w["dtype"]) if lg is None else lg
     res = ns.sample(lg, w["temperature"], w["top_p"], w["top_k"], w["min_p"],
-                    seed=w["seed"] if seed is None else seed, step=step, want_probs=want_probs, want_min_kept=True)
+                    seed=w["seed"] if seed is None else seed, step=step, want_probs=want_probs, want_min_kept=True,
+                    single_workgroup=single)
     torch.cuda.synchronize()
     probs = None
     if want_probs:
@@ -222,3 +223,48 @@ def test_draws_match_oracle_on_worked_example():
     f = np.bincount(tok, minlength=16) / n
     assert f[3:].sum() == 0
     assert np.allclose(f[:3], [0.6522, 0.2399, 0.1078], atol=0.015)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_split_row_equals_single_workgroup(n):
+    """The register-resident split-row path and the single-workgroup path take
+    the same decisions with the same arithmetic: identical outputs, bit for
+    bit, including the probabilities."""
+    rows = PROB_ROWS[n]
+    say(f"workload {n}: split-row vs single-workgroup")
+    w = workloads.make(n)
+    import torch
+
+    lg = device_logits(w["logits"], w["dtype"])
+    a = _gpu(w, lg=lg, want_probs=True, prob_rows=rows)
+    b = _gpu(w, lg=lg, want_probs=True, prob_rows=rows, single=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
+    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_crossing_bin_overflow(dtype):
+    """Rows whose crossing bin holds more tokens than the resolver's list (one
+    or two tied levels over 40,001 tokens) are resolved by re-reading the row;
+    results still match the oracle and the single-workgroup path."""
+    V = 40001
+    rng = np.random.default_rng(5)
+    L = np.zeros((6, V), np.float32)
+    L[1, rng.random(V) < 0.5] = 1.0            # two levels, ~20K tokens each
+    L[2] = rng.integers(-1, 2, V)              # three levels
+    L[3, :] = 0.25                             # one level
+    L[4] = rng.normal(0, 1e-6, V)              # near-constant: one narrow bin
+    L[5, ::3] = -np.inf
+    T = np.asarray([1.0, 1.0, 0.5, 2.0, 1.0, 1.0], np.float32)
+    P = np.asarray([0.5, 0.6, 0.95, 0.1, 0.5, 0.99], np.float32)
+    w = dict(logits=workloads.f32_to_bf16_bits(L) if dtype == "bf16" else L, dtype=dtype, temperature=T, top_p=P,
+             top_k=np.zeros(6, np.int32), min_p=np.zeros(6, np.float32), seed=77, B=6, V=V)
+    say(f"crossing-bin overflow rows {dtype}")
+    a = _gpu(w, want_probs=True, prob_rows=range(6))
+    rep, _ = oracle_and_compare(w, *a[:3], gpu_probs=a[3], prob_rows=list(range(6)))
+    say(f"crossing-bin overflow {dtype}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+    b = _gpu(w, want_probs=True, prob_rows=range(6), single=True)
+    assert all(np.array_equal(np.asarray(x).view(np.uint32), np.asarray(y).view(np.uint32)) for x, y in zip(a, b))
