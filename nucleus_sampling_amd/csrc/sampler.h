@@ -25,6 +25,8 @@
 //   whose crossing bin holds more than kCap tokens.
 #pragma once
 
+#include <stddef.h>
+
 #include "common.h"
 #include "model.h"
 #include "params.h"
@@ -36,6 +38,8 @@ namespace nucleus {
 constexpr int kEPT = 32;                  // tokens per thread held in registers
 constexpr int kChunk = kThreads * kEPT;   // tokens per workgroup
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kCandLds = 3072;             // candidates the resolver stages in LDS
+constexpr int kMergeBatch = 4;           // loads in flight per thread in the histogram merge
 
 struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
 struct MinF { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
@@ -123,6 +127,77 @@ __device__ __forceinline__ void row_groups(const Params& p, const void* rowp, F&
 }
 
 // ---------------------------------------------------------------------------
+// Cross-workgroup traffic.  Everything one workgroup publishes for another is
+// written with device-coherent stores and read with device-coherent loads
+// (relaxed agent-scope atomics: `sc1` accesses that bypass the per-XCD
+// caches), so no cache-wide writeback or invalidate is ever needed.  Before a
+// workgroup signals, every wave waits until its own stores have completed
+// (s_waitcnt 0), and the signal is an atomic performed after that.
+// ---------------------------------------------------------------------------
+template <class T>
+__device__ __forceinline__ void put(T* p, T v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class T>
+__device__ __forceinline__ T get(const T* p)
+{
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bulk coherent traffic goes through buffer instructions carrying the same
+// device-coherence bit (sc1) as the atomics above, but without the
+// per-access waits the compiler attaches to atomics, so many loads can be in
+// flight at once.  A resource covers up to 2 GB from `base`.
+constexpr int kSC1 = 16;  // cache-policy bits: device-coherent (sc1)
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint64_t join64(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent(const void* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ uint32_t cload32(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSC1);
+}
+__device__ __forceinline__ uint64_t cload64(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSC1);
+    return ((uint64_t)v.y << 32) | v.x;
+}
+__device__ __forceinline__ u32x4v cload128(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1);
+}
+__device__ __forceinline__ void cstore32(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kSC1);
+}
+__device__ __forceinline__ void cstore128(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4v v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSC1);
+}
+__device__ __forceinline__ void cstore64(__amdgpu_buffer_rsrc_t r, uint32_t off, uint64_t v)
+{
+    u32x2v w;
+    w.x = (uint32_t)v;
+    w.y = (uint32_t)(v >> 32);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kSC1);
+}
+
+// Every wave of the workgroup waits for its outstanding memory operations,
+// then the workgroup synchronises: afterwards all its stores are complete.
+__device__ __forceinline__ void drain_and_sync()
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // Per-row barrier in the workspace (sense-reversing: the last arrival leaves
 // the count at zero, and the last arriver bumps the generation the others
 // wait on once its merge is published).
@@ -133,25 +208,27 @@ struct BarrierShared {
 
 __device__ __forceinline__ bool barrier_arrive(RowCtl* c, uint32_t K, uint64_t epoch, BarrierShared& bs)
 {
-    __syncthreads();
+    drain_and_sync();
     if (threadIdx.x == 0) {
-        const uint32_t g0 = __hip_atomic_load(&c->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        // Count this arrival; a word tagged with another epoch is stale and
-        // restarts at one.  The last arrival leaves the count at zero.
-        uint64_t v = __hip_atomic_load(&c->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t n;
-        while (true) {
-            n = ((v >> 8) == epoch) ? (uint32_t)(v & 0xFFu) + 1u : 1u;
-            const uint64_t nv = (epoch << 8) | (n == K ? 0u : n);
-            if (__hip_atomic_compare_exchange_strong(&c->arrive, &v, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT))
-                break;
+        const uint32_t g0 = get(&c->gen);
+        // The arrival word is (epoch << 8) | count.  The first arrival of a
+        // call finds another epoch there and installs (epoch, 1) by CAS; every
+        // other arrival is one atomic add.
+        uint32_t n = 0;
+        uint64_t v = get(&c->arrive);
+        if ((v >> 8) != epoch &&
+            __hip_atomic_compare_exchange_strong(&c->arrive, &v, (epoch << 8) | 1u, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            n = 1;
+        if (n == 0) {
+            const uint64_t old =
+                __hip_atomic_fetch_add(&c->arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            n = (uint32_t)(old & 0xFFu) + 1u;
         }
+        if (n == K) put(&c->arrive, epoch << 8);  // nobody arrives again before the release
         bs.g0 = g0;
         bs.last = (n == K) ? 1u : 0u;
         bs.timeout = 0;
-        if (bs.last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     return bs.last != 0;
@@ -160,11 +237,8 @@ __device__ __forceinline__ bool barrier_arrive(RowCtl* c, uint32_t K, uint64_t e
 // Called by every thread of the last arriver once its merge is published.
 __device__ __forceinline__ void barrier_release(RowCtl* c)
 {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(&c->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    drain_and_sync();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(&c->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Every thread of a workgroup that arrived but was not last.  Returns false
@@ -173,14 +247,13 @@ __device__ __forceinline__ bool barrier_wait(RowCtl* c, BarrierShared& bs)
 {
     if (threadIdx.x == 0) {
         uint32_t n = 0;
-        while (__hip_atomic_load(&c->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == bs.g0) {
-            __builtin_amdgcn_s_sleep(2);
+        while (get(&c->gen) == bs.g0) {
+            __builtin_amdgcn_s_sleep(1);
             if (++n > kSpinLimit) {
                 bs.timeout = 1;
                 break;
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     return bs.timeout == 0;
@@ -485,6 +558,7 @@ struct TileShared {
             uint32_t hc[kBins];
         } h;
         float factor[kBins];
+        u32x2v cand[kCandLds];  // the row's candidates, staged for the resolver
     } u;
     ResolveShared rs;
     double red[64];
@@ -513,20 +587,34 @@ __device__ __forceinline__ RowState uniform(const RowState& a)
     return s;
 }
 
+// Byte offsets of the published fields of RowCtl.
+constexpr uint32_t kOffMode = 16, kOffM = 20, kOffXmin = 24, kOffCbin = 28, kOffCut = 32, kOffCount = 36,
+                   kOffTc = 40, kOffAbove = 48, kOffStotal = 56, kOffSkeep = 64, kOffToken = 72, kOffCandN = 12;
+
+static_assert(offsetof(RowCtl, cand_n) == kOffCandN && offsetof(RowCtl, mode) == kOffMode &&
+                  offsetof(RowCtl, m) == kOffM && offsetof(RowCtl, xmin) == kOffXmin &&
+                  offsetof(RowCtl, cbin) == kOffCbin && offsetof(RowCtl, cut_key) == kOffCut &&
+                  offsetof(RowCtl, count) == kOffCount && offsetof(RowCtl, tc) == kOffTc &&
+                  offsetof(RowCtl, a_above) == kOffAbove && offsetof(RowCtl, s_total) == kOffStotal &&
+                  offsetof(RowCtl, s_keep) == kOffSkeep && offsetof(RowCtl, token) == kOffToken,
+              "RowCtl field offsets");
+
 __device__ __forceinline__ void read_state(RowCtl* c, RowState& st)
 {
     if (threadIdx.x == 0) {
-        st.mode = c->mode;
-        st.m = c->m;
-        st.xmin = c->xmin;
-        st.cbin = c->cbin;
-        st.tc = c->tc;
-        st.a_above = c->a_above;
-        st.s_total = c->s_total;
-        st.s_keep = c->s_keep;
-        st.token = c->token;
-        st.count = c->count;
-        st.cut_key = c->cut_key;
+        const __amdgpu_buffer_rsrc_t r = coherent(c);
+        const u32x4v q1 = cload128(r, 16), q2 = cload128(r, 32), q3 = cload128(r, 48), q4 = cload128(r, 64);
+        st.mode = q1.x;
+        st.m = __uint_as_float(q1.y);
+        st.xmin = __uint_as_float(q1.z);
+        st.cbin = q1.w;
+        st.cut_key = q2.x;
+        st.count = q2.y;
+        st.tc = join64(q2.z, q2.w);
+        st.a_above = __longlong_as_double((long long)join64(q3.x, q3.y));
+        st.s_total = __longlong_as_double((long long)join64(q3.z, q3.w));
+        st.s_keep = __longlong_as_double((long long)join64(q4.x, q4.y));
+        st.token = q4.z;
     }
     __syncthreads();
 }
@@ -571,14 +659,22 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
     lmax = block_reduce<kThreads>(lmax, MaxF(), sh.redf);
     lmin = block_reduce<kThreads>(lmin, MinF(), sh.redf);
     bad = block_reduce<kThreads>(bad, OrI32(), sh.redi);
-    if (t == 0) wk.slot_a[wg] = make_uint4(__float_as_uint(lmax), __float_as_uint(lmin), (uint32_t)bad, 0u);
+    if (t == 0) {
+        u32x4v a;
+        a.x = __float_as_uint(lmax);
+        a.y = __float_as_uint(lmin);
+        a.z = (uint32_t)bad;
+        a.w = 0;
+        cstore128(coherent(wk.slot_a + wg), 0, a);
+    }
     const RowParams rp = row_params(p, b);
 
     if (barrier_arrive(ctl, K, wk.epoch, sh.bar)) {
         float m = -INFINITY, mn = INFINITY;
         int e = 0;
+        const __amdgpu_buffer_rsrc_t ra = coherent(wk.slot_a + b * K);
         for (uint32_t k = t; k < K; k += kThreads) {
-            const uint4 a = wk.slot_a[b * K + k];
+            const u32x4v a = cload128(ra, k * 16);
             m = fmaxf(m, __uint_as_float(a.x));
             mn = fminf(mn, __uint_as_float(a.y));
             e |= (int)a.z;
@@ -587,9 +683,10 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
         mn = block_reduce<kThreads>(mn, MinF(), sh.redf);
         e = block_reduce<kThreads>(e, OrI32(), sh.redi);
         if (t == 0) {
-            ctl->m = m;
-            ctl->xmin = mn;
-            ctl->mode = first_mode(e != 0, m, rp.T, rp.P, rp.MP, rp.K, want_probs);
+            const __amdgpu_buffer_rsrc_t rc = coherent(ctl);
+            cstore32(rc, kOffM, __float_as_uint(m));
+            cstore32(rc, kOffXmin, __float_as_uint(mn));
+            cstore32(rc, kOffMode, first_mode(e != 0, m, rp.T, rp.P, rp.MP, rp.K, want_probs));
         }
         barrier_release(ctl);
     } else if (!barrier_wait(ctl, sh.bar)) {
@@ -619,32 +716,71 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
             }
         }
         __syncthreads();
-        uint64_t* my_h = wk.slot_h + wg * kBins;
-        uint32_t* my_c = wk.slot_c + wg * kBins;
+        const __amdgpu_buffer_rsrc_t rh = coherent(wk.slot_h + b * K * kBins);
+        const __amdgpu_buffer_rsrc_t rcn = coherent(wk.slot_c + b * K * kBins);
         for (int i = t; i < kBins; i += kThreads) {
-            my_h[i] = sh.u.h.hm[i];
-            if (counts) my_c[i] = sh.u.h.hc[i];
+            cstore64(rh, (uint32_t)((chunk * kBins + i) * 8), sh.u.h.hm[i]);
+            if (counts) cstore32(rcn, (uint32_t)((chunk * kBins + i) * 4), sh.u.h.hc[i]);
         }
         if (barrier_arrive(ctl, K, wk.epoch, sh.bar)) {
+            // Every thread takes 16-byte pieces (two bins) of every slot, eight
+            // loads in flight at a time, and adds them into LDS: the K slots are
+            // read in parallel rather than one round trip after another.
             for (int i = t; i < kBins; i += kThreads) {
-                uint64_t s = 0;
-                uint32_t c = 0;
-                for (uint32_t k = 0; k < K; ++k) {
-                    s += wk.slot_h[(b * K + k) * kBins + i];
-                    if (counts) c += wk.slot_c[(b * K + k) * kBins + i];
+                sh.u.h.hm[i] = 0;
+                sh.u.h.hc[i] = 0;
+            }
+            __syncthreads();
+            const uint32_t pieces = K * (kBins / 2);
+            for (uint32_t q0 = t; q0 < pieces; q0 += kMergeBatch * kThreads) {
+                u32x4v v[kMergeBatch];
+#pragma unroll
+                for (int u = 0; u < kMergeBatch; ++u) {
+                    const uint32_t q = q0 + u * kThreads;
+                    v[u] = cload128(rh, (q < pieces ? q : 0) * 16);
                 }
-                sh.u.h.hm[i] = s;
-                sh.u.h.hc[i] = c;
+#pragma unroll
+                for (int u = 0; u < kMergeBatch; ++u) {
+                    const uint32_t q = q0 + u * kThreads;
+                    if (q < pieces) {
+                        const uint32_t i = (q % (kBins / 2)) * 2;
+                        if (v[u].x | v[u].y) atomicAdd((unsigned long long*)&sh.u.h.hm[i], (unsigned long long)join64(v[u].x, v[u].y));
+                        if (v[u].z | v[u].w) atomicAdd((unsigned long long*)&sh.u.h.hm[i + 1], (unsigned long long)join64(v[u].z, v[u].w));
+                    }
+                }
+            }
+            if (counts) {
+                const uint32_t cpieces = K * (kBins / 4);
+                for (uint32_t q0 = t; q0 < cpieces; q0 += kMergeBatch * kThreads) {
+                    u32x4v v[kMergeBatch];
+#pragma unroll
+                    for (int u = 0; u < kMergeBatch; ++u) {
+                        const uint32_t q = q0 + u * kThreads;
+                        v[u] = cload128(rcn, (q < cpieces ? q : 0) * 16);
+                    }
+#pragma unroll
+                    for (int u = 0; u < kMergeBatch; ++u) {
+                        const uint32_t q = q0 + u * kThreads;
+                        if (q < cpieces) {
+                            const uint32_t i = (q % (kBins / 4)) * 4;
+                            if (v[u].x) atomicAdd(&sh.u.h.hc[i], v[u].x);
+                            if (v[u].y) atomicAdd(&sh.u.h.hc[i + 1], v[u].y);
+                            if (v[u].z) atomicAdd(&sh.u.h.hc[i + 2], v[u].z);
+                            if (v[u].w) atomicAdd(&sh.u.h.hc[i + 3], v[u].w);
+                        }
+                    }
+                }
             }
             __syncthreads();
             const Decision d = decide(model, sh.u.h.hm, counts ? sh.u.h.hc : nullptr, rp.K, rp.P, sh.red);
             if (t == 0) {
-                ctl->cand_n = 0;  // the candidates of this call are appended after this barrier
-                ctl->mode = d.mode;
-                ctl->cbin = d.cbin;
-                ctl->tc = d.tc;
-                ctl->a_above = d.a_above;
-                ctl->s_total = d.s_total;
+                const __amdgpu_buffer_rsrc_t rc = coherent(ctl);
+                put(&ctl->cand_n, 0u);  // the candidates of this call are appended after this barrier
+                cstore32(rc, kOffMode, d.mode);
+                cstore32(rc, kOffCbin, d.cbin);
+                cstore64(rc, kOffTc, d.tc);
+                cstore64(rc, kOffAbove, (uint64_t)__double_as_longlong(d.a_above));
+                cstore64(rc, kOffStotal, (uint64_t)__double_as_longlong(d.s_total));
             }
             barrier_release(ctl);
         } else if (!barrier_wait(ctl, sh.bar)) {
@@ -683,47 +819,76 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
         if (t == 0) sh.cand_base = total ? atomicAdd(&ctl->cand_n, total) : 0u;
         __syncthreads();
         uint32_t pos = sh.cand_base + (uint32_t)excl;
-        uint2* cand = wk.cand + b * kCap;
+        const __amdgpu_buffer_rsrc_t rk = coherent(wk.cand + b * kCap);
 #pragma unroll
         for (int e = 0; e < kEPT; ++e) {
             if (x[e] >= cand_lo && x[e] < keep_lo) {
                 if (pos < (uint32_t)kCap)
-                    cand[pos] = make_uint2(order_key(x[e]), lane0 + (uint32_t)(e >> 2) * (kThreads * 4) + (uint32_t)(e & 3));
+                    cstore64(rk, pos * 8,
+                             ((uint64_t)(lane0 + (uint32_t)(e >> 2) * (kThreads * 4) + (uint32_t)(e & 3)) << 32) |
+                                 order_key(x[e]));
                 ++pos;
             }
         }
     }
     acc = block_race(acc, sh.rs);
     if (t == 0) {
-        RacePart rpart;
-        rpart.best = acc.best;
-        rpart.count = acc.count;
-        rpart.minkey = acc.minkey;
-        wk.slot_r[wg] = rpart;
+        u32x4v q;
+        q.x = (uint32_t)acc.best;
+        q.y = (uint32_t)(acc.best >> 32);
+        q.z = acc.count;
+        q.w = acc.minkey;
+        cstore128(coherent(wk.slot_r + wg), 0, q);
     }
 
     if (barrier_arrive(ctl, K, wk.epoch, sh.bar)) {
         RaceAcc part;
         part.init();
+        const __amdgpu_buffer_rsrc_t rr = coherent(wk.slot_r + b * K);
         for (uint32_t k = t; k < K; k += kThreads) {
-            const RacePart q = wk.slot_r[b * K + k];
-            part.best = q.best > part.best ? q.best : part.best;
-            part.count += q.count;
-            part.minkey = q.minkey < part.minkey ? q.minkey : part.minkey;
+            const u32x4v q = cload128(rr, k * 16);
+            const uint64_t qb = join64(q.x, q.y);
+            part.best = qb > part.best ? qb : part.best;
+            part.count += q.z;
+            part.minkey = q.w < part.minkey ? q.w : part.minkey;
         }
         part = block_race(part, sh.rs);
         uint32_t n = 0;
         if (has_cands) {
-            if (t == 0) sh.cand_base = __hip_atomic_load(&ctl->cand_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (t == 0) sh.cand_base = get(&ctl->cand_n);
             __syncthreads();
             n = sh.cand_base;
         }
-        if (n <= (uint32_t)kCap) {
-            const uint2* cand = wk.cand + b * kCap;
+        if (n <= (uint32_t)kCandLds) {
+            // One pass over the list with four loads in flight per thread puts
+            // it in LDS; the resolver's passes then read LDS.
+            const __amdgpu_buffer_rsrc_t rk = coherent(wk.cand + b * kCap);
+            for (uint32_t i0 = t; i0 < n; i0 += 4 * kThreads) {
+                u32x2v c[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t i = i0 + u * kThreads;
+                    c[u] = __builtin_amdgcn_raw_buffer_load_b64(rk, (i < n ? i : 0) * 8, 0, kSC1);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (i0 + u * kThreads < n) sh.u.cand[i0 + u * kThreads] = c[u];
+            }
+            __syncthreads();
             resolve_row(p, b, model, rp, st,
                         part, [&](auto&& fn) {
                             for (uint32_t i = t; i < n; i += kThreads) {
-                                const uint2 c = cand[i];
+                                const u32x2v c = sh.u.cand[i];
+                                fn(c.x, c.y);
+                            }
+                        },
+                        sh.rs);
+        } else if (n <= (uint32_t)kCap) {
+            const __amdgpu_buffer_rsrc_t rk = coherent(wk.cand + b * kCap);
+            resolve_row(p, b, model, rp, st,
+                        part, [&](auto&& fn) {
+                            for (uint32_t i = t; i < n; i += kThreads) {
+                                const u32x2v c = __builtin_amdgcn_raw_buffer_load_b64(rk, i * 8, 0, kSC1);
                                 fn(c.x, c.y);
                             }
                         },
@@ -741,10 +906,11 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
         }
         write_outputs(p, b, st);
         if (t == 0) {
-            ctl->token = st.token;
-            ctl->count = st.count;
-            ctl->cut_key = st.cut_key;
-            ctl->s_keep = st.s_keep;
+            const __amdgpu_buffer_rsrc_t rc = coherent(ctl);
+            cstore32(rc, kOffToken, st.token);
+            cstore32(rc, kOffCount, st.count);
+            cstore32(rc, kOffCut, st.cut_key);
+            cstore64(rc, kOffSkeep, (uint64_t)__double_as_longlong(st.s_keep));
         }
         barrier_release(ctl);
         if (!want_probs) return;
