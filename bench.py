@@ -187,7 +187,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic_from_profile(w["name"], batch_bytes),
-                     "kernel": "tile_kernel", "avg_launch_ms": avg_ms, "median_launch_ms": med_ms,
+                     "kernel": "tile_kernel" if need else "row_kernel", "avg_launch_ms": avg_ms,
+                     "median_launch_ms": med_ms,
                      "algorithmic_bytes_per_launch": batch_bytes},
         "stream_read": {"gbps": stream_gbps, "avg_ms": read_ms, "frac_of_peak": stream_gbps / PEAK_HBM_GBPS,
                         "sampler_vs_stream": achieved / stream_gbps},

@@ -67,10 +67,11 @@ extern "C" {
 #define NUCLEUS_EDEVICE (-4)    /* no usable gfx950 device for the current HIP context */
 
 /* Option flags. */
-#define NUCLEUS_FLAG_SINGLE_WORKGROUP 1 /* run every row on one workgroup that re-reads the row
-                                           from memory for each phase (no workspace needed).
-                                           Same results, bit for bit; slower.  For verification
-                                           and for callers that cannot provide a workspace. */
+#define NUCLEUS_FLAG_SINGLE_WORKGROUP 1 /* run every row on one workgroup that streams the row
+                                           from memory once per phase (no workspace needed),
+                                           whatever the batch size.  Same results, bit for bit.
+                                           Batches of 128 rows or more take this path anyway;
+                                           for smaller ones it is slower than splitting rows. */
 
 /* Logit element types. */
 #define NUCLEUS_F32 0
@@ -126,8 +127,9 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
                    const nucleus_options* opt);
 
 /* Device workspace, in bytes, that nucleus_sample needs for a batch of this
- * shape and dtype on its default path (0 if none: rows longer than
- * 64 * 16384 tokens, or B == 0).  Returns 0 for invalid shapes. */
+ * shape and dtype on its default path.  Only batches of fewer than 128 rows
+ * of at most 64 * 8192 tokens split rows over workgroups and need one; for
+ * every other shape, B == 0 and invalid shapes it returns 0. */
 size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype);
 
 /* Static description of a return code. */

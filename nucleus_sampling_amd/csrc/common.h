@@ -178,6 +178,7 @@ struct MaxU64 { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { r
 struct SumU64 { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return a + b; } };
 struct MinU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
 struct MaxI32 { __device__ int operator()(int a, int b) const { return a > b ? a : b; } };
+struct MinI32 { __device__ int operator()(int a, int b) const { return a < b ? a : b; } };
 struct OrI32 { __device__ int operator()(int a, int b) const { return a | b; } };
 
 // ceil(p * S) for p in (0, 1) as an fp32 and S < 2^63, exactly: the integer

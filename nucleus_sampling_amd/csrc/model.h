@@ -179,64 +179,104 @@ struct Decision {
     double s_total;    // weight of all survivors
 };
 
-// Sum of exp(-j w) * H[j] * 2^-31 over bins [0, nb) in a fixed order: 32
-// groups of 32 bins summed sequentially, then the groups in order.  Called
-// by one wave; every lane returns the same value.
-__device__ __forceinline__ double group_sum(const RowModel& r, const uint64_t* H, int g)
+// Weight of bin j: exp(-j w) * H * 2^-31 (0.0 for an empty bin).
+__device__ __forceinline__ double bin_weight(const RowModel& r, int j, uint64_t h)
 {
 #pragma clang fp contract(off)
-    double acc = 0.0;
-    for (int j = 32 * g; j < 32 * g + 32; ++j)
-        if (H[j]) acc += edge_weight(r, j) * ((double)H[j] * (1.0 / kFx));
-    return acc;
+    return h ? edge_weight(r, j) * ((double)h * (1.0 / kFx)) : 0.0;
 }
 
-// Decide how a row's cut is found from its merged histogram H (weights) and
-// C (counts of survivors per bin, only when k > 0).  Must be called by all
+__device__ __forceinline__ double lane_read_f64(double v, int lane)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Decide how a row's cut is found from its merged histogram H (integer
+// weights) and C (counts of survivors per bin, only when k > 0).  Both are
+// overwritten: H with the running bin weights (doubles), C with running
+// counts, each restarting at every group of 32 bins.  Must be called by all
 // threads of one workgroup; `red` is workgroup scratch of >= 64 doubles.
-// Deterministic: the summation order is fixed, whatever the block size.
-__device__ Decision decide(const RowModel& r, const uint64_t* H, const uint32_t* C, int k, float p, double* red)
+//
+// Deterministic: every sum runs in one fixed order whatever the block size.
+// The weight of bin j is exp(-j w) * H[j] * 2^-31; thread g adds the 32 bins
+// of group g one by one from 0.0 (keeping each running value), and S adds
+// the 32 group sums one by one.  Adding an empty bin's 0.0 changes nothing.
+// The searches then compare these same running values against the
+// threshold, so the cut never lands on an empty bin.
+__device__ __forceinline__ Decision decide(const RowModel& r, uint64_t* H, uint32_t* C, int k, float p,
+                                          double* red)
 {
 #pragma clang fp contract(off)
     __shared__ Decision dec;
     const int t = threadIdx.x;
-    if (t < 32) {  // group sums (32 groups of 32 bins) and counts
-        red[t] = group_sum(r, H, t);
-        uint64_t gc = 0;
+    double* W = (double*)H;
+    for (int j = t; j < kBins; j += blockDim.x) W[j] = bin_weight(r, j, H[j]);
+    __syncthreads();
+    if (t < 32) {  // group t: running sums of weights and counts
+        double acc = 0.0;
+        uint32_t cc = 0;
+#pragma unroll 8
+        for (int i = 0; i < 32; ++i) {
+            acc += W[32 * t + i];
+            W[32 * t + i] = acc;
+        }
         if (C)
-            for (int j = 32 * t; j < 32 * t + 32; ++j) gc += C[j];
-        red[32 + t] = (double)gc;
+#pragma unroll 8
+            for (int i = 0; i < 32; ++i) {
+                cc += C[32 * t + i];
+                C[32 * t + i] = cc;
+            }
+        red[t] = acc;
+        red[32 + t] = (double)cc;
     }
     __syncthreads();
-    if (t == 0) {
+    if (t < kWave) {
+        // Every lane runs the sequential sum over the 32 groups and keeps the
+        // running values before its own group (lane g < 32).
+        const int lane = t;
+        double S = 0.0, run_g = 0.0, gs = 0.0;
+        uint64_t total = 0, crun_g = 0, gc = 0;
+#pragma unroll 1
+        for (int c = 0; c < 32; c += 8) {
+            double v[8], n[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                v[q] = red[c + q];
+                n[q] = red[32 + c + q];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (lane == c + q) {
+                    run_g = S;
+                    gs = v[q];
+                    crun_g = total;
+                    gc = (uint64_t)n[q];
+                }
+                S += v[q];
+                total += (uint64_t)n[q];
+            }
+        }
         Decision d;
         d.mode = kModeP;
         d.cbin = 0;
         d.tc = 0;
         d.a_above = 0.0;
-        double S = 0.0;
-        uint64_t total = 0;
-        for (int g = 0; g < 32; ++g) {
-            S += red[g];
-            total += (uint64_t)red[32 + g];
-        }
         d.s_total = S;
         bool topk = false;
         if (C && k > 0 && total > (uint64_t)k) {
             // top-k binds: the first bin where the running count reaches k.
-            uint64_t run = 0;
-            int g = 0;
-            while (run + (uint64_t)red[32 + g] < (uint64_t)k) {
-                run += (uint64_t)red[32 + g];
-                ++g;
-            }
-            int j = 32 * g;
-            while (run + C[j] < (uint64_t)k) {
-                run += C[j];
-                ++j;
-            }
+            const uint64_t mg = __ballot(lane < 32 && crun_g + gc >= (uint64_t)k);
+            const int g = mg ? (int)__builtin_ctzll(mg) : 31;
+            const uint64_t run = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(crun_g >> 32), g) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)crun_g, g);
+            const uint32_t pc = lane < 32 ? C[32 * g + lane] : 0u;
+            const uint64_t mi = __ballot(lane < 32 && run + pc >= (uint64_t)k);
+            const int i = mi ? (int)__builtin_ctzll(mi) : 31;
             d.mode = kModeK;
-            d.cbin = (uint32_t)j;
+            d.cbin = (uint32_t)(32 * g + i);
             topk = true;
         }
         if (!topk) {
@@ -245,24 +285,18 @@ __device__ Decision decide(const RowModel& r, const uint64_t* H, const uint32_t*
             } else if (p <= 0.0f) {
                 d.mode = kModeTop;
             } else {
-                // top-p: the first bin whose running weight (through it) reaches
-                // p*S.  Group prefixes use the same additions as S, and bins inside
-                // a group the same additions as its group sum, so the search always
-                // stops at a non-empty bin.
+                // top-p: the first group (of the first 31) whose running weight
+                // through it reaches p*S, then the first bin (of its first 31)
+                // likewise; the last group / bin when none does.
                 const double thr = (double)p * S;
-                double run = 0.0;
-                int g = 0;
-                while (g < 31 && run + red[g] < thr) {
-                    run += red[g];
-                    ++g;
-                }
-                int j = 32 * g;
-                double acc = 0.0;
-                for (; j < 32 * g + 31; ++j) {
-                    const double nxt = H[j] ? acc + edge_weight(r, j) * ((double)H[j] * (1.0 / kFx)) : acc;
-                    if (run + nxt >= thr) break;
-                    acc = nxt;
-                }
+                const uint64_t mg = __ballot(lane < 31 && run_g + gs >= thr);
+                const int g = mg ? (int)__builtin_ctzll(mg) : 31;
+                double run = lane_read_f64(run_g, g);
+                const double pw = lane < 32 ? W[32 * g + lane] : 0.0;
+                const uint64_t mi = __ballot(lane < 31 && run + pw >= thr);
+                const int i = mi ? (int)__builtin_ctzll(mi) : 31;
+                const double acc = i > 0 ? lane_read_f64(pw, i - 1) : 0.0;
+                const int j = 32 * g + i;
                 run = run + acc;
                 d.cbin = (uint32_t)j;
                 d.a_above = run;
@@ -273,7 +307,7 @@ __device__ Decision decide(const RowModel& r, const uint64_t* H, const uint32_t*
                 d.tc = tc;
             }
         }
-        dec = d;
+        if (lane == 0) dec = d;
     }
     __syncthreads();
     const Decision out = dec;

@@ -37,11 +37,17 @@ int check_device()
     return known[dev] == 1 ? NUCLEUS_OK : NUCLEUS_EDEVICE;
 }
 
-// Workgroups per row on the split-row path, or 0 when rows are too long for it.
-int chunks_for(int64_t V)
+// Batches with at least this many rows run one workgroup per row: a CU per
+// row already keeps the device's memory busy.  Smaller batches split each
+// row over ceil(V / kChunk) workgroups.
+constexpr int64_t kSplitBelowRows = 128;
+
+// Workgroups per row on the split-row path, or 0 for the one-workgroup-per-row
+// kernel (large batches, rows longer than the split path takes).
+int chunks_for(int64_t B, int64_t V)
 {
     const int64_t K = (V + kChunk - 1) / kChunk;
-    return K <= kMaxChunks ? (int)K : 0;
+    return (B < kSplitBelowRows && K <= kMaxChunks) ? (int)K : 0;
 }
 
 // A distinct 56-bit tag per call.  The sequence starts at a value derived
@@ -84,7 +90,7 @@ const char* nucleus_strerror(int code)
 size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype)
 {
     if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16)) return 0;
-    const int K = chunks_for(V);
+    const int K = chunks_for(B, V);
     if (B == 0 || K == 0) return 0;
     return work_layout(B, K, kBins).total;
 }
@@ -106,7 +112,7 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
         (min_p && !aligned(min_p)) || !aligned(out_token) || !aligned(out_keep_count) ||
         (out_probs && !aligned(out_probs)) || (opt && opt->out_min_kept_logit && !aligned(opt->out_min_kept_logit)))
         return NUCLEUS_EINVAL;
-    const int K = single ? 0 : chunks_for(V);
+    const int K = single ? 0 : chunks_for(B, V);
     const size_t need = K ? work_layout(B, K, kBins).total : 0;
     if (need > 0 && (!opt || !opt->workspace || opt->workspace_bytes < need || (uintptr_t)opt->workspace % 256))
         return NUCLEUS_EWORKSPACE;
@@ -152,11 +158,11 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
         else
             hipLaunchKernelGGL(tile_kernel<kBF16>, grid, block, 0, s, p, wk);
     } else {
-        const dim3 grid((unsigned)B), block(kThreads);
+        const dim3 grid((unsigned)B), block(kRowThreads);
         if (dtype == NUCLEUS_F32)
-            hipLaunchKernelGGL(generic_kernel<kF32>, grid, block, 0, s, p);
+            hipLaunchKernelGGL(row_kernel<kF32>, grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL(generic_kernel<kBF16>, grid, block, 0, s, p);
+            hipLaunchKernelGGL(row_kernel<kBF16>, grid, block, 0, s, p);
     }
     return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
 }

@@ -19,10 +19,11 @@
 //   and the barriers cannot deadlock; a bounded spin turns a violation of that
 //   assumption into a row error (token -2) instead of a hang.
 //
-// generic_kernel: one workgroup per row streaming the row from global memory
-//   for each phase, taking the same decisions with the same arithmetic.  It
-//   serves rows too long for the split path and, through the resolver, rows
-//   whose crossing bin holds more than kCap tokens.
+// row_kernel: one 1024-thread workgroup per row (a CU each) streaming the
+//   row from global memory once per phase with many loads in flight; the
+//   crossing bin's tokens are compacted into LDS for the resolver.  Same
+//   decisions, same arithmetic.  It serves batches large enough to fill the
+//   device with rows, and rows too long for the split path.
 #pragma once
 
 #include <stddef.h>
@@ -370,16 +371,39 @@ __device__ __forceinline__ void race_one(const Params& p, int64_t b, const RowMo
     acc.minkey = key < acc.minkey ? key : acc.minkey;
 }
 
-// The smallest logit whose bin is < c (c >= 1): bins fall as logits rise, so
-// this is a binary search over order keys between the lowest finite logit and
-// the row max (whose bin is 0).
+// The smallest finite logit whose bin is < c (c >= 1).  Bins fall as logits
+// rise (the row max is in bin 0), so over order keys this is the boundary
+// between keys with bin >= c and keys with bin < c.  The search starts from
+// the estimate m - c/s, gallops in key steps until it brackets the boundary
+// and bisects the bracket: the same answer as a bisection over all keys, in a
+// few evaluations.
 __device__ __forceinline__ float lowest_in_bins_below(const RowModel& r, uint32_t c)
 {
-    uint32_t lo = order_key(-3.4028234663852886e38f), hi = order_key(r.m);  // answer in [lo, hi]
-    if (bin_of(bin_pos(r, key_value(lo))) < c) return key_value(lo);
-    while (hi - lo > 1) {  // invariant: bin(lo) >= c, bin(hi) < c
+    const uint32_t kmin = order_key(-3.4028234663852886e38f), kmax = order_key(r.m);
+    auto below = [&](uint32_t key) { return bin_of(bin_pos(r, key_value(key))) < c; };
+    if (below(kmin)) return key_value(kmin);
+    const float est = r.m - (float)c / r.s;
+    uint32_t k = order_key(est > -3.4028234663852886e38f ? est : -3.4028234663852886e38f);
+    k = k < kmin ? kmin : (k > kmax ? kmax : k);
+    uint32_t lo, hi;  // below(lo) is false, below(hi) is true
+    if (below(k)) {
+        hi = k;
+        for (uint32_t step = 1;; step <<= 1) {
+            lo = (hi - kmin > step) ? hi - step : kmin;
+            if (!below(lo)) break;
+            hi = lo;
+        }
+    } else {
+        lo = k;
+        for (uint32_t step = 1;; step <<= 1) {
+            hi = (kmax - lo > step) ? lo + step : kmax;
+            if (below(hi)) break;
+            lo = hi;
+        }
+    }
+    while (hi - lo > 1) {
         const uint32_t mid = lo + (hi - lo) / 2;
-        if (bin_of(bin_pos(r, key_value(mid))) < c) hi = mid; else lo = mid;
+        if (below(mid)) hi = mid; else lo = mid;
     }
     return key_value(hi);
 }
@@ -414,26 +438,47 @@ __device__ __forceinline__ Classes classify(const RowModel& r, const RowState& s
 
 struct ResolveShared {
     SelectShared sel;
-    uint64_t red64[kThreads / kWave];
-    uint32_t red32[kThreads / kWave];
+    uint64_t red64[kMaxWaves];
+    uint32_t red32[kMaxWaves];
+    uint32_t red32b[kMaxWaves];
 };
 
-// Merge partial race accumulators of the workgroup (all threads return the merge).
+// Merge partial race accumulators of the workgroup (all threads return the
+// merge): wave reductions, then one exchange through LDS.
+template <int NT>
 __device__ __forceinline__ RaceAcc block_race(RaceAcc a, ResolveShared& rs)
 {
+    constexpr int W = NT / kWave;
+    a.best = wave_reduce(a.best, MaxU64());
+    a.count = wave_reduce(a.count, SumU32());
+    a.minkey = wave_reduce(a.minkey, MinU32());
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    __syncthreads();
+    if (lane == 0) {
+        rs.red64[w] = a.best;
+        rs.red32[w] = a.count;
+        rs.red32b[w] = a.minkey;
+    }
+    __syncthreads();
     RaceAcc o;
-    o.best = block_reduce<kThreads>(a.best, MaxU64(), rs.red64);
-    o.count = block_reduce<kThreads>(a.count, SumU32(), rs.red32);
-    o.minkey = block_reduce<kThreads>(a.minkey, MinU32(), rs.red32);
+    o.best = rs.red64[0];
+    o.count = rs.red32[0];
+    o.minkey = rs.red32b[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) {
+        o.best = rs.red64[i] > o.best ? rs.red64[i] : o.best;
+        o.count += rs.red32[i];
+        o.minkey = rs.red32b[i] < o.minkey ? rs.red32b[i] : o.minkey;
+    }
     return o;
 }
 
 // The last step of a row: given the merged race partial of the surely kept
 // tokens (`part`) and a way to visit the candidates (`visit(fn(key, idx))`),
 // find the exact cut, race the kept candidates and fill st.token / count /
-// cut_key / s_keep.  All threads; uniform control flow.
-template <class Visit>
-__device__ void resolve_row(const Params& p, int64_t b, const RowModel& r, const RowParams& rp, RowState& st,
+// cut_key / s_keep.  All NT threads; uniform control flow.
+template <int NT, class Visit>
+__device__ __forceinline__ void resolve_row(const Params& p, int64_t b, const RowModel& r, const RowParams& rp, RowState& st,
                             RaceAcc part, Visit visit, ResolveShared& rs)
 {
     if (st.mode == kModeError) {
@@ -457,7 +502,7 @@ __device__ void resolve_row(const Params& p, int64_t b, const RowModel& r, const
         st.s_keep = st.s_total;
     } else if (st.mode == kModeP) {
         const uint64_t tc = st.tc;
-        const SelectResult sr = select_level(
+        const SelectResult sr = select_level<NT>(
             [&](auto&& fn) {
                 visit([&](uint32_t key, uint32_t) { fn(key, (uint64_t)bin_fx(r, bin_pos(r, key_value(key)))); });
             },
@@ -468,14 +513,14 @@ __device__ void resolve_row(const Params& p, int64_t b, const RowModel& r, const
         visit([&](uint32_t key, uint32_t idx) {
             if (key >= cut) race_one(p, b, r, key, idx, c);
         });
-        c = block_race(c, rs);
+        c = block_race<NT>(c, rs);
         acc.best = c.best > acc.best ? c.best : acc.best;
         acc.count += c.count;
         acc.minkey = c.minkey < acc.minkey ? c.minkey : acc.minkey;
         st.s_keep = st.a_above + edge_weight(r, (int)st.cbin) * ((double)(sr.above + sr.at) * (1.0 / kFx));
     } else {  // kModeK: top-k binds; every candidate decision is taken here
         const uint64_t kk = (uint64_t)rp.K;
-        const SelectResult tk = select_level(
+        const SelectResult tk = select_level<NT>(
             [&](auto&& fn) { visit([&](uint32_t key, uint32_t) { fn(key, (uint64_t)1); }); },
             [&](uint64_t) { return kk; }, rs.sel);
         uint32_t cut = tk.level;
@@ -484,7 +529,7 @@ __device__ void resolve_row(const Params& p, int64_t b, const RowModel& r, const
         } else if (rp.P < 1.0f) {
             const uint32_t vk = tk.level;
             const float P = rp.P;
-            const SelectResult sp = select_level(
+            const SelectResult sp = select_level<NT>(
                 [&](auto&& fn) {
                     visit([&](uint32_t key, uint32_t) {
                         if (key >= vk) {
@@ -506,8 +551,8 @@ __device__ void resolve_row(const Params& p, int64_t b, const RowModel& r, const
                 kept_w += fixed40(r, bin_of(t), bin_fx(r, t));
             }
         });
-        c = block_race(c, rs);
-        kept_w = block_reduce<kThreads>(kept_w, SumU64(), rs.red64);
+        c = block_race<NT>(c, rs);
+        kept_w = block_reduce<NT>(kept_w, SumU64(), rs.red64);
         acc = c;
         st.s_keep = (double)kept_w * 0x1p-40;
     }
@@ -531,9 +576,10 @@ __device__ __forceinline__ void write_outputs(const Params& p, int64_t b, const 
 }
 
 // Per-bin factors edge(j) * 2^-31 / S_keep for the probability pass.
+template <int NT>
 __device__ __forceinline__ void prob_factors(const RowModel& r, const RowState& st, float* factor)
 {
-    for (int j = threadIdx.x; j < kBins; j += kThreads)
+    for (int j = threadIdx.x; j < kBins; j += NT)
         factor[j] = (st.s_keep > 0.0) ? (float)(edge_weight(r, j) * (1.0 / kFx) / st.s_keep) : 0.0f;
     __syncthreads();
 }
@@ -831,7 +877,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
             }
         }
     }
-    acc = block_race(acc, sh.rs);
+    acc = block_race<kThreads>(acc, sh.rs);
     if (t == 0) {
         u32x4v q;
         q.x = (uint32_t)acc.best;
@@ -852,7 +898,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
             part.count += q.z;
             part.minkey = q.w < part.minkey ? q.w : part.minkey;
         }
-        part = block_race(part, sh.rs);
+        part = block_race<kThreads>(part, sh.rs);
         uint32_t n = 0;
         if (has_cands) {
             if (t == 0) sh.cand_base = get(&ctl->cand_n);
@@ -875,7 +921,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
                     if (i0 + u * kThreads < n) sh.u.cand[i0 + u * kThreads] = c[u];
             }
             __syncthreads();
-            resolve_row(p, b, model, rp, st,
+            resolve_row<kThreads>(p, b, model, rp, st,
                         part, [&](auto&& fn) {
                             for (uint32_t i = t; i < n; i += kThreads) {
                                 const u32x2v c = sh.u.cand[i];
@@ -885,7 +931,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
                         sh.rs);
         } else if (n <= (uint32_t)kCap) {
             const __amdgpu_buffer_rsrc_t rk = coherent(wk.cand + b * kCap);
-            resolve_row(p, b, model, rp, st,
+            resolve_row<kThreads>(p, b, model, rp, st,
                         part, [&](auto&& fn) {
                             for (uint32_t i = t; i < n; i += kThreads) {
                                 const u32x2v c = __builtin_amdgcn_raw_buffer_load_b64(rk, i * 8, 0, kSC1);
@@ -894,7 +940,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
                         },
                         sh.rs);
         } else {  // the crossing bin overflowed the list: visit the row in global memory
-            resolve_row(p, b, model, rp, st,
+            resolve_row<kThreads>(p, b, model, rp, st,
                         part, [&](auto&& fn) {
                             row_groups<DT>(p, rowp, [&](int64_t i0, const float* xs) {
 #pragma unroll
@@ -916,7 +962,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
         if (!want_probs) return;
         // The resolving workgroup re-reads its chunk so that its registers are
         // free for the resolver; the others write from registers below.
-        if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors(model, st, sh.u.factor);
+        if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kThreads>(model, st, sh.u.factor);
         float* prow = p.out_probs + b * p.V;
         for (int v = 0; v < kEPT / 4; ++v) {
             const int64_t i0 = base + ((int64_t)v * kThreads + t) * 4;
@@ -937,7 +983,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
     st = uniform(sh.st);
 
     // ---- probabilities of this chunk, from registers
-    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors(model, st, sh.u.factor);
+    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kThreads>(model, st, sh.u.factor);
     float* prow = p.out_probs + b * p.V;
 #pragma unroll
     for (int v = 0; v < kEPT / 4; ++v) {
@@ -951,7 +997,109 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
 // ---------------------------------------------------------------------------
 // One workgroup per row, every phase streamed from global memory.
 // ---------------------------------------------------------------------------
-struct GenericShared {
+// ---------------------------------------------------------------------------
+// The one-workgroup-per-row kernel.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 1024;  // 16 waves: one workgroup per CU
+constexpr int kRowUnroll = 8;      // 4-token groups per thread whose loads are in flight together
+constexpr int kRowCand = 8192;     // crossing-bin candidates held in LDS
+constexpr int kRaceQueue = 128;    // per-wave ring of 4-token groups waiting for the race
+
+// One aligned 4-token group (f32: 16 bytes, bf16: 8 bytes) at group index g.
+template <int DT, bool NTL>
+__device__ __forceinline__ void load_group(const void* rowp, uint32_t g, float x[4])
+{
+    if (DT == kF32) {
+        const f32x4* a = (const f32x4*)rowp + g;
+        const f32x4 v = NTL ? __builtin_nontemporal_load(a) : *a;
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    } else {
+        const u32x2* a = (const u32x2*)rowp + g;
+        const u32x2 v = NTL ? __builtin_nontemporal_load(a) : *a;
+        x[0] = __uint_as_float(v.x << 16);
+        x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        x[2] = __uint_as_float(v.y << 16);
+        x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    }
+}
+
+// Calls f(i0, x[4]) for every 4-token group of the row (tokens at or past V
+// read as -inf).  Each thread takes kRowUnroll groups per step and issues all
+// their loads before using any, so 8 KB per wave are in flight.  Every lane
+// calls f the same number of times (groups past the row are all -inf), so f
+// may use wave-wide operations.  NTL marks the loads non-temporal (the row's
+// last pass).
+template <int DT, bool NTL, class F>
+__device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&& f)
+{
+    const uint32_t V = (uint32_t)p.V;
+    const uint32_t ng = (V + 3) >> 2, nfull = V >> 2;
+    const uint32_t t = threadIdx.x;
+    if (p.vec_in && nfull > 0) {
+        for (uint32_t g0 = 0; g0 < ng; g0 += kRowUnroll * kRowThreads) {
+            float x[kRowUnroll][4];
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u) {
+                const uint32_t g = g0 + (uint32_t)u * kRowThreads + t;
+                load_group<DT, NTL>(rowp, g < nfull ? g : nfull - 1, x[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u) {
+                const uint32_t g = g0 + (uint32_t)u * kRowThreads + t;
+                if (g >= nfull) {  // the row's partial last group, or past the row
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t i = 4 * g + j;
+                        x[u][j] = i < V ? (DT == kF32 ? ((const float*)rowp)[i]
+                                                      : bf16_to_float(((const uint16_t*)rowp)[i]))
+                                        : -INFINITY;
+                    }
+                }
+                f(g << 2, x[u]);
+            }
+        }
+    } else {
+        for (uint32_t g0 = 0; g0 < ng; g0 += kRowThreads) {
+            const uint32_t g = g0 + t;
+            float x[4];
+            load4<DT>(rowp, (int64_t)g << 2, V, 0, x);  // -inf past V
+            f(g << 2, x);
+        }
+    }
+}
+
+// Appends (key, idx) for the lanes with pred to an LDS list: one LDS atomic
+// per wave, positions from the lane's rank among the appending lanes.
+// Appends past `cap` are counted but dropped.
+__device__ __forceinline__ void lds_append(uint32_t* counter, u32x2v* list, uint32_t cap, bool pred, uint32_t key,
+                                           uint32_t idx)
+{
+    const uint64_t mask = __ballot(pred);
+    if (mask == 0) return;
+    const int leader = __builtin_ctzll(mask);
+    const uint32_t lo = (uint32_t)mask, hi = (uint32_t)(mask >> 32);
+    uint32_t base = 0;
+    if ((int)__lane_id() == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+    if (pred) {
+        const uint32_t off = base + __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+        if (off < cap) {
+            u32x2v e;
+            e.x = key;
+            e.y = idx;
+            list[off] = e;
+        }
+    }
+}
+
+// Per-wave ring of 4-token groups holding at least one kept token: the race
+// runs on full waves of such groups instead of on every group of the row.
+struct RaceQueue {
+    uint32_t i0[kRaceQueue];
+    f32x4 x[kRaceQueue];
+};
+
+struct RowShared {
     union {
         struct {
             uint64_t hm[kBins];
@@ -959,25 +1107,62 @@ struct GenericShared {
         } h;
         float factor[kBins];
     } u;
+    u32x2v cand[kRowCand];
+    RaceQueue rq[kRowThreads / kWave];
     ResolveShared rs;
     double red[64];
-    float redf[kThreads / kWave];
-    int redi[kThreads / kWave];
+    float redf[kMaxWaves], redf2[kMaxWaves];
+    int redi[kMaxWaves];
+    uint32_t cand_n;
+    uint32_t sstar_bits;  // best exact race score found so far in the workgroup (bits of a float >= 0)
 };
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void generic_kernel(Params p)
+// Row max, smallest finite logit and error flag over the workgroup: wave
+// reductions, then one exchange through LDS.
+template <int NT>
+__device__ __forceinline__ void block_extremes(float& mx, float& mn, int& bad, float* rf, float* rf2, int* ri)
 {
-    __shared__ GenericShared sh;
+    constexpr int W = NT / kWave;
+    mx = wave_reduce(mx, MaxF());
+    mn = wave_reduce(mn, MinF());
+    bad = wave_reduce(bad, OrI32());
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    __syncthreads();
+    if (lane == 0) {
+        rf[w] = mx;
+        rf2[w] = mn;
+        ri[w] = bad;
+    }
+    __syncthreads();
+    mx = rf[0];
+    mn = rf2[0];
+    bad = ri[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) {
+        mx = fmaxf(mx, rf[i]);
+        mn = fminf(mn, rf2[i]);
+        bad |= ri[i];
+    }
+}
+
+// One workgroup of kRowThreads per row, streaming the row from global memory
+// once per pass (max, histogram, race + candidates, optional probabilities);
+// the crossing bin's candidates stay in LDS for the resolver.  It takes the
+// same decisions with the same arithmetic as tile_kernel.
+template <int DT>
+__global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p)
+{
+    __shared__ RowShared sh;
     const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
     const int64_t esz = DT == kF32 ? 4 : 2;
     const void* rowp = (const char*)p.logits + b * p.stride * esz;
     const bool want_probs = p.out_probs != nullptr;
 
+    // ---- pass 1: row max, smallest finite logit, NaN / +inf
     float lmax = -INFINITY, lmin = INFINITY;
     int bad = 0;
-    row_groups<DT>(p, rowp, [&](int64_t, const float* xs) {
+    stream_row<DT, false>(p, rowp, [&](uint32_t, const float* xs) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float v = xs[j];
@@ -986,78 +1171,165 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Params p)
             lmin = (v > -INFINITY) ? fminf(lmin, v) : lmin;
         }
     });
-    lmax = block_reduce<kThreads>(lmax, MaxF(), sh.redf);
-    lmin = block_reduce<kThreads>(lmin, MinF(), sh.redf);
-    bad = block_reduce<kThreads>(bad, OrI32(), sh.redi);
+    block_extremes<kRowThreads>(lmax, lmin, bad, sh.redf, sh.redf2, sh.redi);
     const RowParams rp = row_params(p, b);
     RowState st;
-    st.mode = first_mode(bad != 0, lmax, rp.T, rp.P, rp.MP, rp.K, want_probs);
-    st.m = lmax;
-    st.xmin = lmin;
+    st.mode = uniform(first_mode(bad != 0, lmax, rp.T, rp.P, rp.MP, rp.K, want_probs));
+    st.m = uniform(lmax);
+    st.xmin = uniform(lmin);
     st.cbin = 0;
     st.tc = 0;
     st.a_above = st.s_total = st.s_keep = 0.0;
     RowModel model = {};
-    if (st.mode >= kModeTop) model = make_model(st.m, st.xmin, rp.T, rp.MP);
+    if (st.mode >= kModeTop) model = uniform(make_model(st.m, st.xmin, rp.T, rp.MP));
 
+    // ---- pass 2: bin histogram of the survivors
     if (st.mode == kModeHist) {
         const bool counts = rp.K > 0;
-        for (int i = t; i < kBins; i += kThreads) {
+        for (int i = t; i < kBins; i += kRowThreads) {
             sh.u.h.hm[i] = 0;
             sh.u.h.hc[i] = 0;
         }
         __syncthreads();
-        row_groups<DT>(p, rowp, [&](int64_t, const float* xs) {
+        // The last bin takes the whole tail of the row: it is summed in
+        // registers and added once per wave instead of by LDS atomics.
+        uint64_t tail_w = 0;
+        uint32_t tail_c = 0;
+        stream_row<DT, false>(p, rowp, [&](uint32_t, const float* xs) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (survives(model, xs[j])) {
                     const float tp = bin_pos(model, xs[j]);
                     const uint32_t jb = bin_of(tp);
-                    atomicAdd((unsigned long long*)&sh.u.h.hm[jb], (unsigned long long)bin_fx(model, tp));
-                    if (counts) atomicAdd(&sh.u.h.hc[jb], 1u);
+                    const uint32_t fx = bin_fx(model, tp);
+                    if (jb == (uint32_t)(kBins - 1)) {
+                        tail_w += fx;
+                        tail_c += 1;
+                    } else {
+                        atomicAdd((unsigned long long*)&sh.u.h.hm[jb], (unsigned long long)fx);
+                        if (counts) atomicAdd(&sh.u.h.hc[jb], 1u);
+                    }
                 }
             }
         });
+        tail_w = wave_reduce(tail_w, SumU64());
+        tail_c = wave_reduce(tail_c, SumU32());
+        if ((t & (kWave - 1)) == 0 && tail_c) {
+            atomicAdd((unsigned long long*)&sh.u.h.hm[kBins - 1], (unsigned long long)tail_w);
+            if (counts) atomicAdd(&sh.u.h.hc[kBins - 1], tail_c);
+        }
         __syncthreads();
         const Decision d = decide(model, sh.u.h.hm, counts ? sh.u.h.hc : nullptr, rp.K, rp.P, sh.red);
-        st.mode = d.mode;
-        st.cbin = d.cbin;
-        st.tc = d.tc;
-        st.a_above = d.a_above;
-        st.s_total = d.s_total;
+        st.mode = uniform(d.mode);
+        st.cbin = uniform(d.cbin);
+        st.tc = uniform(d.tc);
+        st.a_above = uniform(d.a_above);
+        st.s_total = uniform(d.s_total);
     }
 
+    // ---- pass 3: race the surely kept tokens; the crossing bin's tokens go to LDS
     const Classes cl = classify(model, st);
     const float keep_lo = cl.keep_lo, cand_lo = cl.cand_lo;
     const bool scored = st.mode != kModeGreedy;
+    const bool has_cand = cand_lo < keep_lo;
     const float c_log2e = model.invT * 1.4426950408889634f;
+    if (t == 0) {
+        sh.cand_n = 0;
+        sh.sstar_bits = 0;
+    }
+    __syncthreads();
     RaceAcc acc;
     acc.init();
     float sstar = 0.0f;
-    row_groups<DT>(p, rowp, [&](int64_t i0, const float* xs) {
-        bool keep[4];
+    RaceQueue& rq = sh.rq[t / kWave];
+    const uint32_t lane = (uint32_t)t & (kWave - 1);
+    uint32_t qh = 0, qn = 0;  // ring head and fill, the same in every lane of the wave
+    // Race the `cnt` (<= 64) oldest queued groups, one per lane.  The screen
+    // uses the best score any wave of the workgroup has reached (a score some
+    // token achieved, so screening against it never drops a possible winner).
+    auto drain = [&](uint32_t cnt) __attribute__((always_inline)) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        const float shared_best = __uint_as_float(sh.sstar_bits);
+        sstar = fmaxf(sstar, shared_best);
+        if (lane < cnt) {
+            const uint32_t slot = (qh + lane) & (kRaceQueue - 1);
+            const f32x4 v = rq.x[slot];
+            const float xs[4] = {v.x, v.y, v.z, v.w};
+            bool keep[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) keep[j] = xs[j] >= keep_lo;
-        race_group(p, b, scored, model, c_log2e, (uint32_t)i0, xs, keep, acc, sstar);
+            for (int j = 0; j < 4; ++j) keep[j] = xs[j] >= keep_lo;
+            race_group(p, b, scored, model, c_log2e, rq.i0[slot], xs, keep, acc, sstar);
+        }
+        const float wave_best = wave_reduce(sstar, MaxF());
+        if (lane == 0 && wave_best > shared_best) atomicMax(&sh.sstar_bits, __float_as_uint(wave_best));
+        qh = (qh + cnt) & (kRaceQueue - 1);
+        qn -= cnt;
+    };
+    stream_row<DT, false>(p, rowp, [&](uint32_t i0, const float* xs) {
+        const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
+        const uint64_t m = __ballot(any);
+        if (m) {
+            if (any) {
+                const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                const uint32_t slot = (qh + qn + r) & (kRaceQueue - 1);
+                f32x4 v;
+                v.x = xs[0]; v.y = xs[1]; v.z = xs[2]; v.w = xs[3];
+                rq.i0[slot] = i0;
+                rq.x[slot] = v;
+            }
+            qn += (uint32_t)__popcll(m);
+            if (qn >= (uint32_t)kWave) drain(kWave);
+        }
+        if (has_cand) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                lds_append(&sh.cand_n, sh.cand, kRowCand, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]),
+                           i0 + j);
+        }
     });
-    acc = block_race(acc, sh.rs);
-    resolve_row(p, b, model, rp, st, acc,
-                [&](auto&& fn) {
-                    row_groups<DT>(p, rowp, [&](int64_t i0, const float* xs) {
+    if (qn) drain(qn);
+    acc = block_race<kRowThreads>(acc, sh.rs);
+    const uint32_t n = uniform(sh.cand_n);
+    if (n <= (uint32_t)kRowCand) {
+        resolve_row<kRowThreads>(p, b, model, rp, st, acc,
+                                 [&](auto&& fn) {
+                                     for (uint32_t i = t; i < n; i += kRowThreads) {
+                                         const u32x2v c = sh.cand[i];
+                                         fn(c.x, c.y);
+                                     }
+                                 },
+                                 sh.rs);
+    } else {  // more candidates than LDS holds: visit the row in global memory
+        resolve_row<kRowThreads>(p, b, model, rp, st, acc,
+                                 [&](auto&& fn) {
+                                     stream_row<DT, false>(p, rowp, [&](uint32_t i0, const float* xs) {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), (uint32_t)(i0 + j));
-                    });
-                },
-                sh.rs);
+                                         for (int j = 0; j < 4; ++j)
+                                             if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), i0 + j);
+                                     });
+                                 },
+                                 sh.rs);
+    }
     write_outputs(p, b, st);
     if (!want_probs) return;
-    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors(model, st, sh.u.factor);
+
+    // ---- pass 4: renormalised probabilities
+    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kRowThreads>(model, st, sh.u.factor);
     float* prow = p.out_probs + b * p.V;
-    row_groups<DT>(p, rowp, [&](int64_t i0, const float* xs) {
+    const uint32_t V = (uint32_t)p.V;
+    stream_row<DT, true>(p, rowp, [&](uint32_t i0, const float* xs) {
+        float q[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (i0 + j < p.V) prow[i0 + j] = prob_of(st.mode, model, st, sh.u.factor, xs[j], i0 + j);
+        for (int j = 0; j < 4; ++j) q[j] = prob_of(st.mode, model, st, sh.u.factor, xs[j], i0 + j);
+        if (i0 + 4 <= V && ((uintptr_t)(prow + i0) & 15) == 0) {
+            f32x4 v;
+            v.x = q[0]; v.y = q[1]; v.z = q[2]; v.w = q[3];
+            __builtin_nontemporal_store(v, (f32x4*)(prow + i0));
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (i0 + j < V) prow[i0 + j] = q[j];
+        }
     });
 }
 

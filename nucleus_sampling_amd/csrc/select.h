@@ -20,14 +20,14 @@
 
 namespace nucleus {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;     // split-row workgroups
+constexpr int kMaxWaves = 16;     // largest workgroup: 1024 threads
 constexpr int kDigitBins = 256;
 
 struct SelectShared {
     uint64_t hist[kDigitBins];
-    uint64_t red64[kThreads / kWave];
-    int redi[kThreads / kWave];
-    uint64_t bcast;
+    uint64_t res_before, res_at, res_total;
+    int res_j;
 };
 
 struct SelectResult {
@@ -37,58 +37,108 @@ struct SelectResult {
     uint64_t total;     // total eligible weight
 };
 
+__device__ __forceinline__ uint64_t lane_read64(uint64_t v, int lane)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // `visit(fn)` calls fn(key, weight) for every eligible token this thread
 // owns (weight > 0; zero-weight tokens are skipped).  Every thread of the
-// workgroup must call select_level.  `thr_of_total(total)` maps the total
-// eligible weight to the threshold (called once, uniformly).  If no level
-// qualifies (thr == 0), the top level is returned.
-template <class Visit, class ThrFn>
-__device__ SelectResult select_level(Visit visit, ThrFn thr_of_total, SelectShared& sh)
+// workgroup (NT >= 64 threads) must call select_level.  `thr_of_total(total)`
+// maps the total eligible weight to the threshold.  If no level qualifies
+// (thr == 0), the top level is returned.
+//
+// Per digit: all threads add their tokens into the 256-bin LDS histogram;
+// then the first wave alone scans it (lane l holds digits 255-4l .. 252-4l,
+// highest first), publishes the chosen digit and clears the histogram for
+// the next digit.  Two workgroup barriers per digit.
+template <int NT, class Visit, class ThrFn>
+__device__ __forceinline__ SelectResult select_level(Visit visit, ThrFn thr_of_total, SelectShared& sh)
 {
     uint32_t prefix = 0, mask = 0;
-    uint64_t base = 0, thr = 0, total = 0, at = 0;
+    uint64_t base = 0, thr = 0, total = 0;
     const int t = threadIdx.x;
+    for (int i = t; i < kDigitBins; i += NT) sh.hist[i] = 0;
+    __syncthreads();
     for (int lvl = 0; lvl < 4; ++lvl) {
         const int shift = 24 - 8 * lvl;
-        sh.hist[t] = 0;
-        __syncthreads();
         visit([&](uint32_t key, uint64_t w) {
             if ((key & mask) == prefix)
                 atomicAdd((unsigned long long*)&sh.hist[(key >> shift) & 0xFFu], (unsigned long long)w);
         });
         __syncthreads();
-        // Thread t owns digit d = 255 - t, so threads run from the top digit down.
-        const int d = kDigitBins - 1 - t;
-        const uint64_t hw = sh.hist[d];
-        if (lvl == 0) {
-            total = block_reduce<kThreads>(hw, SumU64(), sh.red64);
-            thr = thr_of_total(total);
-        }
-        const uint64_t before = base + block_exclusive_sum<kThreads>(hw, sh.red64);
-        // Lowest non-empty digit whose weight above is < thr; if none (thr == 0),
-        // the highest non-empty digit.
-        const int cand = (hw > 0 && before < thr) ? t : -1;
-        int j = block_reduce<kThreads>(cand, MaxI32(), sh.redi);
-        if (j < 0) {
-            const int top = (hw > 0) ? (kDigitBins - 1 - t) : -1;  // smallest t with weight
-            j = kDigitBins - 1 - block_reduce<kThreads>(top, MaxI32(), sh.redi);
-        }
-        if (t == j) {
-            sh.bcast = before;
-            sh.hist[0] = hw;  // safe: every thread has read its own bin above
+        if (t < kWave) {
+            uint64_t h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = sh.hist[kDigitBins - 1 - (4 * t + i)];
+            const uint64_t ls = h[0] + h[1] + h[2] + h[3];
+            if (lvl == 0) {
+                total = wave_reduce(ls, SumU64());
+                thr = thr_of_total(total);
+            }
+            // Exclusive prefix of the lane sums: weight of the digits above this lane's.
+            uint64_t x = ls;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint64_t y = __shfl_up(x, o, kWave);
+                if (t >= o) x += y;
+            }
+            uint64_t bf = base + x - ls;
+            // Lowest non-empty digit whose weight above is < thr (largest rank);
+            // failing that, the highest non-empty digit (smallest rank).
+            int cand = -1, top = kDigitBins;
+            uint64_t cb = 0, ch = 0, tb = 0, th = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rank = 4 * t + i;
+                if (h[i] > 0 && bf < thr) {
+                    cand = rank;
+                    cb = bf;
+                    ch = h[i];
+                }
+                if (h[i] > 0 && rank < top) {
+                    top = rank;
+                    tb = bf;
+                    th = h[i];
+                }
+                bf += h[i];
+            }
+            int j = wave_reduce(cand, MaxI32());
+            uint64_t jb = base, jh = 0;
+            if (j >= 0) {
+                jb = lane_read64(cb, j >> 2);
+                jh = lane_read64(ch, j >> 2);
+            } else {
+                j = wave_reduce(top, MinI32());
+                if (j < kDigitBins) {
+                    jb = lane_read64(tb, j >> 2);
+                    jh = lane_read64(th, j >> 2);
+                } else {
+                    j = 0;  // nothing eligible: level 0xFF.. of the prefix, weight 0
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sh.hist[4 * t + i] = 0;
+            if (t == 0) {
+                sh.res_j = j;
+                sh.res_before = jb;
+                sh.res_at = jh;
+                if (lvl == 0) sh.res_total = total;
+            }
         }
         __syncthreads();
-        base = sh.bcast;
-        at = sh.hist[0];
-        __syncthreads();
+        const int j = sh.res_j;
+        base = sh.res_before;
         prefix |= (uint32_t)(kDigitBins - 1 - j) << shift;
         mask |= 0xFFu << shift;
     }
     SelectResult r;
     r.level = prefix;
     r.above = base;
-    r.at = at;
-    r.total = total;
+    r.at = sh.res_at;
+    r.total = sh.res_total;
     return r;
 }
 

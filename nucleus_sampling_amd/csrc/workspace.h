@@ -13,7 +13,7 @@
 namespace nucleus {
 
 constexpr int kCap = 8192;       // candidates per row handed to the resolver
-constexpr int kMaxChunks = 64;   // split-row path limit: V <= 64 * 16384
+constexpr int kMaxChunks = 64;   // split-row path limit: V <= 64 * 8192
 
 // Per-row control block: barrier state and the values published at each
 // phase.  128 bytes.
