@@ -58,6 +58,56 @@ def traffic_from_profile(name: str, bytes_per_launch: float):
     return d.get("traffic_bytes_per_launch")
 
 
+CAL_BYTES = 256 * 2**20  # bytes read and written by the calibration kernel
+
+
+def _pmc_rows(d: str):
+    """(kernel name, counter value) per dispatch from a rocprofv3 counter_collection CSV under d."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append((r.get("Kernel_Name", ""), float(r.get("Counter_Value", "nan"))))
+    return rows
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, name: str, shape, dtype: str):
+    """Per-launch HBM bytes of the sampler's kernels from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the calibration kernel (CAL_BYTES read and written)."""
+    import numpy as np
+    B, V = shape
+    algo = B * V * (2 if dtype == "bf16" else 4)
+    out = {"workload": name, "kernel_hash": kernel_hash(), "algorithmic_bytes_per_launch": algo,
+           "calibration": f"torch.add over {CAL_BYTES} bytes (reads and writes CAL_BYTES)"}
+    per = {}
+    for label, d in (("fetch", fetch_dir), ("write", write_dir)):
+        rows = _pmc_rows(d)
+        cal = [v for k, v in rows if "elementwise" in k and "add" in k.lower() and "Fill" not in k]
+        if not cal:
+            raise SystemExit(f"no calibration dispatch found under {d}")
+        factor = CAL_BYTES / (np.median(cal) * 1024.0)
+        kern = {}
+        for k, v in rows:
+            for short in ("row_kernel", "race_kernel", "probs_kernel", "tile_kernel"):
+                if f"nucleus::{short}" in k or k.startswith(short) or f" {short}<" in k or f"{short}<" in k:
+                    kern.setdefault(short, []).append(v)
+        per[label] = {"scale_factor": factor, "calibration_counter_kib": float(np.median(cal)),
+                      "kernels": {k: {"dispatches": len(v), "counter_kib_mean": float(np.mean(v)),
+                                      "bytes_per_dispatch": float(np.mean(v)) * 1024.0 * factor}
+                                  for k, v in kern.items()}}
+    out.update(per)
+    fetch = sum(v["bytes_per_dispatch"] for v in per["fetch"]["kernels"].values())
+    write = sum(v["bytes_per_dispatch"] for v in per["write"]["kernels"].values())
+    out["traffic_bytes_per_launch"] = fetch + write
+    out["fetch_over_algorithmic"] = fetch / algo
+    path = os.path.join(ROOT, "profiles", f"pmc_{name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def cpu_baseline(w, seconds: float, threads: int):
     import oracle
 
@@ -87,7 +137,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-steps", action="store_true", help="only run the timed loop (for rocprofv3)")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="before the timed loop, run a plain elementwise kernel that reads and writes 256 MiB "
+                         "(the scale reference for FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --pmc-calibrate "
+                         "--profile-steps into profiles/pmc_<workload>.json and print it")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        import workloads
+        print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], workloads.NAMES[args.workload],
+                                     workloads.SHAPES[args.workload], workloads.DTYPES[args.workload]), indent=1))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); rows are independent, so a batch "
@@ -128,6 +190,13 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.pmc_calibrate:
+        cal_src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        cal_dst = torch.empty_like(cal_src)
+        for _ in range(3):
+            torch.add(cal_src, 1.0, out=cal_dst)
+        torch.cuda.synchronize()
+        del cal_src, cal_dst
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
