@@ -134,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--buffers", type=int, default=0, help="input copies to rotate (default: > 512 MB total)")
+    ap.add_argument("--path", choices=["default", "single", "split", "rows"], default="default",
+                    help="force one of the library's paths (for comparisons; the headline uses the default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-steps", action="store_true", help="only run the timed loop (for rocprofv3)")
@@ -181,11 +183,17 @@ def main():
     out = ns.SampleResult(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                           None, None)
     stream = torch.cuda.current_stream(dev)
-    need = ns.workspace_bytes(B, V, host.dtype)
+    flags = {"default": 0, "single": ns.NUCLEUS_FLAG_SINGLE_WORKGROUP, "split": ns.NUCLEUS_FLAG_SPLIT_ROWS,
+             "rows": ns.NUCLEUS_FLAG_ROW_RACE}[args.path]
+    need = ns.workspace_bytes(B, V, host.dtype, flags)
     ws = ns.workspace_for(dev, stream, need) if need else None
+    kernel = {"default": "row_kernel" if B >= 128 else "tile_kernel", "single": "row_kernel",
+              "split": "tile_kernel", "rows": "row_kernel+race_kernel"}[args.path]
 
     def step(i):
-        ns.sample(bufs[i % nbuf], T, P, K, MP, seed=w["seed"], step=i, out=out, workspace=ws, stream=stream)
+        ns.sample(bufs[i % nbuf], T, P, K, MP, seed=w["seed"], step=i, out=out, workspace=ws, stream=stream,
+                  single_workgroup=args.path == "single", split_rows=args.path == "split",
+                  row_race=args.path == "rows")
 
     for i in range(args.warmup):
         step(i)
@@ -256,7 +264,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic_from_profile(w["name"], batch_bytes),
-                     "kernel": "tile_kernel" if need else "row_kernel", "avg_launch_ms": avg_ms,
+                     "kernel": kernel, "path": args.path, "avg_launch_ms": avg_ms,
                      "median_launch_ms": med_ms,
                      "algorithmic_bytes_per_launch": batch_bytes},
         "stream_read": {"gbps": stream_gbps, "avg_ms": read_ms, "frac_of_peak": stream_gbps / PEAK_HBM_GBPS,

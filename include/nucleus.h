@@ -67,11 +67,22 @@ extern "C" {
 #define NUCLEUS_EDEVICE (-4)    /* no usable gfx950 device for the current HIP context */
 
 /* Option flags. */
-#define NUCLEUS_FLAG_SINGLE_WORKGROUP 1 /* run every row on one workgroup that streams the row
-                                           from memory once per phase (no workspace needed),
-                                           whatever the batch size.  Same results, bit for bit.
-                                           Batches of 128 rows or more take this path anyway;
-                                           for smaller ones it is slower than splitting rows. */
+#define NUCLEUS_FLAG_SINGLE_WORKGROUP 1 /* run every row, every phase, on one workgroup that
+                                           streams the row from memory once per phase (the path
+                                           batches of 128 rows or more take by default); no
+                                           workspace needed.  Same results, bit for bit.  For
+                                           verification and for callers that cannot provide a
+                                           workspace. */
+#define NUCLEUS_FLAG_SPLIT_ROWS 2       /* split every row over register-resident workgroups
+                                           (the path batches under 128 rows take by default)
+                                           whatever the batch size; rows longer than 64 * 8192
+                                           tokens are then NUCLEUS_EINVAL.  Same results, bit
+                                           for bit.  For verification. */
+#define NUCLEUS_FLAG_ROW_RACE 4         /* one workgroup per row for the histogram passes and the
+                                           race spread over 8192-token chunks of all rows,
+                                           whatever the batch size (needs a workspace: 256 bytes
+                                           plus a 64 KB candidate list per row).  Same results,
+                                           bit for bit. */
 
 /* Logit element types. */
 #define NUCLEUS_F32 0
@@ -79,7 +90,7 @@ extern "C" {
 
 typedef struct nucleus_options {
     int32_t dtype;               /* NUCLEUS_F32 (default) or NUCLEUS_BF16 */
-    int32_t flags;               /* 0, or NUCLEUS_FLAG_SINGLE_WORKGROUP */
+    int32_t flags;               /* 0, or one NUCLEUS_FLAG_* value (not both) */
     void* stream;                /* hipStream_t to launch on; NULL = the null stream */
     int64_t row_stride;          /* elements between row starts; 0 means V */
     void* workspace;             /* device scratch of >= nucleus_workspace_bytes(B, V, dtype) bytes,
@@ -108,9 +119,9 @@ typedef struct nucleus_options {
  * min_p           device [B] float, or NULL (min-p off for every row).
  * seed, step      Philox key and the high counter words; reusing them reproduces
  *                 the draws exactly.
- * out_token       device [B] int32: the sampled id, or -1 on a row error (-2 if the
- *                 workgroups of a row could not meet within seconds, e.g. because
- *                 other work held the whole device).
+ * out_token       device [B] int32: the sampled id, or -1 on a row error (-2 if, on the
+ *                 split-row path, the workgroups of a row could not meet within
+ *                 seconds, e.g. because other work held the whole device).
  * out_keep_count  device [B] int32: size of the kept set (1 for greedy rows,
  *                 0 on a row error).
  * out_probs       device [B, V] float, or NULL: the renormalised kept
@@ -127,10 +138,16 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
                    const nucleus_options* opt);
 
 /* Device workspace, in bytes, that nucleus_sample needs for a batch of this
- * shape and dtype on its default path.  Only batches of fewer than 128 rows
- * of at most 64 * 8192 tokens split rows over workgroups and need one; for
- * every other shape, B == 0 and invalid shapes it returns 0. */
+ * shape and dtype with no flags: batches under 128 rows of at most
+ * 64 * 8192 tokens need the split-row path's (per row: a 128-byte control
+ * block, 12.3 KB per 8192-token chunk and a 64 KB candidate list); other
+ * batches need none.  Returns 0 for B == 0 and for invalid shapes. */
 size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype);
+
+/* The same for a call with the given option flags (0 for
+ * NUCLEUS_FLAG_SINGLE_WORKGROUP; 0 for a flag combination nucleus_sample
+ * rejects).  At most one flag may be set. */
+size_t nucleus_workspace_bytes_for(int64_t B, int64_t V, int32_t dtype, int32_t flags);
 
 /* Static description of a return code. */
 const char* nucleus_strerror(int code);

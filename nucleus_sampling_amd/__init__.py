@@ -26,6 +26,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnucleus.
 NUCLEUS_F32 = 0
 NUCLEUS_BF16 = 1
 NUCLEUS_FLAG_SINGLE_WORKGROUP = 1
+NUCLEUS_FLAG_SPLIT_ROWS = 2
+NUCLEUS_FLAG_ROW_RACE = 4
 
 
 class NucleusError(RuntimeError):
@@ -59,6 +61,8 @@ def lib():
         L.nucleus_sample.restype = ctypes.c_int
         L.nucleus_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32]
         L.nucleus_workspace_bytes.restype = ctypes.c_size_t
+        L.nucleus_workspace_bytes_for.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32]
+        L.nucleus_workspace_bytes_for.restype = ctypes.c_size_t
         L.nucleus_strerror.argtypes = [ctypes.c_int]
         L.nucleus_strerror.restype = ctypes.c_char_p
         L.nucleus_version.argtypes = []
@@ -85,9 +89,9 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
 
 
-def workspace_bytes(B: int, V: int, dtype: torch.dtype = torch.float32) -> int:
+def workspace_bytes(B: int, V: int, dtype: torch.dtype = torch.float32, flags: int = 0) -> int:
     code = NUCLEUS_BF16 if dtype == torch.bfloat16 else NUCLEUS_F32
-    return int(lib().nucleus_workspace_bytes(int(B), int(V), code))
+    return int(lib().nucleus_workspace_bytes_for(int(B), int(V), code, int(flags)))
 
 
 _workspaces = {}
@@ -133,15 +137,19 @@ class SampleResult(NamedTuple):
 def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, seed: int = 0, step: int = 0, *,
            want_probs: bool = False, want_min_kept: bool = False, out: Optional[SampleResult] = None,
            workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
-           single_workgroup: bool = False) -> SampleResult:
+           single_workgroup: bool = False, split_rows: bool = False, row_race: bool = False) -> SampleResult:
     """Sample one token per row of ``logits`` [B, V] (float32 or bfloat16 on a
     gfx950 device; rows may be strided, the last dimension must be dense).
 
     Launches on ``stream`` (default: the current stream) and returns without
     synchronising.  ``out`` may supply preallocated outputs; ``workspace`` a
     byte tensor of at least ``workspace_bytes(B, V, dtype)`` (by default one
-    is cached per device and stream).  ``single_workgroup`` runs
-    every row on one workgroup that re-reads the row (same results, slower).
+    is cached per device and stream).  ``single_workgroup`` runs every row
+    on one workgroup that re-reads the row; ``split_rows`` splits every row
+    over workgroups whatever the batch size; ``row_race`` takes the
+    large-batch path (a workgroup per row, the race spread over chunks)
+    whatever the batch size.  All give the same results, bit for bit; they
+    exist for verification.
     """
     if logits.dim() != 2:
         raise ValueError("logits must be [B, V]")
@@ -164,12 +172,14 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
             torch.empty(B, dtype=torch.float32, device=dev) if want_min_kept else None,
         )
     s = stream if stream is not None else torch.cuda.current_stream(dev)
-    need = 0 if single_workgroup else workspace_bytes(B, V, logits.dtype)
+    flags = ((NUCLEUS_FLAG_SINGLE_WORKGROUP if single_workgroup else 0) | (NUCLEUS_FLAG_SPLIT_ROWS if split_rows else 0)
+             | (NUCLEUS_FLAG_ROW_RACE if row_race else 0))
+    need = workspace_bytes(B, V, logits.dtype, flags)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = workspace_for(dev, s, need)
     opt = _Options()
     opt.dtype = code
-    opt.flags = NUCLEUS_FLAG_SINGLE_WORKGROUP if single_workgroup else 0
+    opt.flags = flags
     opt.stream = s.cuda_stream
     opt.row_stride = logits.stride(0) if B > 1 else V
     opt.workspace = workspace.data_ptr() if (workspace is not None and need) else None

@@ -11,6 +11,7 @@
 #include "nucleus.h"
 #include "common.h"
 #include "params.h"
+#include "rowpath.h"
 #include "sampler.h"
 #include "stream_read.h"
 #include "workspace.h"
@@ -37,17 +38,39 @@ int check_device()
     return known[dev] == 1 ? NUCLEUS_OK : NUCLEUS_EDEVICE;
 }
 
-// Batches with at least this many rows run one workgroup per row: a CU per
-// row already keeps the device's memory busy.  Smaller batches split each
-// row over ceil(V / kChunk) workgroups.
+// Batches with at least this many rows give each row a CU of its own
+// (row_kernel, every phase in one workgroup).  Smaller batches split each row
+// over ceil(V / kChunk) register-resident workgroups (tile_kernel).  The
+// chunked-race path (row_kernel's histogram passes, then race_kernel spread
+// over the device) is taken on request.
 constexpr int64_t kSplitBelowRows = 128;
 
-// Workgroups per row on the split-row path, or 0 for the one-workgroup-per-row
-// kernel (large batches, rows longer than the split path takes).
-int chunks_for(int64_t B, int64_t V)
+enum Path { kPathTile, kPathRows, kPathFused };
+
+// Workgroups per row of the split-row path, 0 if rows are too long for it.
+int tile_chunks(int64_t V)
 {
     const int64_t K = (V + kChunk - 1) / kChunk;
-    return (B < kSplitBelowRows && K <= kMaxChunks) ? (int)K : 0;
+    return K <= kMaxChunks ? (int)K : 0;
+}
+
+// The path a call takes; -1 for a flag combination that cannot run.
+int choose_path(int64_t B, int64_t V, int32_t flags)
+{
+    const int32_t known = NUCLEUS_FLAG_SINGLE_WORKGROUP | NUCLEUS_FLAG_SPLIT_ROWS | NUCLEUS_FLAG_ROW_RACE;
+    if ((flags & ~known) || __builtin_popcount((unsigned)flags) > 1) return -1;
+    if (flags & NUCLEUS_FLAG_SINGLE_WORKGROUP) return kPathFused;
+    if (flags & NUCLEUS_FLAG_ROW_RACE) return kPathRows;
+    if (flags & NUCLEUS_FLAG_SPLIT_ROWS) return tile_chunks(V) ? kPathTile : -1;
+    return (B < kSplitBelowRows && tile_chunks(V)) ? kPathTile : kPathFused;
+}
+
+size_t path_workspace(int path, int64_t B, int64_t V)
+{
+    if (B == 0) return 0;
+    if (path == kPathTile) return work_layout(B, tile_chunks(V), kBins).total;
+    if (path == kPathRows) return row_work_bytes(B, nullptr, nullptr);
+    return 0;
 }
 
 // A distinct 56-bit tag per call.  The sequence starts at a value derived
@@ -61,6 +84,28 @@ uint64_t next_epoch()
         return (t * 0x9E3779B97F4A7C15ull) ^ ((uint64_t)(uintptr_t)&counter << 17);
     }();
     return (base + counter.fetch_add(1) + 1) & ((uint64_t(1) << 56) - 1);
+}
+
+// Workgroups of race_kernel that fit on the current device at once (its
+// occupancy times the CU count), per dtype; 0 if the runtime cannot say.
+int64_t race_workgroups(int32_t dtype)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    static std::mutex mu;
+    static int64_t known[64][2] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    int64_t& k = known[dev][dtype == NUCLEUS_BF16 ? 1 : 0];
+    if (k == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        const hipError_t e = dtype == NUCLEUS_BF16
+                                 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, race_kernel<kBF16>, kRaceThreads, 0)
+                                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, race_kernel<kF32>, kRaceThreads, 0);
+        if (e != hipSuccess || per_cu < 1) return 0;
+        k = (int64_t)cus * per_cu;
+    }
+    return k;
 }
 
 template <class T>
@@ -87,12 +132,16 @@ const char* nucleus_strerror(int code)
     }
 }
 
-size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype)
+size_t nucleus_workspace_bytes_for(int64_t B, int64_t V, int32_t dtype, int32_t flags)
 {
     if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16)) return 0;
-    const int K = chunks_for(B, V);
-    if (B == 0 || K == 0) return 0;
-    return work_layout(B, K, kBins).total;
+    const int path = choose_path(B, V, flags);
+    return path < 0 ? 0 : path_workspace(path, B, V);
+}
+
+size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype)
+{
+    return nucleus_workspace_bytes_for(B, V, dtype, 0);
 }
 
 int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temperature, const float* top_p,
@@ -103,8 +152,8 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     const int64_t stride = (opt && opt->row_stride) ? opt->row_stride : V;
     if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || stride < V) return NUCLEUS_EINVAL;
     if (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16) return NUCLEUS_EINVAL;
-    if (opt && (opt->flags & ~NUCLEUS_FLAG_SINGLE_WORKGROUP) != 0) return NUCLEUS_EINVAL;
-    const bool single = opt && (opt->flags & NUCLEUS_FLAG_SINGLE_WORKGROUP);
+    const int path = choose_path(B, V, opt ? opt->flags : 0);
+    if (path < 0) return NUCLEUS_EINVAL;
     if (B == 0) return NUCLEUS_OK;
     if (!logits || !temperature || !top_p || !out_token || !out_keep_count) return NUCLEUS_EINVAL;
     const size_t esz = dtype == NUCLEUS_F32 ? 4 : 2;
@@ -112,8 +161,7 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
         (min_p && !aligned(min_p)) || !aligned(out_token) || !aligned(out_keep_count) ||
         (out_probs && !aligned(out_probs)) || (opt && opt->out_min_kept_logit && !aligned(opt->out_min_kept_logit)))
         return NUCLEUS_EINVAL;
-    const int K = single ? 0 : chunks_for(B, V);
-    const size_t need = K ? work_layout(B, K, kBins).total : 0;
+    const size_t need = path_workspace(path, B, V);
     if (need > 0 && (!opt || !opt->workspace || opt->workspace_bytes < need || (uintptr_t)opt->workspace % 256))
         return NUCLEUS_EWORKSPACE;
     const int dev_rc = check_device();
@@ -140,7 +188,8 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     p.vec_in = ((uintptr_t)logits % vec_bytes == 0) && ((size_t)stride * esz) % vec_bytes == 0;
 
     hipStream_t s = opt ? (hipStream_t)opt->stream : nullptr;
-    if (K) {
+    if (path == kPathTile) {
+        const int K = tile_chunks(V);
         const WorkLayout L = work_layout(B, K, kBins);
         char* ws = (char*)opt->workspace;
         Work wk;
@@ -157,12 +206,34 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
             hipLaunchKernelGGL(tile_kernel<kF32>, grid, block, 0, s, p, wk);
         else
             hipLaunchKernelGGL(tile_kernel<kBF16>, grid, block, 0, s, p, wk);
+    } else if (path == kPathRows) {
+        size_t next_off = 0, cand_off = 0;
+        row_work_bytes(B, &next_off, &cand_off);
+        RowWork rw;
+        rw.st = (RowPathState*)opt->workspace;
+        rw.next = (uint32_t*)((char*)opt->workspace + next_off);
+        rw.cand = (uint2*)((char*)opt->workspace + cand_off);
+        rw.N = (int)((V + kRaceChunk - 1) / kRaceChunk);
+        const int64_t items = B * rw.N;
+        const int64_t resident = race_workgroups(dtype);
+        if (resident <= 0) return NUCLEUS_ELAUNCH;
+        const dim3 rows((unsigned)B), chunks((unsigned)(padded_rows(B) * rw.N));
+        const dim3 racers((unsigned)(items < resident ? items : resident));
+        if (dtype == NUCLEUS_F32) {
+            hipLaunchKernelGGL((row_kernel<kF32, true>), rows, dim3(kRowThreads), 0, s, p, rw);
+            hipLaunchKernelGGL(race_kernel<kF32>, racers, dim3(kRaceThreads), 0, s, p, rw);
+            if (out_probs) hipLaunchKernelGGL(probs_kernel<kF32>, chunks, dim3(kRaceThreads), 0, s, p, rw);
+        } else {
+            hipLaunchKernelGGL((row_kernel<kBF16, true>), rows, dim3(kRowThreads), 0, s, p, rw);
+            hipLaunchKernelGGL(race_kernel<kBF16>, racers, dim3(kRaceThreads), 0, s, p, rw);
+            if (out_probs) hipLaunchKernelGGL(probs_kernel<kBF16>, chunks, dim3(kRaceThreads), 0, s, p, rw);
+        }
     } else {
-        const dim3 grid((unsigned)B), block(kRowThreads);
+        const RowWork none = {};
         if (dtype == NUCLEUS_F32)
-            hipLaunchKernelGGL(row_kernel<kF32>, grid, block, 0, s, p);
+            hipLaunchKernelGGL((row_kernel<kF32, false>), dim3((unsigned)B), dim3(kRowThreads), 0, s, p, none);
         else
-            hipLaunchKernelGGL(row_kernel<kBF16>, grid, block, 0, s, p);
+            hipLaunchKernelGGL((row_kernel<kBF16, false>), dim3((unsigned)B), dim3(kRowThreads), 0, s, p, none);
     }
     return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
 }

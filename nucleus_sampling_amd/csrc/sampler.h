@@ -305,22 +305,10 @@ struct RaceAcc {
 // The exact race score e_i / E_i of one token (e from the compensated
 // tempered weight, E from the token's Philox word).  Every path computes a
 // winner's score with this one function, so all paths agree bit for bit; the
-// hot loops only reach it for the few tokens that pass race_may_win.
-__device__ __forceinline__ float exact_score(float x, float m, float T, float invT, uint32_t word)
+// hot loops only reach it for the few tokens that pass race_group's screen.
+__device__ __attribute__((noinline)) float exact_score(float x, float m, float T, float invT, uint32_t word)
 {
     return tempered_weight(x, m, T, invT) / exp1_from_word(word);
-}
-
-// Cheap screen before exact_score: a token can only reach the current best
-// score sstar if e_hat * (1 + 1e-4) >= sstar * w, where e_hat approximates
-// e_i to better than 3e-5 relative (|argument| <= 126 before underflow), and
-// w = 1 - u <= -ln u = E_i.  The comparison is strict in the rejecting
-// direction, so a token that could tie the best is never screened out.
-__device__ __forceinline__ bool race_may_win(float x, float m, float c_log2e, uint32_t word, float sstar)
-{
-    const float e_hat = __builtin_amdgcn_exp2f((x - m) * c_log2e);
-    const float w = ((float)(0xFFFFFFFFu - word) + 0.5f) * 0x1p-32f;
-    return !(e_hat * 1.0001f < sstar * w);
 }
 
 __device__ __forceinline__ uint32_t philox_word(const uint4& w4, uint32_t j)
@@ -331,31 +319,51 @@ __device__ __forceinline__ uint32_t philox_word(const uint4& w4, uint32_t j)
 // Race four consecutive tokens i0..i0+3 of which keep[j] are kept.  `scored`
 // is false for greedy rows, where every kept token scores 1 so that the
 // lowest index wins.  sstar is this lane's best exact score so far.
+//
+// The screen.  A token can reach sstar only if e/E >= sstar, i.e. E <= e/sstar,
+// and since E = -ln u falls as u rises, only if u >= exp(-e/sstar).  With
+// e_up = e_hat (1 + 1e-4) >= e (e_hat = exp2 of the scaled logit difference is
+// within 3e-5 of e while |argument| <= 126; below that the token cannot win
+// against the row max, whose score is at least 1/23), theta = exp2(-e_up
+// log2(e) / sstar) is computed in fp32 to within 1e-4 relative (its exponent
+// to within 5e-7 relative while theta is a normal float), and u from the
+// 32-bit word to within 1.2e-7; so u (1 + 1e-4) >= theta holds for every token
+// that can reach sstar, ties included.  Tokens that pass reach exact_score;
+// after the first few groups of a row they are rare.
 __device__ __forceinline__ void race_group(const Params& p, int64_t b, bool scored, const RowModel& r, float c_log2e,
                                            uint32_t i0, const float x[4], const bool keep[4], RaceAcc& acc,
                                            float& sstar)
 {
-    if (!(keep[0] | keep[1] | keep[2] | keep[3])) return;
-    uint4 w4 = make_uint4(0, 0, 0, 0);
-    if (scored) w4 = philox4x32_10(make_uint4(i0 >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
+    const uint32_t km = (keep[0] ? 1u : 0u) | (keep[1] ? 2u : 0u) | (keep[2] ? 4u : 0u) | (keep[3] ? 8u : 0u);
+    if (!km) return;
+    acc.count += (uint32_t)__builtin_popcount(km);
+    float xm = INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xm = keep[j] ? fminf(xm, x[j]) : xm;
+    const uint32_t kmin = order_key(xm);
+    acc.minkey = kmin < acc.minkey ? kmin : acc.minkey;
+    if (!scored) {
+        const uint64_t pk = race_pack(1.0f, i0 + (uint32_t)__builtin_ctz(km));
+        acc.best = pk > acc.best ? pk : acc.best;
+        return;
+    }
+    const uint4 w4 = philox4x32_10(make_uint4(i0 >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
+    const float kz = (sstar > 0.0f ? __builtin_amdgcn_rcpf(sstar) : 3.0e38f) * (-1.4426950408889634f * 1.0001f);
+    uint32_t pass = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        if (!keep[j]) continue;
-        acc.count += 1;
-        const uint32_t k = order_key(x[j]);
-        acc.minkey = k < acc.minkey ? k : acc.minkey;
-        if (!scored) {
-            const uint64_t pk = race_pack(1.0f, i0 + j);
-            acc.best = pk > acc.best ? pk : acc.best;
-            continue;
-        }
-        const uint32_t word = philox_word(w4, j);
-        if (race_may_win(x[j], r.m, c_log2e, word, sstar)) {
-            const float s = exact_score(x[j], r.m, r.T, r.invT, word);
-            const uint64_t pk = race_pack(s, i0 + j);
-            acc.best = pk > acc.best ? pk : acc.best;
-            sstar = fmaxf(sstar, s);
-        }
+        const float e_hat = __builtin_amdgcn_exp2f((x[j] - r.m) * c_log2e);
+        const float theta = __builtin_amdgcn_exp2f(e_hat * kz);
+        const float u = fmaf((float)philox_word(w4, (uint32_t)j), 0x1p-32f, 0x1p-33f);
+        pass |= (keep[j] && u * 1.0001f >= theta) ? (1u << j) : 0u;
+    }
+    while (pass) {
+        const uint32_t j = (uint32_t)__builtin_ctz(pass);
+        pass &= pass - 1u;
+        const float s = exact_score(x[j], r.m, r.T, r.invT, philox_word(w4, j));
+        const uint64_t pk = race_pack(s, i0 + j);
+        acc.best = pk > acc.best ? pk : acc.best;
+        sstar = fmaxf(sstar, s);
     }
 }
 
@@ -997,340 +1005,4 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
 // ---------------------------------------------------------------------------
 // One workgroup per row, every phase streamed from global memory.
 // ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
-// The one-workgroup-per-row kernel.
-// ---------------------------------------------------------------------------
-constexpr int kRowThreads = 1024;  // 16 waves: one workgroup per CU
-constexpr int kRowUnroll = 8;      // 4-token groups per thread whose loads are in flight together
-constexpr int kRowCand = 8192;     // crossing-bin candidates held in LDS
-constexpr int kRaceQueue = 128;    // per-wave ring of 4-token groups waiting for the race
-
-// One aligned 4-token group (f32: 16 bytes, bf16: 8 bytes) at group index g.
-template <int DT, bool NTL>
-__device__ __forceinline__ void load_group(const void* rowp, uint32_t g, float x[4])
-{
-    if (DT == kF32) {
-        const f32x4* a = (const f32x4*)rowp + g;
-        const f32x4 v = NTL ? __builtin_nontemporal_load(a) : *a;
-        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-    } else {
-        const u32x2* a = (const u32x2*)rowp + g;
-        const u32x2 v = NTL ? __builtin_nontemporal_load(a) : *a;
-        x[0] = __uint_as_float(v.x << 16);
-        x[1] = __uint_as_float(v.x & 0xFFFF0000u);
-        x[2] = __uint_as_float(v.y << 16);
-        x[3] = __uint_as_float(v.y & 0xFFFF0000u);
-    }
-}
-
-// Calls f(i0, x[4]) for every 4-token group of the row (tokens at or past V
-// read as -inf).  Each thread takes kRowUnroll groups per step and issues all
-// their loads before using any, so 8 KB per wave are in flight.  Every lane
-// calls f the same number of times (groups past the row are all -inf), so f
-// may use wave-wide operations.  NTL marks the loads non-temporal (the row's
-// last pass).
-template <int DT, bool NTL, class F>
-__device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&& f)
-{
-    const uint32_t V = (uint32_t)p.V;
-    const uint32_t ng = (V + 3) >> 2, nfull = V >> 2;
-    const uint32_t t = threadIdx.x;
-    if (p.vec_in && nfull > 0) {
-        for (uint32_t g0 = 0; g0 < ng; g0 += kRowUnroll * kRowThreads) {
-            float x[kRowUnroll][4];
-#pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const uint32_t g = g0 + (uint32_t)u * kRowThreads + t;
-                load_group<DT, NTL>(rowp, g < nfull ? g : nfull - 1, x[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const uint32_t g = g0 + (uint32_t)u * kRowThreads + t;
-                if (g >= nfull) {  // the row's partial last group, or past the row
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t i = 4 * g + j;
-                        x[u][j] = i < V ? (DT == kF32 ? ((const float*)rowp)[i]
-                                                      : bf16_to_float(((const uint16_t*)rowp)[i]))
-                                        : -INFINITY;
-                    }
-                }
-                f(g << 2, x[u]);
-            }
-        }
-    } else {
-        for (uint32_t g0 = 0; g0 < ng; g0 += kRowThreads) {
-            const uint32_t g = g0 + t;
-            float x[4];
-            load4<DT>(rowp, (int64_t)g << 2, V, 0, x);  // -inf past V
-            f(g << 2, x);
-        }
-    }
-}
-
-// Appends (key, idx) for the lanes with pred to an LDS list: one LDS atomic
-// per wave, positions from the lane's rank among the appending lanes.
-// Appends past `cap` are counted but dropped.
-__device__ __forceinline__ void lds_append(uint32_t* counter, u32x2v* list, uint32_t cap, bool pred, uint32_t key,
-                                           uint32_t idx)
-{
-    const uint64_t mask = __ballot(pred);
-    if (mask == 0) return;
-    const int leader = __builtin_ctzll(mask);
-    const uint32_t lo = (uint32_t)mask, hi = (uint32_t)(mask >> 32);
-    uint32_t base = 0;
-    if ((int)__lane_id() == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-    base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
-    if (pred) {
-        const uint32_t off = base + __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-        if (off < cap) {
-            u32x2v e;
-            e.x = key;
-            e.y = idx;
-            list[off] = e;
-        }
-    }
-}
-
-// Per-wave ring of 4-token groups holding at least one kept token: the race
-// runs on full waves of such groups instead of on every group of the row.
-struct RaceQueue {
-    uint32_t i0[kRaceQueue];
-    f32x4 x[kRaceQueue];
-};
-
-struct RowShared {
-    union {
-        struct {
-            uint64_t hm[kBins];
-            uint32_t hc[kBins];
-        } h;
-        float factor[kBins];
-    } u;
-    u32x2v cand[kRowCand];
-    RaceQueue rq[kRowThreads / kWave];
-    ResolveShared rs;
-    double red[64];
-    float redf[kMaxWaves], redf2[kMaxWaves];
-    int redi[kMaxWaves];
-    uint32_t cand_n;
-    uint32_t sstar_bits;  // best exact race score found so far in the workgroup (bits of a float >= 0)
-};
-
-// Row max, smallest finite logit and error flag over the workgroup: wave
-// reductions, then one exchange through LDS.
-template <int NT>
-__device__ __forceinline__ void block_extremes(float& mx, float& mn, int& bad, float* rf, float* rf2, int* ri)
-{
-    constexpr int W = NT / kWave;
-    mx = wave_reduce(mx, MaxF());
-    mn = wave_reduce(mn, MinF());
-    bad = wave_reduce(bad, OrI32());
-    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-    __syncthreads();
-    if (lane == 0) {
-        rf[w] = mx;
-        rf2[w] = mn;
-        ri[w] = bad;
-    }
-    __syncthreads();
-    mx = rf[0];
-    mn = rf2[0];
-    bad = ri[0];
-#pragma unroll
-    for (int i = 1; i < W; ++i) {
-        mx = fmaxf(mx, rf[i]);
-        mn = fminf(mn, rf2[i]);
-        bad |= ri[i];
-    }
-}
-
-// One workgroup of kRowThreads per row, streaming the row from global memory
-// once per pass (max, histogram, race + candidates, optional probabilities);
-// the crossing bin's candidates stay in LDS for the resolver.  It takes the
-// same decisions with the same arithmetic as tile_kernel.
-template <int DT>
-__global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p)
-{
-    __shared__ RowShared sh;
-    const int64_t b = blockIdx.x;
-    const int t = threadIdx.x;
-    const int64_t esz = DT == kF32 ? 4 : 2;
-    const void* rowp = (const char*)p.logits + b * p.stride * esz;
-    const bool want_probs = p.out_probs != nullptr;
-
-    // ---- pass 1: row max, smallest finite logit, NaN / +inf
-    float lmax = -INFINITY, lmin = INFINITY;
-    int bad = 0;
-    stream_row<DT, false>(p, rowp, [&](uint32_t, const float* xs) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float v = xs[j];
-            bad |= (v != v) | (v == INFINITY);
-            lmax = fmaxf(lmax, v);
-            lmin = (v > -INFINITY) ? fminf(lmin, v) : lmin;
-        }
-    });
-    block_extremes<kRowThreads>(lmax, lmin, bad, sh.redf, sh.redf2, sh.redi);
-    const RowParams rp = row_params(p, b);
-    RowState st;
-    st.mode = uniform(first_mode(bad != 0, lmax, rp.T, rp.P, rp.MP, rp.K, want_probs));
-    st.m = uniform(lmax);
-    st.xmin = uniform(lmin);
-    st.cbin = 0;
-    st.tc = 0;
-    st.a_above = st.s_total = st.s_keep = 0.0;
-    RowModel model = {};
-    if (st.mode >= kModeTop) model = uniform(make_model(st.m, st.xmin, rp.T, rp.MP));
-
-    // ---- pass 2: bin histogram of the survivors
-    if (st.mode == kModeHist) {
-        const bool counts = rp.K > 0;
-        for (int i = t; i < kBins; i += kRowThreads) {
-            sh.u.h.hm[i] = 0;
-            sh.u.h.hc[i] = 0;
-        }
-        __syncthreads();
-        // The last bin takes the whole tail of the row: it is summed in
-        // registers and added once per wave instead of by LDS atomics.
-        uint64_t tail_w = 0;
-        uint32_t tail_c = 0;
-        stream_row<DT, false>(p, rowp, [&](uint32_t, const float* xs) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (survives(model, xs[j])) {
-                    const float tp = bin_pos(model, xs[j]);
-                    const uint32_t jb = bin_of(tp);
-                    const uint32_t fx = bin_fx(model, tp);
-                    if (jb == (uint32_t)(kBins - 1)) {
-                        tail_w += fx;
-                        tail_c += 1;
-                    } else {
-                        atomicAdd((unsigned long long*)&sh.u.h.hm[jb], (unsigned long long)fx);
-                        if (counts) atomicAdd(&sh.u.h.hc[jb], 1u);
-                    }
-                }
-            }
-        });
-        tail_w = wave_reduce(tail_w, SumU64());
-        tail_c = wave_reduce(tail_c, SumU32());
-        if ((t & (kWave - 1)) == 0 && tail_c) {
-            atomicAdd((unsigned long long*)&sh.u.h.hm[kBins - 1], (unsigned long long)tail_w);
-            if (counts) atomicAdd(&sh.u.h.hc[kBins - 1], tail_c);
-        }
-        __syncthreads();
-        const Decision d = decide(model, sh.u.h.hm, counts ? sh.u.h.hc : nullptr, rp.K, rp.P, sh.red);
-        st.mode = uniform(d.mode);
-        st.cbin = uniform(d.cbin);
-        st.tc = uniform(d.tc);
-        st.a_above = uniform(d.a_above);
-        st.s_total = uniform(d.s_total);
-    }
-
-    // ---- pass 3: race the surely kept tokens; the crossing bin's tokens go to LDS
-    const Classes cl = classify(model, st);
-    const float keep_lo = cl.keep_lo, cand_lo = cl.cand_lo;
-    const bool scored = st.mode != kModeGreedy;
-    const bool has_cand = cand_lo < keep_lo;
-    const float c_log2e = model.invT * 1.4426950408889634f;
-    if (t == 0) {
-        sh.cand_n = 0;
-        sh.sstar_bits = 0;
-    }
-    __syncthreads();
-    RaceAcc acc;
-    acc.init();
-    float sstar = 0.0f;
-    RaceQueue& rq = sh.rq[t / kWave];
-    const uint32_t lane = (uint32_t)t & (kWave - 1);
-    uint32_t qh = 0, qn = 0;  // ring head and fill, the same in every lane of the wave
-    // Race the `cnt` (<= 64) oldest queued groups, one per lane.  The screen
-    // uses the best score any wave of the workgroup has reached (a score some
-    // token achieved, so screening against it never drops a possible winner).
-    auto drain = [&](uint32_t cnt) __attribute__((always_inline)) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        const float shared_best = __uint_as_float(sh.sstar_bits);
-        sstar = fmaxf(sstar, shared_best);
-        if (lane < cnt) {
-            const uint32_t slot = (qh + lane) & (kRaceQueue - 1);
-            const f32x4 v = rq.x[slot];
-            const float xs[4] = {v.x, v.y, v.z, v.w};
-            bool keep[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) keep[j] = xs[j] >= keep_lo;
-            race_group(p, b, scored, model, c_log2e, rq.i0[slot], xs, keep, acc, sstar);
-        }
-        const float wave_best = wave_reduce(sstar, MaxF());
-        if (lane == 0 && wave_best > shared_best) atomicMax(&sh.sstar_bits, __float_as_uint(wave_best));
-        qh = (qh + cnt) & (kRaceQueue - 1);
-        qn -= cnt;
-    };
-    stream_row<DT, false>(p, rowp, [&](uint32_t i0, const float* xs) {
-        const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
-        const uint64_t m = __ballot(any);
-        if (m) {
-            if (any) {
-                const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                const uint32_t slot = (qh + qn + r) & (kRaceQueue - 1);
-                f32x4 v;
-                v.x = xs[0]; v.y = xs[1]; v.z = xs[2]; v.w = xs[3];
-                rq.i0[slot] = i0;
-                rq.x[slot] = v;
-            }
-            qn += (uint32_t)__popcll(m);
-            if (qn >= (uint32_t)kWave) drain(kWave);
-        }
-        if (has_cand) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                lds_append(&sh.cand_n, sh.cand, kRowCand, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]),
-                           i0 + j);
-        }
-    });
-    if (qn) drain(qn);
-    acc = block_race<kRowThreads>(acc, sh.rs);
-    const uint32_t n = uniform(sh.cand_n);
-    if (n <= (uint32_t)kRowCand) {
-        resolve_row<kRowThreads>(p, b, model, rp, st, acc,
-                                 [&](auto&& fn) {
-                                     for (uint32_t i = t; i < n; i += kRowThreads) {
-                                         const u32x2v c = sh.cand[i];
-                                         fn(c.x, c.y);
-                                     }
-                                 },
-                                 sh.rs);
-    } else {  // more candidates than LDS holds: visit the row in global memory
-        resolve_row<kRowThreads>(p, b, model, rp, st, acc,
-                                 [&](auto&& fn) {
-                                     stream_row<DT, false>(p, rowp, [&](uint32_t i0, const float* xs) {
-#pragma unroll
-                                         for (int j = 0; j < 4; ++j)
-                                             if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), i0 + j);
-                                     });
-                                 },
-                                 sh.rs);
-    }
-    write_outputs(p, b, st);
-    if (!want_probs) return;
-
-    // ---- pass 4: renormalised probabilities
-    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kRowThreads>(model, st, sh.u.factor);
-    float* prow = p.out_probs + b * p.V;
-    const uint32_t V = (uint32_t)p.V;
-    stream_row<DT, true>(p, rowp, [&](uint32_t i0, const float* xs) {
-        float q[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) q[j] = prob_of(st.mode, model, st, sh.u.factor, xs[j], i0 + j);
-        if (i0 + 4 <= V && ((uintptr_t)(prow + i0) & 15) == 0) {
-            f32x4 v;
-            v.x = q[0]; v.y = q[1]; v.z = q[2]; v.w = q[3];
-            __builtin_nontemporal_store(v, (f32x4*)(prow + i0));
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (i0 + j < V) prow[i0 + j] = q[j];
-        }
-    });
-}
-
 }  // namespace nucleus

@@ -55,7 +55,43 @@ struct Work {
     uint64_t epoch;       // this call's tag (56 bits), distinct for every call
 };
 
-inline int64_t padded_rows(int64_t B) { return (B + 7) / 8 * 8; }
+// Per-row state of the row path (row_kernel publishes the decided state and
+// the row's model for race_kernel and probs_kernel; race_kernel merges the
+// race partials of a row's chunks into it and the row's last chunk writes
+// the outputs back for probs_kernel).  256 bytes.
+struct RowPathState {
+    uint32_t mode;       // row mode (model.h)
+    float m;             // row max
+    float xmin;          // smallest finite logit
+    uint32_t cbin;       // crossing bin (mode P) / last candidate bin (mode K)
+    uint64_t tc;         // mode P threshold inside the crossing bin
+    double a_above;      // mode P: weight of the bins above the crossing bin
+    double s_total;      // weight of all survivors
+    float keep_lo;       // surely kept iff x >= keep_lo
+    float cand_lo;       // candidate iff cand_lo <= x < keep_lo
+    uint64_t best;       // merged race: max of (score bits << 32 | ~index)
+    uint32_t count;      // merged race: kept tokens seen
+    uint32_t minkey;     // merged race: smallest kept key
+    uint32_t cand_n;     // candidates appended
+    uint32_t done;       // chunks finished
+    uint32_t token;      // outputs, for probs_kernel
+    uint32_t out_count;
+    uint32_t cut_key;
+    uint32_t pad0;
+    double s_keep;
+    uint32_t pad[8];
+    uint64_t model[16];  // the row's RowModel (model.h), 128 bytes reserved
+};
+static_assert(sizeof(RowPathState) == 256, "RowPathState layout");
+
+struct RowWork {
+    RowPathState* st;     // [rows]
+    uint32_t* next;       // race_kernel's work counter (reset by row_kernel)
+    uint2* cand;          // [rows][kCap]: key, index
+    int N;                // race chunks per row
+};
+
+__host__ __device__ inline int64_t padded_rows(int64_t B) { return (B + 7) / 8 * 8; }
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -63,6 +99,18 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct WorkLayout {
     size_t ctl, slot_a, slot_h, slot_c, slot_r, cand, total;
 };
+
+// Row-path workspace: [rows] RowPathState, a 256-byte block holding the work
+// counter, then [rows][kCap] candidates.
+inline size_t row_work_bytes(int64_t B, size_t* next_off, size_t* cand_off)
+{
+    const size_t rows = (size_t)padded_rows(B);
+    const size_t nx = align256(rows * sizeof(RowPathState));
+    const size_t off = nx + 256;
+    if (next_off) *next_off = nx;
+    if (cand_off) *cand_off = off;
+    return align256(off + rows * (size_t)kCap * 8);
+}
 
 inline WorkLayout work_layout(int64_t B, int K, int bins)
 {

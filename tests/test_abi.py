@@ -51,7 +51,20 @@ def test_workspace_query(L):
     assert L.nucleus_workspace_bytes(4, 0, 0) == 0
     assert L.nucleus_workspace_bytes(4, 1 << 31, 0) == 0
     assert L.nucleus_workspace_bytes(4, 10, 7) == 0
-    assert ns.workspace_bytes(256, 128256) >= 0
+    # Small batches split rows (per-chunk slots); large ones run a workgroup
+    # per row and need nothing; the chunked-race flag needs per-row state and
+    # a candidate list.
+    assert L.nucleus_workspace_bytes(2, 8, 0) > 0
+    assert L.nucleus_workspace_bytes(256, 128256, 0) == 0
+    assert L.nucleus_workspace_bytes_for(256, 128256, 0, 1) == 0
+    assert L.nucleus_workspace_bytes_for(256, 128256, 0, 4) >= 256 * (256 + 8192 * 8)
+    assert L.nucleus_workspace_bytes_for(256, 128256, 0, 2) > L.nucleus_workspace_bytes_for(256, 128256, 0, 4)
+    small, large = L.nucleus_workspace_bytes_for(2, 8, 0, 4), L.nucleus_workspace_bytes_for(256, 8, 0, 4)
+    assert 0 < small < large and large >= 256 * 8192 * 8  # grows with the rows: per-row state and list
+    assert L.nucleus_workspace_bytes_for(4, 64 * 8192 + 1, 0, 2) == 0  # too long to split
+    assert L.nucleus_workspace_bytes_for(4, 100, 0, 3) == 0            # two flags
+    assert L.nucleus_workspace_bytes_for(4, 100, 0, 8) == 0            # unknown flag
+    assert ns.workspace_bytes(256, 128256) == L.nucleus_workspace_bytes(256, 128256, 0)
 
 
 def _call(L, logits=1 << 20, B=2, V=8, T=1 << 21, P=1 << 22, tok=1 << 23, cnt=1 << 24, opt=None):
@@ -81,9 +94,13 @@ def test_host_side_argument_errors(L):
     opt = ns._Options()
     opt.row_stride = 4  # < V
     assert _call(L, opt=ctypes.byref(opt)) == EINVAL
+    for flags in (8, 3, 5, 6, 7):  # an undefined bit, or more than one flag
+        opt = ns._Options()
+        opt.flags = flags
+        assert _call(L, opt=ctypes.byref(opt)) == EINVAL
     opt = ns._Options()
-    opt.flags = 2  # undefined flag bit
-    assert _call(L, opt=ctypes.byref(opt)) == EINVAL
+    opt.flags = 2
+    assert _call(L, V=64 * 8192 + 1, opt=ctypes.byref(opt)) == EINVAL  # too long to split
     # The default path needs a workspace for these shapes.
     opt = ns._Options()
     assert _call(L, opt=ctypes.byref(opt)) == -2

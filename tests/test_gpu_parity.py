@@ -15,7 +15,14 @@ from gpu_util import device_logits, oracle_and_compare, say
 pytestmark = pytest.mark.gpu
 
 
-def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None, single=False):
+# The library's paths: None = its own choice for the batch; "single" = one
+# workgroup per row for everything; "split" = rows split over
+# register-resident workgroups; "rows" = a workgroup per row for the
+# histogram passes with the race spread over chunks.
+PATHS = [None, "single", "split", "rows"]
+
+
+def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None, path=None):
     import torch
 
     import nucleus_sampling_amd as ns
@@ -23,7 +30,7 @@ def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None, single
     lg = device_logits(w["logits"], w["dtype"]) if lg is None else lg
     res = ns.sample(lg, w["temperature"], w["top_p"], w["top_k"], w["min_p"],
                     seed=w["seed"] if seed is None else seed, step=step, want_probs=want_probs, want_min_kept=True,
-                    single_workgroup=single)
+                    single_workgroup=path == "single", split_rows=path == "split", row_race=path == "rows")
     torch.cuda.synchronize()
     probs = None
     if want_probs:
@@ -74,32 +81,34 @@ def _random_batch(rng, B, V, dtype, extras=True):
     return dict(logits=logits, dtype=dtype, temperature=T, top_p=P, top_k=K, min_p=MP, seed=4242, B=B, V=V)
 
 
+@pytest.mark.parametrize("path", [None, "rows", "single"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [1, 2, 3, 5, 63, 64, 65, 1023, 4097, 9999, 40001])
-def test_small_and_ragged_shapes(V, dtype):
+def test_small_and_ragged_shapes(V, dtype, path):
     rng = np.random.default_rng(V * 7 + (dtype == "bf16"))
     B = 9
     w = _random_batch(rng, B, V, dtype)
-    say(f"ragged V={V} {dtype} B={B}")
-    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(B))
+    say(f"ragged V={V} {dtype} B={B} path={path}")
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(B), path=path)
     rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(B)))
     say(f"ragged V={V} {dtype}: {rep.summary()}")
     assert rep.ok(), rep.failures
 
 
+@pytest.mark.parametrize("path", [None, "rows", "single"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_strided_unaligned_rows(dtype):
+def test_strided_unaligned_rows(dtype, path):
     """Rows whose starts are not 16-byte aligned take the scalar-load path."""
     import torch
 
     rng = np.random.default_rng(17)
     B, V, pad = 6, 3001, 3
     w = _random_batch(rng, B, V, dtype)
-    say(f"strided rows V={V} stride={V + pad} {dtype}")
+    say(f"strided rows V={V} stride={V + pad} {dtype} path={path}")
     base = device_logits(np.pad(w["logits"], ((0, 0), (0, pad))), dtype)
     lg = base[:, :V]
     assert lg.stride(0) == V + pad
-    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(B), lg=lg)
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(B), lg=lg, path=path)
     rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(B)))
     assert rep.ok(), rep.failures
     torch.cuda.synchronize()
@@ -152,23 +161,25 @@ def _edge_batch():
         np.asarray(MP, np.float32)
 
 
+@pytest.mark.parametrize("path", [None, "rows", "single"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_edge_rows(dtype):
+def test_edge_rows(dtype, path):
     L, T, P, K, MP = _edge_batch()
     if dtype == "bf16":
         L = workloads.f32_to_bf16_bits(L)
     w = dict(logits=L, dtype=dtype, temperature=T, top_p=P, top_k=K, min_p=MP, seed=1, B=len(T), V=L.shape[1])
-    say(f"edge rows ({len(T)}) {dtype}")
-    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(len(T)))
+    say(f"edge rows ({len(T)}) {dtype} path={path}")
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(len(T)), path=path)
     rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(len(T))))
     say(f"edge rows {dtype}: {rep.summary()}")
     assert rep.ok(), rep.failures
 
 
-def test_single_column():
+@pytest.mark.parametrize("path", PATHS)
+def test_single_column(path):
     rng = np.random.default_rng(2)
     w = _random_batch(rng, 5, 1, "f32")
-    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(5))
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(5), path=path)
     rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(5)))
     assert rep.ok(), rep.failures
 
@@ -226,21 +237,23 @@ def test_draws_match_oracle_on_worked_example():
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
-def test_split_row_equals_single_workgroup(n):
-    """The register-resident split-row path and the single-workgroup path take
-    the same decisions with the same arithmetic: identical outputs, bit for
-    bit, including the probabilities."""
+def test_paths_agree_bit_for_bit(n):
+    """Every path takes the same decisions with the same arithmetic: the
+    split-row path, the single-workgroup path and the chunked-race path give
+    identical outputs, bit for bit, including the probabilities."""
     rows = PROB_ROWS[n]
-    say(f"workload {n}: split-row vs single-workgroup")
     w = workloads.make(n)
     import torch
 
     lg = device_logits(w["logits"], w["dtype"])
+    say(f"workload {n}: default path")
     a = _gpu(w, lg=lg, want_probs=True, prob_rows=rows)
-    b = _gpu(w, lg=lg, want_probs=True, prob_rows=rows, single=True)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
-    assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
-    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
+    for path in PATHS[1:]:
+        say(f"workload {n}: path {path}")
+        b = _gpu(w, lg=lg, want_probs=True, prob_rows=rows, path=path)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), path
+        assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32)), path
+        assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32)), path
     torch.cuda.synchronize()
 
 
@@ -251,20 +264,26 @@ def test_crossing_bin_overflow(dtype):
     results still match the oracle and the single-workgroup path."""
     V = 40001
     rng = np.random.default_rng(5)
-    L = np.zeros((6, V), np.float32)
+    L = np.zeros((7, V), np.float32)
     L[1, rng.random(V) < 0.5] = 1.0            # two levels, ~20K tokens each
     L[2] = rng.integers(-1, 2, V)              # three levels
     L[3, :] = 0.25                             # one level
     L[4] = rng.normal(0, 1e-6, V)              # near-constant: one narrow bin
     L[5, ::3] = -np.inf
-    T = np.asarray([1.0, 1.0, 0.5, 2.0, 1.0, 1.0], np.float32)
-    P = np.asarray([0.5, 0.6, 0.95, 0.1, 0.5, 0.99], np.float32)
+    L[6] = rng.normal(0, 1, V)                 # 5000 tokens tied above the rest: a crossing bin
+    L[6, rng.choice(V, 5000, replace=False)] = 2.5  # larger than LDS staging, within the list
+    T = np.asarray([1.0, 1.0, 0.5, 2.0, 1.0, 1.0, 1.0], np.float32)
+    P = np.asarray([0.5, 0.6, 0.95, 0.1, 0.5, 0.99, 0.3], np.float32)
+    B = len(T)
     w = dict(logits=workloads.f32_to_bf16_bits(L) if dtype == "bf16" else L, dtype=dtype, temperature=T, top_p=P,
-             top_k=np.zeros(6, np.int32), min_p=np.zeros(6, np.float32), seed=77, B=6, V=V)
+             top_k=np.zeros(B, np.int32), min_p=np.zeros(B, np.float32), seed=77, B=B, V=V)
     say(f"crossing-bin overflow rows {dtype}")
-    a = _gpu(w, want_probs=True, prob_rows=range(6))
-    rep, _ = oracle_and_compare(w, *a[:3], gpu_probs=a[3], prob_rows=list(range(6)))
+    a = _gpu(w, want_probs=True, prob_rows=range(B))
+    rep, _ = oracle_and_compare(w, *a[:3], gpu_probs=a[3], prob_rows=list(range(B)))
     say(f"crossing-bin overflow {dtype}: {rep.summary()}")
     assert rep.ok(), rep.failures
-    b = _gpu(w, want_probs=True, prob_rows=range(6), single=True)
-    assert all(np.array_equal(np.asarray(x).view(np.uint32), np.asarray(y).view(np.uint32)) for x, y in zip(a, b))
+    for path in ("single", "rows"):
+        say(f"crossing-bin overflow {dtype}: path {path}")
+        b = _gpu(w, want_probs=True, prob_rows=range(B), path=path)
+        assert all(np.array_equal(np.asarray(x).view(np.uint32), np.asarray(y).view(np.uint32))
+                   for x, y in zip(a, b)), path
