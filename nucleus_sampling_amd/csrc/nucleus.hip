@@ -69,7 +69,7 @@ size_t path_workspace(int path, int64_t B, int64_t V)
 {
     if (B == 0) return 0;
     if (path == kPathTile) return work_layout(B, tile_chunks(V), kBins).total;
-    if (path == kPathRows) return row_work_bytes(B, nullptr, nullptr);
+    if (path == kPathRows) return row_work_bytes(B, nullptr);
     return 0;
 }
 
@@ -207,26 +207,31 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
         else
             hipLaunchKernelGGL(tile_kernel<kBF16>, grid, block, 0, s, p, wk);
     } else if (path == kPathRows) {
-        size_t next_off = 0, cand_off = 0;
-        row_work_bytes(B, &next_off, &cand_off);
+        size_t cand_off = 0;
+        row_work_bytes(B, &cand_off);
         RowWork rw;
         rw.st = (RowPathState*)opt->workspace;
-        rw.next = (uint32_t*)((char*)opt->workspace + next_off);
         rw.cand = (uint2*)((char*)opt->workspace + cand_off);
-        rw.N = (int)((V + kRaceChunk - 1) / kRaceChunk);
-        const int64_t items = B * rw.N;
+        rw.N = (int)((V + kItemTokens - 1) / kItemTokens);  // race items per row
+        const int64_t waves = B * rw.N;
         const int64_t resident = race_workgroups(dtype);
         if (resident <= 0) return NUCLEUS_ELAUNCH;
-        const dim3 rows((unsigned)B), chunks((unsigned)(padded_rows(B) * rw.N));
-        const dim3 racers((unsigned)(items < resident ? items : resident));
+        const int64_t wgs_needed = (waves + kRaceThreads / kWave - 1) / (kRaceThreads / kWave);
+        const int NC = (int)((V + kRaceChunk - 1) / kRaceChunk);  // probability chunks per row
+        const dim3 rows((unsigned)B), chunks((unsigned)(padded_rows(B) * NC));
+        const dim3 racers((unsigned)(wgs_needed < resident ? wgs_needed : resident));
+        RowWork pw = rw;
+        pw.N = NC;
         if (dtype == NUCLEUS_F32) {
             hipLaunchKernelGGL((row_kernel<kF32, true>), rows, dim3(kRowThreads), 0, s, p, rw);
             hipLaunchKernelGGL(race_kernel<kF32>, racers, dim3(kRaceThreads), 0, s, p, rw);
-            if (out_probs) hipLaunchKernelGGL(probs_kernel<kF32>, chunks, dim3(kRaceThreads), 0, s, p, rw);
+            hipLaunchKernelGGL(resolve_kernel<kF32>, rows, dim3(kRaceThreads), 0, s, p, rw);
+            if (out_probs) hipLaunchKernelGGL(probs_kernel<kF32>, chunks, dim3(kRaceThreads), 0, s, p, pw);
         } else {
             hipLaunchKernelGGL((row_kernel<kBF16, true>), rows, dim3(kRowThreads), 0, s, p, rw);
             hipLaunchKernelGGL(race_kernel<kBF16>, racers, dim3(kRaceThreads), 0, s, p, rw);
-            if (out_probs) hipLaunchKernelGGL(probs_kernel<kBF16>, chunks, dim3(kRaceThreads), 0, s, p, rw);
+            hipLaunchKernelGGL(resolve_kernel<kBF16>, rows, dim3(kRaceThreads), 0, s, p, rw);
+            if (out_probs) hipLaunchKernelGGL(probs_kernel<kBF16>, chunks, dim3(kRaceThreads), 0, s, p, pw);
         }
     } else {
         const RowWork none = {};

@@ -30,8 +30,9 @@ namespace nucleus {
 
 constexpr int kRowThreads = 1024;  // 16 waves: one workgroup per CU
 constexpr int kRowUnroll = 8;      // 4-token groups per thread whose loads are in flight together
-constexpr int kRowCand = 8192;     // crossing-bin candidates held in LDS
-constexpr int kRaceQueue = 128;    // per-wave ring of 4-token groups waiting for the race
+constexpr int kRowCand = 4096;     // crossing-bin candidates held in LDS
+constexpr int kRaceQueue = 256;    // per-wave ring of 4-token groups waiting for the race
+constexpr int kDrain = 2 * kWave;  // groups raced per drain: two per lane
 constexpr int kRaceThreads = 256;  // race_kernel / probs_kernel workgroups
 constexpr int kRaceUnroll = 8;
 constexpr int kRaceChunk = kRaceThreads * kRaceUnroll * 4;  // tokens per race_kernel workgroup
@@ -54,50 +55,145 @@ __device__ __forceinline__ void load_group(const void* rowp, uint32_t g, float x
     }
 }
 
-// Calls f(i0, x[4]) for the 4-token groups g0 + u * NT + t (u < U) of a row,
-// t = threadIdx.x; tokens at or past V read as -inf.  All U loads are issued
-// before any is used.  Every lane calls f U times, so f may use wave-wide
-// operations.  NTL marks the loads non-temporal.
-template <int DT, bool NTL, int NT, int U, class F>
-__device__ __forceinline__ void load_groups(const Params& p, const void* rowp, uint32_t g0, F&& f)
+// Loads the 4-token groups g0 + u * NT + t (u < U) of a row into x (t: the
+// thread's index among the NT that share the work), all loads issued back to
+// back.  fix_groups must run on x before it is used.  NTL marks the loads
+// non-temporal.
+template <int DT, bool NTL, int NT, int U>
+__device__ __forceinline__ void issue_groups(const Params& p, const void* rowp, uint32_t g0, uint32_t t, float x[U][4])
 {
     const uint32_t V = (uint32_t)p.V;
     const uint32_t nfull = V >> 2;
-    const uint32_t t = threadIdx.x;
-    float x[U][4];
     if (p.vec_in && nfull > 0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t g = g0 + (uint32_t)u * NT + t;
             load_group<DT, NTL>(rowp, g < nfull ? g : nfull - 1, x[u]);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t g = g0 + (uint32_t)u * NT + t;
-            if (g >= nfull) {  // the row's partial last group, or past the row
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t i = 4 * g + j;
-                    x[u][j] = i < V ? (DT == kF32 ? ((const float*)rowp)[i]
-                                                  : bf16_to_float(((const uint16_t*)rowp)[i]))
-                                    : -INFINITY;
-                }
-            }
-        }
     } else {
 #pragma unroll
         for (int u = 0; u < U; ++u) load4<DT>(rowp, (int64_t)(g0 + (uint32_t)u * NT + t) << 2, V, 0, x[u]);
     }
+}
+
+// Tokens at or past V read as -inf; the row's partial last group is loaded
+// one token at a time.
+template <int DT, int NT, int U>
+__device__ __forceinline__ void fix_groups(const Params& p, const void* rowp, uint32_t g0, uint32_t t, float x[U][4])
+{
+    const uint32_t V = (uint32_t)p.V;
+    const uint32_t nfull = V >> 2;
+    if (!(p.vec_in && nfull > 0)) return;  // the scalar path already did
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t g = g0 + (uint32_t)u * NT + t;
+        if (g >= nfull) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t i = 4 * g + j;
+                x[u][j] = i < V ? (DT == kF32 ? ((const float*)rowp)[i] : bf16_to_float(((const uint16_t*)rowp)[i]))
+                                : -INFINITY;
+            }
+        }
+    }
+}
+
+// Calls f(i0, x[4]) for the 4-token groups g0 + u * NT + t (u < U) of a row
+// (t: the thread's index among the NT that share the work); tokens at or
+// past V read as -inf.  All U loads are issued before any is used.  Every
+// lane calls f U times, so f may use wave-wide operations.
+template <int DT, bool NTL, int NT, int U, class F>
+__device__ __forceinline__ void load_groups(const Params& p, const void* rowp, uint32_t g0, uint32_t t, F&& f)
+{
+    float x[U][4];
+    issue_groups<DT, NTL, NT, U>(p, rowp, g0, t, x);
+    fix_groups<DT, NT, U>(p, rowp, g0, t, x);
 #pragma unroll
     for (int u = 0; u < U; ++u) f((g0 + (uint32_t)u * NT + t) << 2, x[u]);
 }
 
-// load_groups over the whole row, kRowUnroll groups per thread per step.
+// Vector loads of the whole groups g0 + u * NT + t (u < U) of an aligned
+// row (addresses clamped to the last whole group; mask_whole sets the rest).
+template <int DT, bool NTL, int NT, int U>
+__device__ __forceinline__ void issue_whole(const void* rowp, uint32_t g0, uint32_t t, uint32_t nfull, float x[U][4])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t g = g0 + (uint32_t)u * NT + t;
+        load_group<DT, NTL>(rowp, g < nfull ? g : nfull - 1, x[u]);
+    }
+}
+
+// Groups past the whole groups read as -inf (selects only: no loads, so the
+// loads still in flight for the other buffer are not waited for).
+template <int NT, int U>
+__device__ __forceinline__ void mask_whole(uint32_t g0, uint32_t t, uint32_t nfull, float x[U][4])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool in = g0 + (uint32_t)u * NT + t < nfull;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[u][j] = in ? x[u][j] : -INFINITY;
+    }
+}
+
+// Calls f(i0, x[4]) for every 4-token group of the row, the same number of
+// times in every lane (so f may use wave-wide operations); a call for no
+// token of the row passes -inf values and an i0 past V.
+//
+// Aligned rows are software-pipelined: two register buffers of
+// kRowUnroll / 2 groups per thread, the next one's loads in flight while f
+// runs on the current one.  The row's partial last group (V not a multiple
+// of 4) takes one more call after the loop, loaded token by token.
 template <int DT, bool NTL, int NT, class F>
 __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&& f)
 {
-    const uint32_t ng = ((uint32_t)p.V + 3) >> 2;
-    for (uint32_t g0 = 0; g0 < ng; g0 += kRowUnroll * NT) load_groups<DT, NTL, NT, kRowUnroll>(p, rowp, g0, f);
+    const uint32_t V = (uint32_t)p.V;
+    const uint32_t ng = (V + 3) >> 2, nfull = V >> 2;
+    const uint32_t t = threadIdx.x;
+    const uint32_t past = ng << 2;  // an i0 no token of the row has
+    if (p.vec_in && nfull > 0) {
+        constexpr int H = kRowUnroll / 2;
+        constexpr uint32_t step = H * NT;
+        float xa[H][4], xb[H][4];
+        issue_whole<DT, NTL, NT, H>(rowp, 0, t, nfull, xa);
+        for (uint32_t g0 = 0; g0 < nfull; g0 += 2 * step) {
+            issue_whole<DT, NTL, NT, H>(rowp, g0 + step, t, nfull, xb);
+            mask_whole<NT, H>(g0, t, nfull, xa);
+#pragma unroll
+            for (int u = 0; u < H; ++u) {
+                const uint32_t g = g0 + (uint32_t)u * NT + t;
+                f(g < nfull ? g << 2 : past, xa[u]);
+            }
+            if (g0 + step >= nfull) break;  // uniform: the second buffer holds no whole group
+            if (g0 + 2 * step < nfull) issue_whole<DT, NTL, NT, H>(rowp, g0 + 2 * step, t, nfull, xa);
+            mask_whole<NT, H>(g0 + step, t, nfull, xb);
+#pragma unroll
+            for (int u = 0; u < H; ++u) {
+                const uint32_t g = g0 + step + (uint32_t)u * NT + t;
+                f(g < nfull ? g << 2 : past, xb[u]);
+            }
+        }
+        if (V & 3u) {  // uniform: the partial last group
+            const bool own = t == nfull % NT;
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t i = 4 * nfull + j;
+                x[j] = (own && i < V) ? (DT == kF32 ? ((const float*)rowp)[i]
+                                                    : bf16_to_float(((const uint16_t*)rowp)[i]))
+                                      : -INFINITY;
+            }
+            f(own ? nfull << 2 : past, x);
+        }
+    } else {  // unaligned rows: token by token
+        for (uint32_t g0 = 0; g0 < ng; g0 += NT) {
+            const uint32_t g = g0 + t;
+            float x[4];
+            load4<DT>(rowp, (int64_t)g << 2, V, 0, x);  // -inf past V
+            f(g < ng ? g << 2 : past, x);
+        }
+    }
 }
 
 // Appends (key, idx) for the lanes with pred to an LDS list: one LDS atomic
@@ -133,17 +229,27 @@ struct RaceQueue {
 
 
 // Per-wave compaction of race work.  A group whose lanes hold a kept token
-// joins the wave's ring; once 64 wait, every lane races one.  `race(active,
-// i0, x)` is called by all lanes of the wave (it may use wave operations).
+// joins the wave's ring; once kDrain wait, every lane races two (lane l takes
+// the l-th and (64 + l)-th oldest).  `race(i0[2], x[2][4], active[2])` is
+// called by all lanes of the wave (it may use wave operations).
 template <class Race>
 __device__ __forceinline__ void wq_drain(RaceQueue& rq, uint32_t& qh, uint32_t& qn, uint32_t lane, uint32_t cnt,
                                          Race&& race)
 {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    const uint32_t slot = (qh + lane) & (kRaceQueue - 1);
-    const f32x4 v = rq.x[slot];
-    const float xs[4] = {v.x, v.y, v.z, v.w};
-    race(lane < cnt, rq.i0[slot], xs);
+    uint32_t i0[2];
+    float xs[2][4];
+    bool active[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t k = lane + (uint32_t)h * kWave;
+        const uint32_t slot = (qh + k) & (kRaceQueue - 1);
+        const f32x4 v = rq.x[slot];
+        xs[h][0] = v.x; xs[h][1] = v.y; xs[h][2] = v.z; xs[h][3] = v.w;
+        i0[h] = rq.i0[slot];
+        active[h] = k < cnt;
+    }
+    race(i0, xs, active);
     qh = (qh + cnt) & (kRaceQueue - 1);
     qn -= cnt;
 }
@@ -163,24 +269,24 @@ __device__ __forceinline__ void wq_push(RaceQueue& rq, uint32_t& qh, uint32_t& q
         rq.x[slot] = v;
     }
     qn += (uint32_t)__popcll(m);
-    if (qn >= (uint32_t)kWave) wq_drain(rq, qh, qn, lane, kWave, race);
+    if (qn >= (uint32_t)kDrain) wq_drain(rq, qh, qn, lane, kDrain, race);
 }
 
-// One race step for a queued group: screen against the best score any wave
-// of the workgroup has reached (a score some token achieved, so the screen
-// never drops a possible winner), race, and publish the wave's best.
+// One race step for two queued groups: screen against the best score any
+// wave of the workgroup has reached (a score some token achieved, so the
+// screen never drops a possible winner), race, and publish the wave's best.
 __device__ __forceinline__ void race_queued(const Params& p, int64_t b, bool scored, const RowModel& r,
-                                            float c_log2e, float keep_lo, bool active, uint32_t i0, const float* xs,
-                                            RaceAcc& acc, float& sstar, uint32_t* shared_bits)
+                                            float c_log2e, float keep_lo, const uint32_t i0[2], const float xs[2][4],
+                                            const bool active[2], RaceAcc& acc, float& sstar, uint32_t* shared_bits)
 {
     const float shared_best = __uint_as_float(*shared_bits);
     sstar = fmaxf(sstar, shared_best);
-    if (active) {
-        bool keep[4];
+    bool keep[2][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) keep[j] = xs[j] >= keep_lo;
-        race_group(p, b, scored, r, c_log2e, i0, xs, keep, acc, sstar);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) keep[h][j] = active[h] && xs[h][j] >= keep_lo;
+    race_groups<2>(p, b, scored, r, c_log2e, i0, xs, keep, acc, sstar);
     // Publish only when some lane improved on the shared best (after the first
     // few groups that is rare, and the wave reduction is skipped).
     if (__ballot(sstar > shared_best)) {
@@ -383,10 +489,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     const Classes cl = classify(model, st);
     const float keep_lo = cl.keep_lo, cand_lo = cl.cand_lo;
     if (PUBLISH) {
-        if (t == 0) {
-            publish_row(rw.st + b, st, model, keep_lo, cand_lo);
-            if (b == 0) *rw.next = 0;  // race_kernel's work counter (it runs after this launch)
-        }
+        if (t == 0) publish_row(rw.st + b, st, model, keep_lo, cand_lo);
         return;
     }
 
@@ -405,8 +508,8 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     RaceQueue& rq = sh.rq[t / kWave];
     const uint32_t lane = (uint32_t)t & (kWave - 1);
     uint32_t qh = 0, qn = 0;  // ring head and fill, the same in every lane of the wave
-    auto race = [&](bool active, uint32_t i0, const float* xs) __attribute__((always_inline)) {
-        race_queued(p, b, scored, model, c_log2e, keep_lo, active, i0, xs, acc, sstar, &sh.sstar_bits);
+    auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
+        race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits);
     };
     stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
         const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
@@ -491,98 +594,138 @@ __device__ __forceinline__ RowState published_state(const RowPathState* ps)
     return st;
 }
 
-struct RaceShared {
-    union {
-        RaceQueue rq[kRaceThreads / kWave];
-        u32x2v cand[kCandLds];  // the resolver's staged candidates
-    } u;
-    ResolveShared rs;
-    uint32_t sstar_bits;
-    uint32_t last;
-    uint32_t grab[2];  // work items, by iteration parity (see race_kernel)
-    uint64_t part_best;
-    uint32_t part_count, part_min, part_n;
-};
+// ---------------------------------------------------------------------------
+// The chunked race (race_kernel) and the per-row resolver (resolve_kernel).
+// ---------------------------------------------------------------------------
+constexpr int kItemGroups = 8;                         // groups per lane per work item
+constexpr int kItemTokens = kWave * kItemGroups * 4;   // 2048 tokens per item
 
-// A row's state as race_kernel needs it.
-struct RaceRow {
-    RowState st;
-    RowModel model;
-    RowParams rp;
-    float keep_lo, cand_lo, c_log2e;
-    bool scored, has_cand;
-};
-
-__device__ __forceinline__ RaceRow race_row(const Params& p, const RowPathState* ps, int64_t b)
+// Every wave of race_kernel works alone on 2048-token items of the batch:
+// item k is chunk k / B of row k % B, and wave w of the W launched takes items
+// w, w + W, w + 2W, ...  The waves resident on a CU thus hold chunks of many
+// rows, so rows that keep many tokens (whose Philox draws dominate) and rows
+// that keep few share every CU.  A wave races its item's kept tokens through
+// its ring, appends the item's candidates to the row's list and merges its
+// race partial into the row with order-free atomics (max of the packed
+// score, sums, min).  No barrier, no waiting, no shared work counter:
+// resolve_kernel, the next launch, reads the merged results.
+template <int DT>
+__global__ __launch_bounds__(kRaceThreads, 4) void race_kernel(Params p, RowWork rw)
 {
-    RaceRow r;
-    r.st = published_state(ps);
-    r.model = uniform(*(const RowModel*)ps->model);
-    r.rp = row_params(p, b);
-    r.keep_lo = uniform(ps->keep_lo);
-    r.cand_lo = uniform(ps->cand_lo);
-    r.scored = r.st.mode != kModeGreedy;
-    r.has_cand = r.cand_lo < r.keep_lo;
-    r.c_log2e = r.model.invT * 1.4426950408889634f;
-    return r;
+    __shared__ RaceQueue rings[kRaceThreads / kWave];
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    RaceQueue& rq = rings[threadIdx.x / kWave];
+    const uint32_t B = (uint32_t)p.B;
+    const uint32_t NI = (uint32_t)rw.N;  // items per row
+    const uint32_t total = B * NI;
+    const int64_t esz = DT == kF32 ? 4 : 2;
+    const uint32_t waves = gridDim.x * (kRaceThreads / kWave);
+    for (uint32_t item = blockIdx.x * (kRaceThreads / kWave) + threadIdx.x / kWave; item < total; item += waves) {
+        const int64_t b = item % B;
+        const uint32_t chunk = item / B;
+        RowPathState* ps = rw.st + b;
+        const uint32_t mode = uniform(ps->mode);
+        if (mode == kModeError) continue;
+        const RowModel model = uniform(*(const RowModel*)ps->model);
+        const float keep_lo = uniform(ps->keep_lo), cand_lo = uniform(ps->cand_lo);
+        const bool scored = mode != kModeGreedy, has_cand = cand_lo < keep_lo;
+        const float c_log2e = model.invT * 1.4426950408889634f;
+        const void* rowp = (const char*)p.logits + b * p.stride * esz;
+        const __amdgpu_buffer_rsrc_t rk = coherent(rw.cand + b * kCap);
+        // The screen starts from the best score the row has reached so far.
+        float wbest = scored ? __uint_as_float((uint32_t)(get(&ps->best) >> 32)) : 0.0f;
+        float sstar = wbest;
+        RaceAcc acc;
+        acc.init();
+        uint32_t qh = 0, qn = 0;
+        auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
+            bool keep[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) keep[h][j] = active[h] && xs[h][j] >= keep_lo;
+            race_groups<2>(p, b, scored, model, c_log2e, i0, xs, keep, acc, sstar);
+            // Share the wave's best score only when some lane improved it.
+            if (__ballot(sstar > wbest)) wbest = wave_reduce(sstar, MaxF());
+            sstar = fmaxf(sstar, wbest);
+        };
+        load_groups<DT, false, kWave, kItemGroups>(
+            p, rowp, chunk * (uint32_t)(kItemTokens / 4), lane, [&](uint32_t i0, const float* xs) {
+                const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
+                wq_push(rq, qh, qn, lane, any, i0, xs, race);
+                if (has_cand) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        global_append(&ps->cand_n, rk, kCap, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]),
+                                      i0 + j);
+                }
+            });
+        if (qn) wq_drain(rq, qh, qn, lane, qn, race);
+        const uint64_t best = wave_reduce(acc.best, MaxU64());
+        const uint32_t count = wave_reduce(acc.count, SumU32());
+        const uint32_t minkey = wave_reduce(acc.minkey, MinU32());
+        if (lane == 0 && count) {
+            __hip_atomic_fetch_max(&ps->best, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&ps->count, count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_min(&ps->minkey, minkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
-// The last chunks of row b are done: resolve the cut from the merged race
-// partial and the row's candidate list, write the outputs.
+struct ResolveKShared {
+    u32x2v cand[kCandLds];
+    ResolveShared rs;
+};
+
+// After race_kernel: one workgroup per row resolves the exact cut from the
+// merged race partial and the row's candidate list, and writes the outputs.
 template <int DT>
-__device__ __forceinline__ void resolve_last(const Params& p, const RowWork& rw, int64_t b, RaceRow& r,
-                                             RaceShared& sh)
+__global__ __launch_bounds__(kRaceThreads) void resolve_kernel(Params p, RowWork rw)
 {
+    __shared__ ResolveKShared sh;
+    const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
     RowPathState* ps = rw.st + b;
+    RowState st = published_state(ps);
+    const RowModel model = uniform(*(const RowModel*)ps->model);
+    const RowParams rp = row_params(p, b);
+    const float cand_lo = uniform(ps->cand_lo), keep_lo = uniform(ps->keep_lo);
+    RaceAcc part;
+    part.best = uniform(ps->best);
+    part.count = uniform(ps->count);
+    part.minkey = uniform(ps->minkey);
+    const uint32_t n = uniform(ps->cand_n);
+    const uint2* list = rw.cand + b * kCap;
     const int64_t esz = DT == kF32 ? 4 : 2;
     const void* rowp = (const char*)p.logits + b * p.stride * esz;
-    const __amdgpu_buffer_rsrc_t rk = coherent(rw.cand + b * kCap);
-    if (t == 0) {
-        sh.part_best = get(&ps->best);
-        sh.part_count = get(&ps->count);
-        sh.part_min = get(&ps->minkey);
-        sh.part_n = get(&ps->cand_n);
-    }
-    __syncthreads();
-    RaceAcc part;
-    part.best = uniform(sh.part_best);
-    part.count = uniform(sh.part_count);
-    part.minkey = uniform(sh.part_min);
-    const uint32_t n = uniform(sh.part_n);
-    const float cand_lo = r.cand_lo, keep_lo = r.keep_lo;
     if (n <= (uint32_t)kCandLds) {
-        for (uint32_t i0 = t; i0 < n; i0 += 4 * kRaceThreads) {
-            u32x2v c[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t i = i0 + u * kRaceThreads;
-                c[u] = __builtin_amdgcn_raw_buffer_load_b64(rk, (i < n ? i : 0) * 8, 0, kSC1);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (i0 + u * kRaceThreads < n) sh.u.cand[i0 + u * kRaceThreads] = c[u];
+        for (uint32_t i = t; i < n; i += kRaceThreads) {
+            const uint2 c = list[i];
+            u32x2v e;
+            e.x = c.x;
+            e.y = c.y;
+            sh.cand[i] = e;
         }
         __syncthreads();
-        resolve_row<kRaceThreads>(p, b, r.model, r.rp, r.st, part,
+        resolve_row<kRaceThreads>(p, b, model, rp, st, part,
                                   [&](auto&& fn) {
                                       for (uint32_t i = t; i < n; i += kRaceThreads) {
-                                          const u32x2v c = sh.u.cand[i];
+                                          const u32x2v c = sh.cand[i];
                                           fn(c.x, c.y);
                                       }
                                   },
                                   sh.rs);
     } else if (n <= (uint32_t)kCap) {
-        resolve_row<kRaceThreads>(p, b, r.model, r.rp, r.st, part,
+        resolve_row<kRaceThreads>(p, b, model, rp, st, part,
                                   [&](auto&& fn) {
                                       for (uint32_t i = t; i < n; i += kRaceThreads) {
-                                          const u32x2v c = __builtin_amdgcn_raw_buffer_load_b64(rk, i * 8, 0, kSC1);
+                                          const uint2 c = list[i];
                                           fn(c.x, c.y);
                                       }
                                   },
                                   sh.rs);
     } else {  // the crossing bin overflowed the list: visit the row in global memory
-        resolve_row<kRaceThreads>(p, b, r.model, r.rp, r.st, part,
+        resolve_row<kRaceThreads>(p, b, model, rp, st, part,
                                   [&](auto&& fn) {
                                       stream_row<DT, false, kRaceThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
 #pragma unroll
@@ -592,118 +735,12 @@ __device__ __forceinline__ void resolve_last(const Params& p, const RowWork& rw,
                                   },
                                   sh.rs);
     }
-    write_outputs(p, b, r.st);
+    write_outputs(p, b, st);
     if (t == 0) {
-        ps->token = r.st.token;
-        ps->out_count = r.st.count;
-        ps->cut_key = r.st.cut_key;
-        ps->s_keep = r.st.s_keep;
-    }
-    __syncthreads();  // the LDS staging area is the race queue's
-}
-
-// The race pass, spread over the device: about one resident round of
-// workgroups takes 8192-token chunks (row-major) from a counter in the
-// workspace, the next one requested while the current one is raced.  A
-// workgroup keeps a row's state and race partial across consecutive chunks
-// of that row and merges them into the row once per run; the run that
-// finishes a row resolves it on the spot.  No workgroup waits for another.
-template <int DT>
-__global__ __launch_bounds__(kRaceThreads, 4) void race_kernel(Params p, RowWork rw)
-{
-    __shared__ RaceShared sh;
-    const uint32_t N = (uint32_t)rw.N;
-    const uint32_t total = (uint32_t)p.B * N;
-    const int t = threadIdx.x;
-    const uint32_t lane = (uint32_t)t & (kWave - 1);
-    const int64_t esz = DT == kF32 ? 4 : 2;
-    RaceQueue& rq = sh.u.rq[t / kWave];
-
-    if (t == 0) sh.grab[0] = __hip_atomic_fetch_add(rw.next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    uint32_t item = uniform(sh.grab[0]);
-    uint32_t parity = 0;
-    int64_t cur = -1;   // row of the current run
-    uint32_t run = 0;   // chunks of that row raced since the last merge
-    RaceRow r = {};
-    RaceAcc acc;
-    acc.init();
-    float sstar = 0.0f;
-    uint32_t qh = 0, qn = 0;
-    for (;;) {
-        const int64_t b = item < total ? (int64_t)(item / N) : -1;  // -1: no work left
-        // A new row, or no work left (possibly on the first grab, when other
-        // workgroups took every item first: then there is no run to close).
-        if (b != cur || b < 0) {
-            if (cur >= 0) {
-                // Close the run: drain the queue, merge, and resolve the row if
-                // this run finished it.
-                RowPathState* pc = rw.st + cur;
-                auto race = [&](bool active, uint32_t i0, const float* xs) __attribute__((always_inline)) {
-                    race_queued(p, cur, r.scored, r.model, r.c_log2e, r.keep_lo, active, i0, xs, acc, sstar,
-                                &sh.sstar_bits);
-                };
-                if (qn) wq_drain(rq, qh, qn, lane, qn, race);
-                acc = block_race<kRaceThreads>(acc, sh.rs);
-                if (t == 0 && acc.count) {
-                    __hip_atomic_fetch_max(&pc->best, acc.best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_fetch_add(&pc->count, acc.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_fetch_min(&pc->minkey, acc.minkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-                // Every store and atomic of the run completes before it is
-                // counted; the run that completes the row then sees them all.
-                drain_and_sync();
-                if (t == 0)
-                    sh.last = (__hip_atomic_fetch_add(&pc->done, run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
-                               run == N);
-                __syncthreads();
-                if (sh.last) resolve_last<DT>(p, rw, cur, r, sh);
-            }
-            if (b < 0) break;
-            cur = b;
-            run = 0;
-            acc.init();
-            sstar = 0.0f;
-            qh = qn = 0;
-            r = race_row(p, rw.st + b, b);
-            // The screen starts from the best score the row has reached so far.
-            if (t == 0) sh.sstar_bits = r.scored ? (uint32_t)(get(&rw.st[b].best) >> 32) : 0u;
-            __syncthreads();
-        }
-        // Ask for the next item now; it is needed only after this chunk.
-        uint32_t nxt = 0;
-        if (t == 0) nxt = __hip_atomic_fetch_add(rw.next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (r.st.mode != kModeError) {
-            const void* rowp = (const char*)p.logits + b * p.stride * esz;
-            RowPathState* ps = rw.st + b;
-            const __amdgpu_buffer_rsrc_t rk = coherent(rw.cand + b * kCap);
-            auto race = [&](bool active, uint32_t i0, const float* xs) __attribute__((always_inline)) {
-                race_queued(p, b, r.scored, r.model, r.c_log2e, r.keep_lo, active, i0, xs, acc, sstar,
-                            &sh.sstar_bits);
-            };
-            const float keep_lo = r.keep_lo, cand_lo = r.cand_lo;
-            const bool has_cand = r.has_cand;
-            load_groups<DT, false, kRaceThreads, kRaceUnroll>(
-                p, rowp, (item % N) * (uint32_t)(kRaceChunk / 4), [&](uint32_t i0, const float* xs) {
-                    const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
-                    wq_push(rq, qh, qn, lane, any, i0, xs, race);
-                    if (has_cand) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            global_append(&ps->cand_n, rk, kCap, xs[j] >= cand_lo && xs[j] < keep_lo,
-                                          order_key(xs[j]), i0 + j);
-                    }
-                });
-        }
-        ++run;
-        // A chunk has no workgroup barrier, so thread 0 may publish the next
-        // item while a slower wave has yet to read this one: the two live
-        // items use alternate slots, and a slot is rewritten only after the
-        // barrier every wave passes once it has read it.
-        parity ^= 1u;
-        if (t == 0) sh.grab[parity] = nxt;
-        __syncthreads();
-        item = uniform(sh.grab[parity]);
+        ps->token = st.token;
+        ps->out_count = st.count;
+        ps->cut_key = st.cut_key;
+        ps->s_keep = st.s_keep;
     }
 }
 
@@ -728,7 +765,7 @@ __global__ __launch_bounds__(kRaceThreads) void probs_kernel(Params p, RowWork r
     float* prow = p.out_probs + b * p.V;
     const uint32_t V = (uint32_t)p.V;
     load_groups<DT, true, kRaceThreads, kRaceUnroll>(
-        p, rowp, cid.chunk * (uint32_t)(kRaceChunk / 4), [&](uint32_t i0, const float* xs) {
+        p, rowp, cid.chunk * (uint32_t)(kRaceChunk / 4), threadIdx.x, [&](uint32_t i0, const float* xs) {
             float q[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) q[j] = prob_of(st.mode, model, st, factor, xs[j], i0 + j);

@@ -316,55 +316,109 @@ __device__ __forceinline__ uint32_t philox_word(const uint4& w4, uint32_t j)
     return j == 0 ? w4.x : j == 1 ? w4.y : j == 2 ? w4.z : w4.w;
 }
 
-// Race four consecutive tokens i0..i0+3 of which keep[j] are kept.  `scored`
-// is false for greedy rows, where every kept token scores 1 so that the
-// lowest index wins.  sstar is this lane's best exact score so far.
+// Race G groups of four consecutive tokens (group g starts at token i0[g];
+// keep[g][j] marks the kept ones).  `scored` is false for greedy rows, where
+// every kept token scores 1 so that the lowest index wins.  sstar is this
+// lane's best exact score so far.  Several groups per call let the Philox
+// rounds of different groups interleave.
 //
-// The screen.  A token can reach sstar only if e/E >= sstar, i.e. E <= e/sstar,
-// and since E = -ln u falls as u rises, only if u >= exp(-e/sstar).  With
-// e_up = e_hat (1 + 1e-4) >= e (e_hat = exp2 of the scaled logit difference is
-// within 3e-5 of e while |argument| <= 126; below that the token cannot win
-// against the row max, whose score is at least 1/23), theta = exp2(-e_up
-// log2(e) / sstar) is computed in fp32 to within 1e-4 relative (its exponent
-// to within 5e-7 relative while theta is a normal float), and u from the
-// 32-bit word to within 1.2e-7; so u (1 + 1e-4) >= theta holds for every token
-// that can reach sstar, ties included.  Tokens that pass reach exact_score;
-// after the first few groups of a row they are rare.
+// The screen.  A token can reach sstar only if e/E >= sstar, i.e.
+// E <= e/sstar; and E = -ln u >= w = 1 - u.  So a token with
+// w > e_up/sstar, e_up = e_hat (1 + 1e-4) >= e, cannot reach sstar (e_hat =
+// exp2 of the scaled logit difference is within 3e-5 of e while |argument|
+// <= 126; below that the token cannot win against the row max, whose score is
+// at least 1/23).  w comes from the 32-bit word to within 1.2e-7 relative and
+// 1/sstar from the hardware reciprocal to within 2^-23, so rejecting when
+// w (1 - 1e-4) > e_up / sstar never drops a token that can reach sstar, ties
+// included.  The bound w <= E is loose only when w is large, i.e. only for
+// tokens whose e is a sizeable share of sstar; the many small tokens of a wide
+// nucleus pass only when u is within e/sstar of 1, where w and E agree.
+template <int G>
+__device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool scored, const RowModel& r, float c_log2e,
+                                            const uint32_t i0[G], const float x[G][4], const bool keep[G][4],
+                                            RaceAcc& acc, float& sstar)
+{
+    uint32_t km[G];
+    bool any = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        km[g] = (keep[g][0] ? 1u : 0u) | (keep[g][1] ? 2u : 0u) | (keep[g][2] ? 4u : 0u) | (keep[g][3] ? 8u : 0u);
+        any |= km[g] != 0;
+    }
+    if (!any) return;
+    float xm = INFINITY;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        acc.count += (uint32_t)__builtin_popcount(km[g]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xm = keep[g][j] ? fminf(xm, x[g][j]) : xm;
+    }
+    const uint32_t kmin = order_key(xm);
+    acc.minkey = kmin < acc.minkey ? kmin : acc.minkey;
+    if (!scored) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (!km[g]) continue;
+            const uint64_t pk = race_pack(1.0f, i0[g] + (uint32_t)__builtin_ctz(km[g]));
+            acc.best = pk > acc.best ? pk : acc.best;
+        }
+        return;
+    }
+    uint4 w4[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        w4[g] = philox4x32_10(make_uint4(i0[g] >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
+    // e_up / sstar = e_hat * k, k = (1 + 1e-4) / sstar; with no score yet
+    // (sstar = 0) every kept token passes.
+    const float k = sstar > 0.0f ? __builtin_amdgcn_rcpf(sstar) * (1.0001f / (1.0f - 1e-4f)) : INFINITY;
+    uint32_t pass = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float e_hat = __builtin_amdgcn_exp2f((x[g][j] - r.m) * c_log2e);
+            const float w = fmaf((float)(0xFFFFFFFFu - philox_word(w4[g], (uint32_t)j)), 0x1p-32f, 0x1p-33f);
+            pass |= (keep[g][j] && !(w > e_hat * k)) ? (1u << (4 * g + j)) : 0u;
+        }
+    while (pass) {
+        const uint32_t k = (uint32_t)__builtin_ctz(pass);
+        pass &= pass - 1u;
+        const uint32_t g = k >> 2, j = k & 3u;
+        uint32_t gi0 = i0[0];
+        float gx = x[0][0];
+        uint32_t word = w4[0].x;
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+            if ((uint32_t)q == g) {
+                gi0 = i0[q];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if ((uint32_t)jj == j) {
+                        gx = x[q][jj];
+                        word = philox_word(w4[q], (uint32_t)jj);
+                    }
+            }
+        const float s = exact_score(gx, r.m, r.T, r.invT, word);
+        const uint64_t pk = race_pack(s, gi0 + j);
+        acc.best = pk > acc.best ? pk : acc.best;
+        sstar = fmaxf(sstar, s);
+    }
+}
+
+// One group (the split-row kernel's register-resident chunk).
 __device__ __forceinline__ void race_group(const Params& p, int64_t b, bool scored, const RowModel& r, float c_log2e,
                                            uint32_t i0, const float x[4], const bool keep[4], RaceAcc& acc,
                                            float& sstar)
 {
-    const uint32_t km = (keep[0] ? 1u : 0u) | (keep[1] ? 2u : 0u) | (keep[2] ? 4u : 0u) | (keep[3] ? 8u : 0u);
-    if (!km) return;
-    acc.count += (uint32_t)__builtin_popcount(km);
-    float xm = INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xm = keep[j] ? fminf(xm, x[j]) : xm;
-    const uint32_t kmin = order_key(xm);
-    acc.minkey = kmin < acc.minkey ? kmin : acc.minkey;
-    if (!scored) {
-        const uint64_t pk = race_pack(1.0f, i0 + (uint32_t)__builtin_ctz(km));
-        acc.best = pk > acc.best ? pk : acc.best;
-        return;
-    }
-    const uint4 w4 = philox4x32_10(make_uint4(i0 >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
-    const float kz = (sstar > 0.0f ? __builtin_amdgcn_rcpf(sstar) : 3.0e38f) * (-1.4426950408889634f * 1.0001f);
-    uint32_t pass = 0;
+    const uint32_t i0s[1] = {i0};
+    float xs[1][4];
+    bool ks[1][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float e_hat = __builtin_amdgcn_exp2f((x[j] - r.m) * c_log2e);
-        const float theta = __builtin_amdgcn_exp2f(e_hat * kz);
-        const float u = fmaf((float)philox_word(w4, (uint32_t)j), 0x1p-32f, 0x1p-33f);
-        pass |= (keep[j] && u * 1.0001f >= theta) ? (1u << j) : 0u;
+        xs[0][j] = x[j];
+        ks[0][j] = keep[j];
     }
-    while (pass) {
-        const uint32_t j = (uint32_t)__builtin_ctz(pass);
-        pass &= pass - 1u;
-        const float s = exact_score(x[j], r.m, r.T, r.invT, philox_word(w4, j));
-        const uint64_t pk = race_pack(s, i0 + j);
-        acc.best = pk > acc.best ? pk : acc.best;
-        sstar = fmaxf(sstar, s);
-    }
+    race_groups<1>(p, b, scored, r, c_log2e, i0s, xs, ks, acc, sstar);
 }
 
 // Race one token by index (resolver candidates).

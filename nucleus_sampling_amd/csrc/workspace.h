@@ -86,9 +86,8 @@ static_assert(sizeof(RowPathState) == 256, "RowPathState layout");
 
 struct RowWork {
     RowPathState* st;     // [rows]
-    uint32_t* next;       // race_kernel's work counter (reset by row_kernel)
     uint2* cand;          // [rows][kCap]: key, index
-    int N;                // race chunks per row
+    int N;                // race_kernel: 2048-token items per row; probs_kernel: 8192-token chunks per row
 };
 
 __host__ __device__ inline int64_t padded_rows(int64_t B) { return (B + 7) / 8 * 8; }
@@ -100,14 +99,11 @@ struct WorkLayout {
     size_t ctl, slot_a, slot_h, slot_c, slot_r, cand, total;
 };
 
-// Row-path workspace: [rows] RowPathState, a 256-byte block holding the work
-// counter, then [rows][kCap] candidates.
-inline size_t row_work_bytes(int64_t B, size_t* next_off, size_t* cand_off)
+// Row-path workspace: [rows] RowPathState, then [rows][kCap] candidates.
+inline size_t row_work_bytes(int64_t B, size_t* cand_off)
 {
     const size_t rows = (size_t)padded_rows(B);
-    const size_t nx = align256(rows * sizeof(RowPathState));
-    const size_t off = nx + 256;
-    if (next_off) *next_off = nx;
+    const size_t off = align256(rows * sizeof(RowPathState));
     if (cand_off) *cand_off = off;
     return align256(off + rows * (size_t)kCap * 8);
 }
