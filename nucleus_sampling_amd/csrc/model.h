@@ -7,18 +7,27 @@
 //
 // Weights.  With m the row max and T > 0, token i weighs e_i = exp(-d_i),
 // d_i = (m - x_i)/T (the tempered softmax numerator, "What do temperature,
-// top-k and top-p each do ...", tempered-softmax equation).  d is cut into
-// kBins bins of width w (in d units) covering [0, D), D = min(32,
-// (m - min x)/T), so the bins adapt to the row's spread; the last bin also
-// takes every token with d >= D (each such token weighs < e^-32, so the
-// whole tail moves S by less than V e^-32 relative).  Bin j's upper edge
-// weighs exp(-j w).  Within its bin a token's weight relative to that edge,
-// exp(-f w) with f in [0, 1), is held as the integer
-//     fx = floor(2^31 * P(f)),   P = cubic Taylor polynomial of exp(-f w),
-// (w <= 1/32 keeps the truncation below 4e-8 relative; rows with wider bins
-// use exp2 instead), so a token weighs
-// exp(-j w) * fx * 2^-31 and each bin's weight is an exact integer sum:
-// associative, hence identical whatever order workgroups or lanes add in.
+// top-k and top-p each do ...", tempered-softmax equation).
+//
+// Bins sit on a fixed lattice of the logit that depends on T alone: cell
+// a(x) = floor(x s), s = 32/T rounded down to a 24-bit mantissa (so x s is
+// exact in double and the cell width in d units is w = 1/(sT), within 2^-23
+// of 1/32).  Because the lattice does not move with the row max, a kernel
+// can histogram a row in the same pass that finds its max.  With A = a(m),
+// a token's bin is j = min(A - a, kBins - 1): bin 0 holds the max, and the
+// last bin also takes every token more than ~32 below it (each weighs
+// < e^-31.9, so the whole tail moves S by less than V e^-31.9 relative).
+//
+// Weights are measured from the lattice point (A + 1)/s just above the max:
+// token x weighs exp(-(A + 1 - x s) w) = q^j exp(-f w), q = exp(-w),
+// f = a + 1 - x s in (0, 1].  That is e_i times one common factor in
+// [1, e^w), which every ratio the sampler takes (the top-p threshold, the
+// renormalised probabilities) cancels.  The in-bin factor is held as the
+// integer
+//     fx = floor(2^31 * P(f)),   P = cubic Taylor polynomial of exp(-f w)
+// (truncation below 5e-8 relative), so each bin's weight is an exact
+// integer sum: associative, hence identical whatever order workgroups or
+// lanes add in.
 //
 // Rules.  A token survives min-p iff x >= max + T ln(min_p) (rounded up to
 // fp32; p_i >= min_p * p_max is exactly that inequality).  The cut search
@@ -46,47 +55,78 @@ enum : uint32_t {
     kModeHist = 7,    // (provisional) needs the histogram to decide between the above
 };
 
+// The part of the model that depends on T alone: the lattice and the
+// in-bin polynomial.
+struct Lattice {
+    double s;   // cells per logit unit: cell of x = floor(x * s); 0 when T = +inf
+    double w;   // cell width in d units, 1/(s T); 0 when every token weighs the same
+    double q;   // exp(-w), the weight ratio of neighbouring bin edges
+    float c0, c1, c2, c3;  // 2^31 * Taylor coefficients of exp(-f w)
+};
+
 struct RowModel {
+    Lattice L;
+    double A;      // cell of the row max
     float m;       // row max
     float T;
     float invT;    // 0 for T = +inf
-    float s;       // bins per logit unit: t = (m - x) * s, bin = floor(t)
     float tmp;     // min-p threshold: survivor iff x >= tmp; -inf when off
-    float c0, c1, c2, c3;  // 2^31 * Taylor coefficients of exp(-f w)
-    double w;      // bin width in d units (0 when every token weighs the same)
-    double q;      // exp(-w), the weight ratio of neighbouring bin edges
-    float nwlog2;  // -w * log2(e), for rows whose bins are wider than 1/32 (wide != 0)
-    uint32_t wide; // 1 when w > 1/32 (only for a saturated s): in-bin weights use exp2
 };
 
-// Build the model of a row from its max, smallest finite logit and
-// parameters (T > 0).  Pure function of its arguments.
-__device__ __forceinline__ RowModel make_model(float m, float xmin, float T, float mp)
+// Lattice of temperature T > 0.  Pure function of T.
+__device__ __forceinline__ Lattice make_lattice(float T)
+{
+#pragma clang fp contract(off)
+    Lattice L;
+    const double sd = 32.0 / (double)T;  // finite for every fp32 T > 0; 0 at +inf
+    // Keep 24 significant bits (round toward zero): x * s is then exact.
+    L.s = __longlong_as_double(__double_as_longlong(sd) & ~((1ll << 29) - 1));
+    const double w = (T == INFINITY) ? 0.0 : 1.0 / (L.s * (double)T);
+    L.w = w;
+    L.q = exp(-w);
+    L.c0 = (float)kFx;
+    L.c1 = (float)(-w * kFx);
+    L.c2 = (float)(w * w * 0.5 * kFx);
+    L.c3 = (float)(-w * w * w * (1.0 / 6.0) * kFx);
+    return L;
+}
+
+// Cell of a finite logit and its offset f = cell + 1 - x s in (0, 1] (0 only
+// past 2^53, where cells are single logits far from any kept token).
+__device__ __forceinline__ double lattice_cell(const Lattice& L, float x, float& f)
+{
+#pragma clang fp contract(off)
+    const double pr = (double)x * L.s;  // exact
+    const double a = floor(pr);
+    f = (float)((a + 1.0) - pr);
+    return a;
+}
+
+// Integer weight of a token relative to its cell's upper edge, in (0, 2^31].
+__device__ __forceinline__ uint32_t cell_fx(const Lattice& L, float f)
+{
+#pragma clang fp contract(off)
+    return (uint32_t)fmaf(fmaf(fmaf(L.c3, f, L.c2), f, L.c1), f, L.c0);
+}
+
+// Bin of cell a in a row whose max is in cell A.
+__device__ __forceinline__ uint32_t bin_of_cell(double A, double a)
+{
+    const double jd = A - a;
+    return jd < (double)(kBins - 1) ? (uint32_t)jd : (uint32_t)(kBins - 1);
+}
+
+// Build the model of a row from its max and parameters (T > 0).  Pure
+// function of its arguments.
+__device__ __forceinline__ RowModel make_model(float m, float T, float mp)
 {
 #pragma clang fp contract(off)
     RowModel r;
+    r.L = make_lattice(T);
+    r.A = floor((double)m * r.L.s);
     r.m = m;
     r.T = T;
     r.invT = (T == INFINITY) ? 0.0f : 1.0f / T;
-    // Window span in logit units: min(range * (1 + 2^-10), 32 T); the small
-    // margin keeps the smallest logit strictly inside the last bin.
-    const float range = (m - xmin) * 1.0009765625f;
-    const float cap = 32.0f * T;
-    const float span = fminf(range, cap);
-    float s = (span > 0.0f) ? (float)kBins / span : 0.0f;
-    if (!(s <= 3.0e38f)) s = 3.0e38f;  // span underflowed: one wide bin 0
-    r.s = s;
-    // w <= 1/32 unless s saturated (a span below 3e-36 or T below 1e-37);
-    // such rows evaluate the in-bin weight with exp2 instead of the cubic.
-    const double w = (s > 0.0f && T != INFINITY) ? 1.0 / ((double)s * (double)T) : 0.0;
-    r.w = w;
-    r.wide = w > 1.0 / 32.0 ? 1u : 0u;
-    r.nwlog2 = (float)(-w * 1.4426950408889634);
-    r.q = exp(-w);
-    r.c0 = (float)kFx;
-    r.c1 = (float)(-w * kFx);
-    r.c2 = (float)(w * w * 0.5 * kFx);
-    r.c3 = (float)(-w * w * w * (1.0 / 6.0) * kFx);
     // min-p: e_i >= mp  <=>  x_i >= m + T ln(mp); at T = +inf every weight is 1.
     float tmp = -INFINITY;
     const float mpc = mp > 1.0f ? 1.0f : mp;
@@ -100,23 +140,29 @@ __device__ __forceinline__ RowModel make_model(float m, float xmin, float T, flo
     return r;
 }
 
-// The model with every field in scalar registers.
+// The lattice / model with every field in scalar registers.
+__device__ __forceinline__ Lattice uniform(const Lattice& a)
+{
+    Lattice L;
+    L.s = uniform(a.s);
+    L.w = uniform(a.w);
+    L.q = uniform(a.q);
+    L.c0 = uniform(a.c0);
+    L.c1 = uniform(a.c1);
+    L.c2 = uniform(a.c2);
+    L.c3 = uniform(a.c3);
+    return L;
+}
+
 __device__ __forceinline__ RowModel uniform(const RowModel& a)
 {
     RowModel r;
+    r.L = uniform(a.L);
+    r.A = uniform(a.A);
     r.m = uniform(a.m);
     r.T = uniform(a.T);
     r.invT = uniform(a.invT);
-    r.s = uniform(a.s);
     r.tmp = uniform(a.tmp);
-    r.c0 = uniform(a.c0);
-    r.c1 = uniform(a.c1);
-    r.c2 = uniform(a.c2);
-    r.c3 = uniform(a.c3);
-    r.w = uniform(a.w);
-    r.q = uniform(a.q);
-    r.nwlog2 = uniform(a.nwlog2);
-    r.wide = uniform(a.wide);
     return r;
 }
 
@@ -125,27 +171,32 @@ __device__ __forceinline__ bool survives(const RowModel& r, float x)
     return x > -INFINITY && x >= r.tmp;
 }
 
-// Bin position of a finite logit: t >= 0, bin = min(floor(t), kBins - 1).
-__device__ __forceinline__ float bin_pos(const RowModel& r, float x)
+// Bin and in-bin integer weight of a finite logit.
+struct Binned {
+    uint32_t j, fx;
+};
+
+__device__ __forceinline__ Binned bin_token(const RowModel& r, float x)
 {
-#pragma clang fp contract(off)
-    return (r.m - x) * r.s;
+    float f;
+    const double a = lattice_cell(r.L, x, f);
+    Binned o;
+    o.j = bin_of_cell(r.A, a);
+    o.fx = cell_fx(r.L, f);
+    return o;
 }
 
-__device__ __forceinline__ uint32_t bin_of(float t)
+__device__ __forceinline__ uint32_t bin_of(const RowModel& r, float x)
 {
-    const uint32_t j = (uint32_t)t;  // saturates for huge t
-    return j < (uint32_t)(kBins - 1) ? j : (uint32_t)(kBins - 1);
+    float f;
+    return bin_of_cell(r.A, lattice_cell(r.L, x, f));
 }
 
-// Integer weight of a token relative to its bin's upper edge, in (0, 2^31].
-__device__ __forceinline__ uint32_t bin_fx(const RowModel& r, float t)
+__device__ __forceinline__ uint32_t bin_fx(const RowModel& r, float x)
 {
-#pragma clang fp contract(off)
-    const float f = __builtin_amdgcn_fractf(t);
-    if (r.wide) return (uint32_t)(__builtin_amdgcn_exp2f(f * r.nwlog2) * (float)kFx);
-    const float p = fmaf(fmaf(fmaf(r.c3, f, r.c2), f, r.c1), f, r.c0);
-    return (uint32_t)p;
+    float f;
+    lattice_cell(r.L, x, f);
+    return cell_fx(r.L, f);
 }
 
 // Weight of bin j's upper edge, exp(-w)^j by binary powering (a fixed
@@ -154,7 +205,7 @@ __device__ __forceinline__ uint32_t bin_fx(const RowModel& r, float t)
 __device__ __forceinline__ double edge_weight(const RowModel& r, int j)
 {
 #pragma clang fp contract(off)
-    double acc = 1.0, sq = r.q;
+    double acc = 1.0, sq = r.L.q;
     for (int k = j; k; k >>= 1) {
         if (k & 1) acc *= sq;
         sq *= sq;
@@ -164,10 +215,10 @@ __device__ __forceinline__ double edge_weight(const RowModel& r, int j)
 
 // Weight of a token at the common 2^-40 scale used when several bins meet
 // (the top-k mode): floor(exp(-j w) * fx * 2^9).
-__device__ __forceinline__ uint64_t fixed40(const RowModel& r, uint32_t j, uint32_t fx)
+__device__ __forceinline__ uint64_t fixed40(const RowModel& r, const Binned& t)
 {
 #pragma clang fp contract(off)
-    return (uint64_t)(edge_weight(r, (int)j) * (double)fx * 512.0);
+    return (uint64_t)(edge_weight(r, (int)t.j) * (double)t.fx * 512.0);
 }
 
 // Result of reading a full histogram.

@@ -3,8 +3,11 @@
 //
 // row_kernel: one 1024-thread workgroup per row streams the row from global
 //   memory once per pass, eight 16-byte loads in flight per thread:
-//     1  row max, smallest finite logit, error flag  -> row mode, model
-//     2  bin histogram of the survivors (LDS)          -> crossing bin (decide)
+//     1  row max, error flag and, since bins sit on a lattice that does not
+//        depend on the max, the bin histogram (LDS)    -> row mode, model,
+//                                                         crossing bin (decide)
+//     2  only for min-p rows (whose survivors depend on the max), or when
+//        the histogram window missed the max: the histogram again
 //   then either finishes the row itself (one more pass racing the surely kept
 //   tokens and gathering the crossing bin's tokens into LDS, the resolver,
 //   and an optional probability pass), or publishes the row's state for
@@ -30,7 +33,10 @@ namespace nucleus {
 
 constexpr int kRowThreads = 1024;  // 16 waves: one workgroup per CU
 constexpr int kRowUnroll = 8;      // 4-token groups per thread whose loads are in flight together
-constexpr int kRowCand = 4096;     // crossing-bin candidates held in LDS
+constexpr int kRowCand = 6144;     // crossing-bin candidates held in LDS
+constexpr int kWaveCand = kRowCand / (kRowThreads / kWave);  // each wave's segment of them
+constexpr int kWin = 4096;         // cells of the fused pass's LDS histogram window
+constexpr int kWinHead = kWin - kBins;  // cells the window reaches above the provisional max
 constexpr int kRaceQueue = 256;    // per-wave ring of 4-token groups waiting for the race
 constexpr int kDrain = 2 * kWave;  // groups raced per drain: two per lane
 constexpr int kRaceThreads = 256;  // race_kernel / probs_kernel workgroups
@@ -139,14 +145,16 @@ __device__ __forceinline__ void mask_whole(uint32_t g0, uint32_t t, uint32_t nfu
 
 // Calls f(i0, x[4]) for every 4-token group of the row, the same number of
 // times in every lane (so f may use wave-wide operations); a call for no
-// token of the row passes -inf values and an i0 past V.
+// token of the row passes -inf values and an i0 past V.  Before the first
+// call, every thread calls first(mx) once with the max of the first tokens
+// it loaded (-inf if none), so first may use workgroup barriers.
 //
 // Aligned rows are software-pipelined: two register buffers of
 // kRowUnroll / 2 groups per thread, the next one's loads in flight while f
 // runs on the current one.  The row's partial last group (V not a multiple
 // of 4) takes one more call after the loop, loaded token by token.
-template <int DT, bool NTL, int NT, class F>
-__device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&& f)
+template <int DT, bool NTL, int NT, class F, class First>
+__device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&& f, First&& first)
 {
     const uint32_t V = (uint32_t)p.V;
     const uint32_t ng = (V + 3) >> 2, nfull = V >> 2;
@@ -160,6 +168,14 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
         for (uint32_t g0 = 0; g0 < nfull; g0 += 2 * step) {
             issue_whole<DT, NTL, NT, H>(rowp, g0 + step, t, nfull, xb);
             mask_whole<NT, H>(g0, t, nfull, xa);
+            if (g0 == 0) {  // uniform
+                float mx = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < H; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, xa[u][j]);
+                first(mx);
+            }
 #pragma unroll
             for (int u = 0; u < H; ++u) {
                 const uint32_t g = g0 + (uint32_t)u * NT + t;
@@ -187,6 +203,11 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
             f(own ? nfull << 2 : past, x);
         }
     } else {  // unaligned rows: token by token
+        {
+            float x[4];
+            load4<DT>(rowp, (int64_t)t << 2, V, 0, x);
+            first(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        }
         for (uint32_t g0 = 0; g0 < ng; g0 += NT) {
             const uint32_t g = g0 + t;
             float x[4];
@@ -196,28 +217,31 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
     }
 }
 
-// Appends (key, idx) for the lanes with pred to an LDS list: one LDS atomic
-// per wave, positions from the lane's rank among the appending lanes.
-// Appends past `cap` are counted but dropped.
-__device__ __forceinline__ void lds_append(uint32_t* counter, u32x2v* list, uint32_t cap, bool pred, uint32_t key,
-                                           uint32_t idx)
+template <int DT, bool NTL, int NT, class F>
+__device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&& f)
+{
+    stream_row<DT, NTL, NT>(p, rowp, f, [](float) {});
+}
+
+// Appends (key, idx) for the lanes with pred to the wave's own segment of an
+// LDS list (kWaveCand entries); n, the same in every lane, counts the
+// wave's appends, those past the segment (dropped) included.  No atomics:
+// positions come from the lanes' ranks.
+__device__ __forceinline__ void wave_append(u32x2v* seg, uint32_t& n, bool pred, uint32_t key, uint32_t idx)
 {
     const uint64_t mask = __ballot(pred);
     if (mask == 0) return;
-    const int leader = __builtin_ctzll(mask);
-    const uint32_t lo = (uint32_t)mask, hi = (uint32_t)(mask >> 32);
-    uint32_t base = 0;
-    if ((int)__lane_id() == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-    base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
     if (pred) {
-        const uint32_t off = base + __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-        if (off < cap) {
+        const uint32_t off =
+            n + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (off < (uint32_t)kWaveCand) {
             u32x2v e;
             e.x = key;
             e.y = idx;
-            list[off] = e;
+            seg[off] = e;
         }
     }
+    n += (uint32_t)__popcll(mask);
 }
 
 // Per-wave ring of 4-token groups holding at least one kept token: the race
@@ -272,6 +296,36 @@ __device__ __forceinline__ void wq_push(RaceQueue& rq, uint32_t& qh, uint32_t& q
     if (qn >= (uint32_t)kDrain) wq_drain(rq, qh, qn, lane, kDrain, race);
 }
 
+// With no score to screen against yet (a wave's first step), every token
+// would pass the screen and be scored one at a time.  Instead every lane
+// scores its first kept token (one exact score per lane, all lanes at once)
+// and the wave's best of those becomes the bound: a score some token reaches,
+// so the screen still keeps every possible winner.
+__device__ __forceinline__ void seed_bound(const Params& p, int64_t b, const RowModel& r,
+                                                     const uint32_t i0[2], const float xs[2][4],
+                                                     const bool keep[2][4], RaceAcc& acc, float& sstar)
+{
+    int pick = -1;
+    float x = 0.0f;
+#pragma unroll
+    for (int k = 7; k >= 0; --k) {
+        const bool kp = keep[k >> 2][k & 3];
+        pick = kp ? k : pick;
+        x = kp ? xs[k >> 2][k & 3] : x;
+    }
+    float s = 0.0f;
+    if (pick >= 0) {
+        const int h = pick >> 2, j = pick & 3;
+        const uint32_t gi0 = h ? i0[1] : i0[0];
+        const uint4 w4 =
+            philox4x32_10(make_uint4(gi0 >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
+        s = exact_score(x, r.m, r.T, r.invT, philox_word(w4, (uint32_t)j));
+        const uint64_t pk = race_pack(s, gi0 + (uint32_t)j);
+        acc.best = pk > acc.best ? pk : acc.best;
+    }
+    sstar = fmaxf(sstar, wave_reduce(s, MaxF()));
+}
+
 // One race step for two queued groups: screen against the best score any
 // wave of the workgroup has reached (a score some token achieved, so the
 // screen never drops a possible winner), race, and publish the wave's best.
@@ -286,6 +340,7 @@ __device__ __forceinline__ void race_queued(const Params& p, int64_t b, bool sco
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 4; ++j) keep[h][j] = active[h] && xs[h][j] >= keep_lo;
+    if (scored && __ballot(sstar == 0.0f)) seed_bound(p, b, r, i0, xs, keep, acc, sstar);
     race_groups<2>(p, b, scored, r, c_log2e, i0, xs, keep, acc, sstar);
     // Publish only when some lane improved on the shared best (after the first
     // few groups that is rare, and the wave reduction is skipped).
@@ -322,46 +377,45 @@ __device__ __forceinline__ void global_append(uint32_t* counter, __amdgpu_buffer
 
 struct RowShared {
     union {
-        struct {
-            uint64_t hm[kBins];
-            uint32_t hc[kBins];
+        struct {  // histogram: a window of lattice cells (bins from decide on)
+            uint64_t hm[kWin];
+            uint32_t hc[kWin];
         } h;
-        float factor[kBins];
+        struct {  // race pass
+            u32x2v cand[kRowCand];
+            RaceQueue rq[kRowThreads / kWave];
+        } r;
+        float factor[kBins];  // probability pass
     } u;
-    u32x2v cand[kRowCand];
-    RaceQueue rq[kRowThreads / kWave];
     ResolveShared rs;
     double red[64];
-    float redf[kMaxWaves], redf2[kMaxWaves];
+    float redf[kMaxWaves];
     int redi[kMaxWaves];
-    uint32_t cand_n;
+    uint32_t wcand[kMaxWaves];  // candidates each wave found (past its segment too)
+    uint32_t wpre[kMaxWaves];   // candidates of the waves before
     uint32_t sstar_bits;  // best exact race score found so far in the workgroup (bits of a float >= 0)
 };
 
-// Row max, smallest finite logit and error flag over the workgroup: wave
-// reductions, then one exchange through LDS.
+// Row max and error flag over the workgroup: wave reductions, then one
+// exchange through LDS.
 template <int NT>
-__device__ __forceinline__ void block_extremes(float& mx, float& mn, int& bad, float* rf, float* rf2, int* ri)
+__device__ __forceinline__ void block_extremes(float& mx, int& bad, float* rf, int* ri)
 {
     constexpr int W = NT / kWave;
     mx = wave_reduce(mx, MaxF());
-    mn = wave_reduce(mn, MinF());
     bad = wave_reduce(bad, OrI32());
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     __syncthreads();
     if (lane == 0) {
         rf[w] = mx;
-        rf2[w] = mn;
         ri[w] = bad;
     }
     __syncthreads();
     mx = rf[0];
-    mn = rf2[0];
     bad = ri[0];
 #pragma unroll
     for (int i = 1; i < W; ++i) {
         mx = fmaxf(mx, rf[i]);
-        mn = fminf(mn, rf2[i]);
         bad |= ri[i];
     }
 }
@@ -391,7 +445,6 @@ __device__ __forceinline__ void publish_row(RowPathState* ps, const RowState& st
     *(RowModel*)ps->model = model;
     ps->mode = st.mode;
     ps->m = st.m;
-    ps->xmin = st.xmin;
     ps->cbin = st.cbin;
     ps->tc = st.tc;
     ps->a_above = st.a_above;
@@ -418,67 +471,136 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     const void* rowp = (const char*)p.logits + b * p.stride * esz;
     const bool want_probs = p.out_probs != nullptr;
 
-    // ---- pass 1: row max, smallest finite logit, NaN / +inf
-    float lmax = -INFINITY, lmin = INFINITY;
-    int bad = 0;
-    stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t, const float* xs) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float v = xs[j];
-            bad |= (v != v) | (v == INFINITY);
-            lmax = fmaxf(lmax, v);
-            lmin = (v > -INFINITY) ? fminf(lmin, v) : lmin;
-        }
-    });
-    block_extremes<kRowThreads>(lmax, lmin, bad, sh.redf, sh.redf2, sh.redi);
+    // ---- pass 1: row max, NaN / +inf; for rows whose
+    // need of a histogram the parameters alone decide (no min-p), also the
+    // histogram, over a window of lattice cells placed from the max of the
+    // first tokens loaded (the lattice does not depend on the max).
     const RowParams rp = row_params(p, b);
+    const bool counts = rp.K > 0;
+    const bool fused = hist_before_max(rp, want_probs);
+    const Lattice lat = uniform(make_lattice(fused ? rp.T : 1.0f));
+    if (fused)
+        for (int i = t; i < kWin; i += kRowThreads) {
+            sh.u.h.hm[i] = 0;
+            sh.u.h.hc[i] = 0;
+        }
+    float lmax = -INFINITY;
+    int bad = 0;
+    bool win = false;     // uniform: the window is placed
+    double base = 0.0;    // uniform: cell held by window slot 0 (slot k holds cell base - k)
+    uint64_t tail_w = 0;  // cells below the window: all in the last bin
+    uint32_t tail_c = 0;
+    stream_row<DT, false, kRowThreads>(
+        p, rowp,
+        [&](uint32_t, const float* xs) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = xs[j];
+                bad |= !(v < INFINITY);  // NaN or +inf
+                lmax = fmaxf(lmax, v);
+            }
+            if (win) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // Branch-free but for the LDS atomics.  NaN and -inf
+                    // are no tokens; k < 0 lies above the window (the row is
+                    // then redone).
+                    const float v = xs[j];
+                    const bool fin = v > -INFINITY;
+                    float f;
+                    const double k = base - lattice_cell(lat, v, f);
+                    const uint32_t fx = cell_fx(lat, f);
+                    const bool tail = fin && k >= (double)kWin;
+                    const bool in = fin && k >= 0.0 && k < (double)kWin;
+                    tail_w += tail ? fx : 0u;
+                    tail_c += tail ? 1u : 0u;
+                    if (in) {
+                        const int slot = (int)k;
+                        atomicAdd((unsigned long long*)&sh.u.h.hm[slot], (unsigned long long)fx);
+                        if (counts) atomicAdd(&sh.u.h.hc[slot], 1u);
+                    }
+                }
+            }
+        },
+        [&](float mx) {
+            if (!fused) return;
+            const float m1 = block_reduce<kRowThreads>(mx, MaxF(), sh.redf);
+            base = uniform(floor((double)m1 * lat.s) + (double)kWinHead);
+            // Cells are exact integers in double below 2^53; a provisional
+            // max of -inf or +inf leaves the window unplaced.
+            win = m1 > -INFINITY && fabs(base) < 0x1p50;
+        });
+    block_extremes<kRowThreads>(lmax, bad, sh.redf, sh.redi);
     RowState st;
     st.mode = uniform(first_mode(bad != 0, lmax, rp.T, rp.P, rp.MP, rp.K, want_probs));
     st.m = uniform(lmax);
-    st.xmin = uniform(lmin);
     st.cbin = 0;
     st.tc = 0;
     st.a_above = st.s_total = st.s_keep = 0.0;
     RowModel model = {};
-    if (st.mode >= kModeTop) model = uniform(make_model(st.m, st.xmin, rp.T, rp.MP));
+    if (st.mode >= kModeTop) model = uniform(make_model(st.m, rp.T, rp.MP));
 
-    // ---- pass 2: bin histogram of the survivors
     if (st.mode == kModeHist) {
-        const bool counts = rp.K > 0;
-        for (int i = t; i < kBins; i += kRowThreads) {
-            sh.u.h.hm[i] = 0;
-            sh.u.h.hc[i] = 0;
-        }
-        __syncthreads();
-        // The last bin takes the whole tail of the row: it is summed in
-        // registers and added once per wave instead of by LDS atomics.
-        uint64_t tail_w = 0;
-        uint32_t tail_c = 0;
-        stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t, const float* xs) {
+        const int lane = t & (kWave - 1);
+        // Bin j of the row is cell A - j: window slot off + j, where
+        // off = base - A lies in [0, kWinHead] unless some token rose above
+        // the window.  Every slot past off + kBins - 1 and the tail below the
+        // window fold into the last bin.
+        const double offd = base - model.A;
+        uint64_t* H = sh.u.h.hm;
+        uint32_t* C = sh.u.h.hc;
+        if (win && offd >= 0.0) {
+            const uint32_t off = (uint32_t)offd;
+            uint64_t fw = 0;
+            uint32_t fc = 0;
+            for (uint32_t k = off + kBins + t; k < (uint32_t)kWin; k += kRowThreads) {
+                fw += H[k];
+                fc += C[k];
+            }
+            fw = wave_reduce(fw + tail_w, SumU64());
+            fc = wave_reduce(fc + tail_c, SumU32());
+            if (lane == 0 && fc) {
+                atomicAdd((unsigned long long*)&H[off + kBins - 1], (unsigned long long)fw);
+                if (counts) atomicAdd(&C[off + kBins - 1], fc);
+            }
+            H += off;
+            C += off;
+        } else {
+            // ---- pass 2 (min-p rows, or the window missed the max): the
+            // histogram of the survivors, bins straight from the model.
+            for (int i = t; i < kBins; i += kRowThreads) {
+                H[i] = 0;
+                C[i] = 0;
+            }
+            __syncthreads();
+            // The last bin takes the whole tail of the row: it is summed in
+            // registers and added once per wave instead of by LDS atomics.
+            tail_w = 0;
+            tail_c = 0;
+            stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t, const float* xs) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (survives(model, xs[j])) {
-                    const float tp = bin_pos(model, xs[j]);
-                    const uint32_t jb = bin_of(tp);
-                    const uint32_t fx = bin_fx(model, tp);
-                    if (jb == (uint32_t)(kBins - 1)) {
-                        tail_w += fx;
-                        tail_c += 1;
-                    } else {
-                        atomicAdd((unsigned long long*)&sh.u.h.hm[jb], (unsigned long long)fx);
-                        if (counts) atomicAdd(&sh.u.h.hc[jb], 1u);
+                for (int j = 0; j < 4; ++j) {
+                    if (survives(model, xs[j])) {
+                        const Binned bt = bin_token(model, xs[j]);
+                        if (bt.j == (uint32_t)(kBins - 1)) {
+                            tail_w += bt.fx;
+                            tail_c += 1;
+                        } else {
+                            atomicAdd((unsigned long long*)&H[bt.j], (unsigned long long)bt.fx);
+                            if (counts) atomicAdd(&C[bt.j], 1u);
+                        }
                     }
                 }
+            });
+            tail_w = wave_reduce(tail_w, SumU64());
+            tail_c = wave_reduce(tail_c, SumU32());
+            if (lane == 0 && tail_c) {
+                atomicAdd((unsigned long long*)&H[kBins - 1], (unsigned long long)tail_w);
+                if (counts) atomicAdd(&C[kBins - 1], tail_c);
             }
-        });
-        tail_w = wave_reduce(tail_w, SumU64());
-        tail_c = wave_reduce(tail_c, SumU32());
-        if ((t & (kWave - 1)) == 0 && tail_c) {
-            atomicAdd((unsigned long long*)&sh.u.h.hm[kBins - 1], (unsigned long long)tail_w);
-            if (counts) atomicAdd(&sh.u.h.hc[kBins - 1], tail_c);
         }
         __syncthreads();
-        const Decision d = decide(model, sh.u.h.hm, counts ? sh.u.h.hc : nullptr, rp.K, rp.P, sh.red);
+        const Decision d = decide(model, H, counts ? C : nullptr, rp.K, rp.P, sh.red);
         st.mode = uniform(d.mode);
         st.cbin = uniform(d.cbin);
         st.tc = uniform(d.tc);
@@ -497,17 +619,16 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     const bool scored = st.mode != kModeGreedy;
     const bool has_cand = cand_lo < keep_lo;
     const float c_log2e = model.invT * 1.4426950408889634f;
-    if (t == 0) {
-        sh.cand_n = 0;
-        sh.sstar_bits = 0;
-    }
+    if (t == 0) sh.sstar_bits = 0;
     __syncthreads();
     RaceAcc acc;
     acc.init();
     float sstar = 0.0f;
-    RaceQueue& rq = sh.rq[t / kWave];
+    RaceQueue& rq = sh.u.r.rq[t / kWave];
     const uint32_t lane = (uint32_t)t & (kWave - 1);
     uint32_t qh = 0, qn = 0;  // ring head and fill, the same in every lane of the wave
+    u32x2v* const seg = sh.u.r.cand + (t / kWave) * kWaveCand;
+    uint32_t wn = 0;          // the wave's candidates, the same in every lane
     auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
         race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits);
     };
@@ -517,24 +638,43 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
         if (has_cand) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                lds_append(&sh.cand_n, sh.cand, kRowCand, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]),
-                           i0 + j);
+                wave_append(seg, wn, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]), i0 + j);
         }
     });
     if (qn) wq_drain(rq, qh, qn, lane, qn, race);
-    acc = block_race<kRowThreads>(acc, sh.rs);
-    const uint32_t n = uniform(sh.cand_n);
-    if (n <= (uint32_t)kRowCand) {
-        resolve_row<kRowThreads>(p, b, model, rp, st, acc,
+    if (lane == 0) sh.wcand[t / kWave] = wn;
+    acc = block_race<kRowThreads>(acc, sh.rs);  // (its barriers publish wcand)
+    uint32_t most = 0, n = 0;
+#pragma unroll
+    for (int w = 0; w < kRowThreads / kWave; ++w) {
+        const uint32_t c = sh.wcand[w];
+        if (t == w) sh.wpre[w] = n;
+        most = max(most, c);
+        n += c;
+    }
+    most = uniform(most);
+    n = uniform(n);
+    if (most <= (uint32_t)kWaveCand) {
+        // Pack the waves' segments into one list, in the race queues' space
+        // (the race is over): every later visit then reads n entries.
+        u32x2v* const list = (u32x2v*)sh.u.r.rq;
+        static_assert(sizeof(sh.u.r.rq) >= sizeof(u32x2v) * kRowCand, "packed list fits the race queues");
+        __syncthreads();
+        for (uint32_t i = t; i < (uint32_t)kRowCand; i += kRowThreads) {
+            const uint32_t w = i / kWaveCand, k = i - w * kWaveCand;
+            if (k < sh.wcand[w]) list[sh.wpre[w] + k] = sh.u.r.cand[i];
+        }
+        __syncthreads();
+        resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
                                  [&](auto&& fn) {
                                      for (uint32_t i = t; i < n; i += kRowThreads) {
-                                         const u32x2v c = sh.cand[i];
+                                         const u32x2v c = list[i];
                                          fn(c.x, c.y);
                                      }
                                  },
                                  sh.rs);
-    } else {  // more candidates than LDS holds: visit the row in global memory
-        resolve_row<kRowThreads>(p, b, model, rp, st, acc,
+    } else {  // more candidates than a wave's segment holds: visit the row in global memory
+        resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
                                  [&](auto&& fn) {
                                      stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
 #pragma unroll
@@ -582,7 +722,6 @@ __device__ __forceinline__ RowState published_state(const RowPathState* ps)
     RowState st;
     st.mode = uniform(ps->mode);
     st.m = uniform(ps->m);
-    st.xmin = uniform(ps->xmin);
     st.cbin = uniform(ps->cbin);
     st.tc = uniform(ps->tc);
     st.a_above = uniform(ps->a_above);
@@ -690,6 +829,9 @@ __global__ __launch_bounds__(kRaceThreads) void resolve_kernel(Params p, RowWork
     const RowModel model = uniform(*(const RowModel*)ps->model);
     const RowParams rp = row_params(p, b);
     const float cand_lo = uniform(ps->cand_lo), keep_lo = uniform(ps->keep_lo);
+    Classes cl;
+    cl.keep_lo = keep_lo;
+    cl.cand_lo = cand_lo;
     RaceAcc part;
     part.best = uniform(ps->best);
     part.count = uniform(ps->count);
@@ -707,7 +849,7 @@ __global__ __launch_bounds__(kRaceThreads) void resolve_kernel(Params p, RowWork
             sh.cand[i] = e;
         }
         __syncthreads();
-        resolve_row<kRaceThreads>(p, b, model, rp, st, part,
+        resolve_row<kRaceThreads>(p, b, model, rp, st, part, cl,
                                   [&](auto&& fn) {
                                       for (uint32_t i = t; i < n; i += kRaceThreads) {
                                           const u32x2v c = sh.cand[i];
@@ -716,7 +858,7 @@ __global__ __launch_bounds__(kRaceThreads) void resolve_kernel(Params p, RowWork
                                   },
                                   sh.rs);
     } else if (n <= (uint32_t)kCap) {
-        resolve_row<kRaceThreads>(p, b, model, rp, st, part,
+        resolve_row<kRaceThreads>(p, b, model, rp, st, part, cl,
                                   [&](auto&& fn) {
                                       for (uint32_t i = t; i < n; i += kRaceThreads) {
                                           const uint2 c = list[i];
@@ -725,7 +867,7 @@ __global__ __launch_bounds__(kRaceThreads) void resolve_kernel(Params p, RowWork
                                   },
                                   sh.rs);
     } else {  // the crossing bin overflowed the list: visit the row in global memory
-        resolve_row<kRaceThreads>(p, b, model, rp, st, part,
+        resolve_row<kRaceThreads>(p, b, model, rp, st, part, cl,
                                   [&](auto&& fn) {
                                       stream_row<DT, false, kRaceThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
 #pragma unroll

@@ -6,7 +6,7 @@
 //   keeps it there for every phase.  The K workgroups of a row meet at
 //   per-row barriers in the workspace; the last to arrive at each barrier
 //   merges what the others published and releases them:
-//     A  row max, smallest finite logit, error flag       -> row mode
+//     A  row max, error flag                              -> row mode
 //     B  bin histograms of the survivors (model.h)         -> crossing bin
 //     C  race partials over the tokens surely kept, and the compacted tokens
 //        of the crossing bin -> the last arriver resolves the exact cut
@@ -265,7 +265,7 @@ __device__ __forceinline__ bool barrier_wait(RowCtl* c, BarrierShared& bs)
 // ---------------------------------------------------------------------------
 struct RowState {
     uint32_t mode;
-    float m, xmin;
+    float m;
     uint32_t cbin;
     uint64_t tc;
     double a_above, s_total, s_keep;
@@ -294,6 +294,16 @@ __device__ __forceinline__ RowParams row_params(const Params& p, int64_t b)
     r.MP = p.min_p ? p.min_p[b] : 0.0f;
     r.K = p.top_k ? p.top_k[b] : 0;
     return r;
+}
+
+// Rows whose histogram the parameters alone call for, before the max is
+// known: a histogram is needed (first_mode would say kModeHist for any finite
+// max) and min-p is off, so every finite token survives whatever the max.
+__device__ __forceinline__ bool hist_before_max(const RowParams& rp, bool want_probs)
+{
+    if (!(rp.T > 0.0f) || rp.P != rp.P || rp.MP != rp.MP) return false;
+    if (rp.MP > 0.0f && rp.T != INFINITY) return false;
+    return rp.K > 0 || (rp.P > 0.0f && rp.P < 1.0f) || (rp.P >= 1.0f && want_probs);
 }
 
 struct RaceAcc {
@@ -436,15 +446,15 @@ __device__ __forceinline__ void race_one(const Params& p, int64_t b, const RowMo
 // The smallest finite logit whose bin is < c (c >= 1).  Bins fall as logits
 // rise (the row max is in bin 0), so over order keys this is the boundary
 // between keys with bin >= c and keys with bin < c.  The search starts from
-// the estimate m - c/s, gallops in key steps until it brackets the boundary
+// the estimate (A - c + 1)/s (the lower edge of bin c - 1), gallops in key steps until it brackets the boundary
 // and bisects the bracket: the same answer as a bisection over all keys, in a
 // few evaluations.
 __device__ __forceinline__ float lowest_in_bins_below(const RowModel& r, uint32_t c)
 {
     const uint32_t kmin = order_key(-3.4028234663852886e38f), kmax = order_key(r.m);
-    auto below = [&](uint32_t key) { return bin_of(bin_pos(r, key_value(key))) < c; };
-    if (below(kmin)) return key_value(kmin);
-    const float est = r.m - (float)c / r.s;
+    auto below = [&](uint32_t key) { return bin_of(r, key_value(key)) < c; };
+    if (below(kmin)) return key_value(kmin);  // also every row with s = 0 (T = +inf)
+    const float est = (float)((r.A - (double)c + 1.0) / r.L.s);
     uint32_t k = order_key(est > -3.4028234663852886e38f ? est : -3.4028234663852886e38f);
     k = k < kmin ? kmin : (k > kmax ? kmax : k);
     uint32_t lo, hi;  // below(lo) is false, below(hi) is true
@@ -536,13 +546,17 @@ __device__ __forceinline__ RaceAcc block_race(RaceAcc a, ResolveShared& rs)
 }
 
 // The last step of a row: given the merged race partial of the surely kept
-// tokens (`part`) and a way to visit the candidates (`visit(fn(key, idx))`),
+// tokens (`part`), the row's classes and a way to visit the candidates
+// (`visit(fn(key, idx))`, every token with cl.cand_lo <= x < cl.keep_lo),
 // find the exact cut, race the kept candidates and fill st.token / count /
 // cut_key / s_keep.  All NT threads; uniform control flow.
 template <int NT, class Visit>
 __device__ __forceinline__ void resolve_row(const Params& p, int64_t b, const RowModel& r, const RowParams& rp, RowState& st,
-                            RaceAcc part, Visit visit, ResolveShared& rs)
+                            RaceAcc part, const Classes& cl, Visit visit, ResolveShared& rs)
 {
+    // Keys every candidate lies between (they bound the radix search).
+    const uint32_t key_lo = order_key(cl.cand_lo);
+    const uint32_t key_hi = cl.keep_lo < INFINITY ? order_key(cl.keep_lo) - 1u : order_key(st.m);
     if (st.mode == kModeError) {
         st.token = 0xFFFFFFFFu;
         st.count = 0;
@@ -559,16 +573,17 @@ __device__ __forceinline__ void resolve_row(const Params& p, int64_t b, const Ro
     }
     RaceAcc acc = part;
     if (st.mode == kModeTop) {
-        st.s_keep = (double)acc.count;  // every top-level token weighs exactly 1
+        // Every top-level token weighs what the max does.
+        st.s_keep = (double)acc.count * ((double)bin_fx(r, st.m) * (1.0 / kFx));
     } else if (st.mode == kModeAll) {
         st.s_keep = st.s_total;
     } else if (st.mode == kModeP) {
         const uint64_t tc = st.tc;
         const SelectResult sr = select_level<NT>(
             [&](auto&& fn) {
-                visit([&](uint32_t key, uint32_t) { fn(key, (uint64_t)bin_fx(r, bin_pos(r, key_value(key)))); });
+                visit([&](uint32_t key, uint32_t) { fn(key, (uint64_t)bin_fx(r, key_value(key))); });
             },
-            [&](uint64_t) { return tc; }, rs.sel);
+            [&](uint64_t) { return tc; }, rs.sel, key_lo, key_hi);
         const uint32_t cut = sr.level;
         RaceAcc c;
         c.init();
@@ -584,7 +599,7 @@ __device__ __forceinline__ void resolve_row(const Params& p, int64_t b, const Ro
         const uint64_t kk = (uint64_t)rp.K;
         const SelectResult tk = select_level<NT>(
             [&](auto&& fn) { visit([&](uint32_t key, uint32_t) { fn(key, (uint64_t)1); }); },
-            [&](uint64_t) { return kk; }, rs.sel);
+            [&](uint64_t) { return kk; }, rs.sel, key_lo, key_hi);
         uint32_t cut = tk.level;
         if (rp.P <= 0.0f) {
             cut = order_key(st.m);
@@ -594,13 +609,10 @@ __device__ __forceinline__ void resolve_row(const Params& p, int64_t b, const Ro
             const SelectResult sp = select_level<NT>(
                 [&](auto&& fn) {
                     visit([&](uint32_t key, uint32_t) {
-                        if (key >= vk) {
-                            const float t = bin_pos(r, key_value(key));
-                            fn(key, fixed40(r, bin_of(t), bin_fx(r, t)));
-                        }
+                        if (key >= vk) fn(key, fixed40(r, bin_token(r, key_value(key))));
                     });
                 },
-                [&](uint64_t total) { return ceil_p_times(P, total); }, rs.sel);
+                [&](uint64_t total) { return ceil_p_times(P, total); }, rs.sel, vk, key_hi);
             cut = sp.level;
         }
         RaceAcc c;
@@ -609,8 +621,7 @@ __device__ __forceinline__ void resolve_row(const Params& p, int64_t b, const Ro
         visit([&](uint32_t key, uint32_t idx) {
             if (key >= cut) {
                 race_one(p, b, r, key, idx, c);
-                const float t = bin_pos(r, key_value(key));
-                kept_w += fixed40(r, bin_of(t), bin_fx(r, t));
+                kept_w += fixed40(r, bin_token(r, key_value(key)));
             }
         });
         c = block_race<NT>(c, rs);
@@ -652,8 +663,8 @@ __device__ __forceinline__ float prob_of(uint32_t mode, const RowModel& r, const
     if (mode == kModeError) return 0.0f;
     if (mode == kModeGreedy) return (uint32_t)i == st.token ? 1.0f : 0.0f;
     if (!(survives(r, x) && order_key(x) >= st.cut_key)) return 0.0f;
-    const float t = bin_pos(r, x);
-    return (float)bin_fx(r, t) * factor[bin_of(t)];
+    const Binned t = bin_token(r, x);
+    return (float)t.fx * factor[t.j];
 }
 
 // ---------------------------------------------------------------------------
@@ -683,7 +694,6 @@ __device__ __forceinline__ RowState uniform(const RowState& a)
     RowState s;
     s.mode = uniform(a.mode);
     s.m = uniform(a.m);
-    s.xmin = uniform(a.xmin);
     s.cbin = uniform(a.cbin);
     s.tc = uniform(a.tc);
     s.a_above = uniform(a.a_above);
@@ -696,11 +706,11 @@ __device__ __forceinline__ RowState uniform(const RowState& a)
 }
 
 // Byte offsets of the published fields of RowCtl.
-constexpr uint32_t kOffMode = 16, kOffM = 20, kOffXmin = 24, kOffCbin = 28, kOffCut = 32, kOffCount = 36,
+constexpr uint32_t kOffMode = 16, kOffM = 20, kOffCbin = 28, kOffCut = 32, kOffCount = 36,
                    kOffTc = 40, kOffAbove = 48, kOffStotal = 56, kOffSkeep = 64, kOffToken = 72, kOffCandN = 12;
 
 static_assert(offsetof(RowCtl, cand_n) == kOffCandN && offsetof(RowCtl, mode) == kOffMode &&
-                  offsetof(RowCtl, m) == kOffM && offsetof(RowCtl, xmin) == kOffXmin &&
+                  offsetof(RowCtl, m) == kOffM &&
                   offsetof(RowCtl, cbin) == kOffCbin && offsetof(RowCtl, cut_key) == kOffCut &&
                   offsetof(RowCtl, count) == kOffCount && offsetof(RowCtl, tc) == kOffTc &&
                   offsetof(RowCtl, a_above) == kOffAbove && offsetof(RowCtl, s_total) == kOffStotal &&
@@ -714,7 +724,6 @@ __device__ __forceinline__ void read_state(RowCtl* c, RowState& st)
         const u32x4v q1 = cload128(r, 16), q2 = cload128(r, 32), q3 = cload128(r, 48), q4 = cload128(r, 64);
         st.mode = q1.x;
         st.m = __uint_as_float(q1.y);
-        st.xmin = __uint_as_float(q1.z);
         st.cbin = q1.w;
         st.cut_key = q2.x;
         st.count = q2.y;
@@ -754,46 +763,41 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
     const uint32_t lane0 = (uint32_t)base + (uint32_t)t * 4u;
     load_chunk<DT, kEPT>(rowp, lane0, (uint32_t)base + kChunk, (uint32_t)p.V, p.vec_in, x);
 
-    // ---- A: row max, smallest finite logit, NaN / +inf
-    float lmax = -INFINITY, lmin = INFINITY;
+    // ---- A: row max, NaN / +inf
+    float lmax = -INFINITY;
     int bad = 0;
 #pragma unroll
     for (int e = 0; e < kEPT; ++e) {
         const float v = x[e];
-        bad |= (v != v) | (v == INFINITY);
+        bad |= !(v < INFINITY);  // NaN or +inf
         lmax = fmaxf(lmax, v);
-        lmin = (v > -INFINITY) ? fminf(lmin, v) : lmin;
     }
     lmax = block_reduce<kThreads>(lmax, MaxF(), sh.redf);
-    lmin = block_reduce<kThreads>(lmin, MinF(), sh.redf);
     bad = block_reduce<kThreads>(bad, OrI32(), sh.redi);
     if (t == 0) {
         u32x4v a;
         a.x = __float_as_uint(lmax);
-        a.y = __float_as_uint(lmin);
-        a.z = (uint32_t)bad;
+        a.y = (uint32_t)bad;
+        a.z = 0;
         a.w = 0;
         cstore128(coherent(wk.slot_a + wg), 0, a);
     }
     const RowParams rp = row_params(p, b);
 
     if (barrier_arrive(ctl, K, wk.epoch, sh.bar)) {
-        float m = -INFINITY, mn = INFINITY;
+        float m = -INFINITY;
         int e = 0;
         const __amdgpu_buffer_rsrc_t ra = coherent(wk.slot_a + b * K);
         for (uint32_t k = t; k < K; k += kThreads) {
             const u32x4v a = cload128(ra, k * 16);
             m = fmaxf(m, __uint_as_float(a.x));
-            mn = fminf(mn, __uint_as_float(a.y));
-            e |= (int)a.z;
+            e |= (int)a.y;
         }
         m = block_reduce<kThreads>(m, MaxF(), sh.redf);
-        mn = block_reduce<kThreads>(mn, MinF(), sh.redf);
         e = block_reduce<kThreads>(e, OrI32(), sh.redi);
         if (t == 0) {
             const __amdgpu_buffer_rsrc_t rc = coherent(ctl);
             cstore32(rc, kOffM, __float_as_uint(m));
-            cstore32(rc, kOffXmin, __float_as_uint(mn));
             cstore32(rc, kOffMode, first_mode(e != 0, m, rp.T, rp.P, rp.MP, rp.K, want_probs));
         }
         barrier_release(ctl);
@@ -804,7 +808,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
     read_state(ctl, sh.st);
     RowState st = uniform(sh.st);
     RowModel model = {};
-    if (st.mode >= kModeTop) model = uniform(make_model(st.m, st.xmin, rp.T, rp.MP));
+    if (st.mode >= kModeTop) model = uniform(make_model(st.m, rp.T, rp.MP));
 
     // ---- B: bin histogram of the survivors
     if (st.mode == kModeHist) {
@@ -817,9 +821,9 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
 #pragma unroll
         for (int e = 0; e < kEPT; ++e) {
             if (survives(model, x[e])) {
-                const float tp = bin_pos(model, x[e]);
-                const uint32_t j = bin_of(tp);
-                atomicAdd((unsigned long long*)&sh.u.h.hm[j], (unsigned long long)bin_fx(model, tp));
+                const Binned bt = bin_token(model, x[e]);
+                const uint32_t j = bt.j;
+                atomicAdd((unsigned long long*)&sh.u.h.hm[j], (unsigned long long)bt.fx);
                 if (counts) atomicAdd(&sh.u.h.hc[j], 1u);
             }
         }
@@ -984,7 +988,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
             }
             __syncthreads();
             resolve_row<kThreads>(p, b, model, rp, st,
-                        part, [&](auto&& fn) {
+                        part, cl, [&](auto&& fn) {
                             for (uint32_t i = t; i < n; i += kThreads) {
                                 const u32x2v c = sh.u.cand[i];
                                 fn(c.x, c.y);
@@ -994,7 +998,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
         } else if (n <= (uint32_t)kCap) {
             const __amdgpu_buffer_rsrc_t rk = coherent(wk.cand + b * kCap);
             resolve_row<kThreads>(p, b, model, rp, st,
-                        part, [&](auto&& fn) {
+                        part, cl, [&](auto&& fn) {
                             for (uint32_t i = t; i < n; i += kThreads) {
                                 const u32x2v c = __builtin_amdgcn_raw_buffer_load_b64(rk, i * 8, 0, kSC1);
                                 fn(c.x, c.y);
@@ -1003,7 +1007,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
                         sh.rs);
         } else {  // the crossing bin overflowed the list: visit the row in global memory
             resolve_row<kThreads>(p, b, model, rp, st,
-                        part, [&](auto&& fn) {
+                        part, cl, [&](auto&& fn) {
                             row_groups<DT>(p, rowp, [&](int64_t i0, const float* xs) {
 #pragma unroll
                                 for (int j = 0; j < 4; ++j)

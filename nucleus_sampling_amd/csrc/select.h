@@ -48,21 +48,30 @@ __device__ __forceinline__ uint64_t lane_read64(uint64_t v, int lane)
 // owns (weight > 0; zero-weight tokens are skipped).  Every thread of the
 // workgroup (NT >= 64 threads) must call select_level.  `thr_of_total(total)`
 // maps the total eligible weight to the threshold.  If no level qualifies
-// (thr == 0), the top level is returned.
+// (thr == 0), the top level is returned; with no eligible token, 0xFFFFFFFF.
+//
+// Every eligible key lies in [lo_key, hi_key].  The leading digits those two
+// share are then every eligible key's digits, and the search above would
+// pick exactly them with the weight above unchanged, so they take no pass:
+// a crossing bin's tokens usually differ only in their low two digits.
 //
 // Per digit: all threads add their tokens into the 256-bin LDS histogram;
 // then the first wave alone scans it (lane l holds digits 255-4l .. 252-4l,
 // highest first), publishes the chosen digit and clears the histogram for
 // the next digit.  Two workgroup barriers per digit.
 template <int NT, class Visit, class ThrFn>
-__device__ __forceinline__ SelectResult select_level(Visit visit, ThrFn thr_of_total, SelectShared& sh)
+__device__ __forceinline__ SelectResult select_level(Visit visit, ThrFn thr_of_total, SelectShared& sh,
+                                                     uint32_t lo_key = 0u, uint32_t hi_key = 0xFFFFFFFFu)
 {
-    uint32_t prefix = 0, mask = 0;
+    const uint32_t diff = lo_key ^ hi_key;
+    const int first = diff ? min(__builtin_clz(diff) >> 3, 3) : 3;  // at least one pass: it finds the total
+    uint32_t mask = first ? 0xFFFFFFFFu << (32 - 8 * first) : 0u;
+    uint32_t prefix = lo_key & mask;
     uint64_t base = 0, thr = 0, total = 0;
     const int t = threadIdx.x;
     for (int i = t; i < kDigitBins; i += NT) sh.hist[i] = 0;
     __syncthreads();
-    for (int lvl = 0; lvl < 4; ++lvl) {
+    for (int lvl = first; lvl < 4; ++lvl) {
         const int shift = 24 - 8 * lvl;
         visit([&](uint32_t key, uint64_t w) {
             if ((key & mask) == prefix)
@@ -74,7 +83,7 @@ __device__ __forceinline__ SelectResult select_level(Visit visit, ThrFn thr_of_t
 #pragma unroll
             for (int i = 0; i < 4; ++i) h[i] = sh.hist[kDigitBins - 1 - (4 * t + i)];
             const uint64_t ls = h[0] + h[1] + h[2] + h[3];
-            if (lvl == 0) {
+            if (lvl == first) {
                 total = wave_reduce(ls, SumU64());
                 thr = thr_of_total(total);
             }
@@ -125,7 +134,7 @@ __device__ __forceinline__ SelectResult select_level(Visit visit, ThrFn thr_of_t
                 sh.res_j = j;
                 sh.res_before = jb;
                 sh.res_at = jh;
-                if (lvl == 0) sh.res_total = total;
+                if (lvl == first) sh.res_total = total;
             }
         }
         __syncthreads();
@@ -135,10 +144,10 @@ __device__ __forceinline__ SelectResult select_level(Visit visit, ThrFn thr_of_t
         mask |= 0xFFu << shift;
     }
     SelectResult r;
-    r.level = prefix;
+    r.total = sh.res_total;
+    r.level = r.total ? prefix : 0xFFFFFFFFu;  // (as every digit of an empty search is 0xFF)
     r.above = base;
     r.at = sh.res_at;
-    r.total = sh.res_total;
     return r;
 }
 

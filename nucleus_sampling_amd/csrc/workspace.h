@@ -23,7 +23,7 @@ struct RowCtl {
     uint32_t cand_n;     // candidates appended this call
     uint32_t mode;       // row mode (model.h)
     float m;             // row max
-    float xmin;          // smallest finite logit
+    uint32_t pad0;
     uint32_t cbin;       // crossing bin (mode P) / last candidate bin (mode K)
     uint32_t cut_key;    // key of the smallest kept logit (published for the probability pass)
     uint32_t count;      // kept count
@@ -46,7 +46,7 @@ struct RacePart {
 
 struct Work {
     RowCtl* ctl;          // [rows]
-    uint4* slot_a;        // [rows * K]: max bits, min bits, error flag, 0
+    uint4* slot_a;        // [rows * K]: max bits, error flag, 0, 0
     uint64_t* slot_h;     // [rows * K][kBins] bin weights
     uint32_t* slot_c;     // [rows * K][kBins] bin counts (top-k rows)
     RacePart* slot_r;     // [rows * K]
@@ -62,7 +62,7 @@ struct Work {
 struct RowPathState {
     uint32_t mode;       // row mode (model.h)
     float m;             // row max
-    float xmin;          // smallest finite logit
+    uint32_t pad1;
     uint32_t cbin;       // crossing bin (mode P) / last candidate bin (mode K)
     uint64_t tc;         // mode P threshold inside the crossing bin
     double a_above;      // mode P: weight of the bins above the crossing bin
