@@ -246,117 +246,126 @@ __device__ __forceinline__ double lane_read_f64(double v, int lane)
 }
 
 // Decide how a row's cut is found from its merged histogram H (integer
-// weights) and C (counts of survivors per bin, only when k > 0).  Both are
-// overwritten: H with the running bin weights (doubles), C with running
-// counts, each restarting at every group of 32 bins.  Must be called by all
-// threads of one workgroup; `red` is workgroup scratch of >= 64 doubles.
+// weights) and C (counts of survivors per bin, only when k > 0).  H is
+// overwritten with the bin weights (doubles).  Must be called by all threads
+// of one workgroup.
 //
-// Deterministic: every sum runs in one fixed order whatever the block size.
-// The weight of bin j is exp(-j w) * H[j] * 2^-31; thread g adds the 32 bins
-// of group g one by one from 0.0 (keeping each running value), and S adds
-// the 32 group sums one by one.  Adding an empty bin's 0.0 changes nothing.
-// The searches then compare these same running values against the
-// threshold, so the cut never lands on an empty bin.
-__device__ __forceinline__ Decision decide(const RowModel& r, uint64_t* H, uint32_t* C, int k, float p,
-                                          double* red)
+// Deterministic whatever the block size: the weight of bin j is
+// exp(-j w) * H[j] * 2^-31, a pure function of j and H[j]; then the first
+// wave alone sums them in one fixed order: lane l adds its 16 bins
+// 16l .. 16l + 15 one by one from 0.0, a fixed six-step wave scan adds the
+// lane totals, and bin j's running weight is (the lanes before l) + (its
+// lane's running value).  Counts are integers, exact in any order.  The
+// top-p search only stops on non-empty bins, so the cut never lands on an
+// empty one whatever the rounding.
+__device__ __forceinline__ Decision decide(const RowModel& r, uint64_t* H, uint32_t* C, int k, float p)
 {
 #pragma clang fp contract(off)
+    constexpr int PER = kBins / kWave;  // bins per lane
     __shared__ Decision dec;
     const int t = threadIdx.x;
     double* W = (double*)H;
     for (int j = t; j < kBins; j += blockDim.x) W[j] = bin_weight(r, j, H[j]);
     __syncthreads();
-    if (t < 32) {  // group t: running sums of weights and counts
-        double acc = 0.0;
-        uint32_t cc = 0;
-#pragma unroll 8
-        for (int i = 0; i < 32; ++i) {
-            acc += W[32 * t + i];
-            W[32 * t + i] = acc;
-        }
-        if (C)
-#pragma unroll 8
-            for (int i = 0; i < 32; ++i) {
-                cc += C[32 * t + i];
-                C[32 * t + i] = cc;
-            }
-        red[t] = acc;
-        red[32 + t] = (double)cc;
-    }
-    __syncthreads();
     if (t < kWave) {
-        // Every lane runs the sequential sum over the 32 groups and keeps the
-        // running values before its own group (lane g < 32).
         const int lane = t;
-        double S = 0.0, run_g = 0.0, gs = 0.0;
-        uint64_t total = 0, crun_g = 0, gc = 0;
-#pragma unroll 1
-        for (int c = 0; c < 32; c += 8) {
-            double v[8], n[8];
+        // Lane totals (the searches below redo these sums bin by bin, in the
+        // same order, so they see the same values).
+        double run = 0.0;
+        uint32_t crun = 0;
+#pragma unroll 4
+        for (int i = 0; i < PER; ++i) {
+            run += W[PER * lane + i];
+            crun += C ? C[PER * lane + i] : 0u;
+        }
+        // Inclusive wave scans of the lane totals, then the exclusive parts.
+        double inc = run;
+        uint64_t cinc = crun;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                v[q] = red[c + q];
-                n[q] = red[32 + c + q];
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                if (lane == c + q) {
-                    run_g = S;
-                    gs = v[q];
-                    crun_g = total;
-                    gc = (uint64_t)n[q];
-                }
-                S += v[q];
-                total += (uint64_t)n[q];
+        for (int o = 1; o < kWave; o <<= 1) {
+            const double y = __shfl_up(inc, o, kWave);
+            const uint64_t cy = __shfl_up(cinc, o, kWave);
+            if (lane >= o) {
+                inc += y;
+                cinc += cy;
             }
         }
+        double before = __shfl_up(inc, 1, kWave);
+        uint64_t cbefore = __shfl_up(cinc, 1, kWave);
+        if (lane == 0) {
+            before = 0.0;
+            cbefore = 0;
+        }
+        const double S = lane_read_f64(inc, kWave - 1);
+        const uint64_t total = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cinc >> 32), kWave - 1)
+                                << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cinc, kWave - 1);
         Decision d;
         d.mode = kModeP;
         d.cbin = 0;
         d.tc = 0;
         d.a_above = 0.0;
         d.s_total = S;
-        bool topk = false;
         if (C && k > 0 && total > (uint64_t)k) {
             // top-k binds: the first bin where the running count reaches k.
-            const uint64_t mg = __ballot(lane < 32 && crun_g + gc >= (uint64_t)k);
-            const int g = mg ? (int)__builtin_ctzll(mg) : 31;
-            const uint64_t run = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(crun_g >> 32), g) << 32) |
-                                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)crun_g, g);
-            const uint32_t pc = lane < 32 ? C[32 * g + lane] : 0u;
-            const uint64_t mi = __ballot(lane < 32 && run + pc >= (uint64_t)k);
-            const int i = mi ? (int)__builtin_ctzll(mi) : 31;
-            d.mode = kModeK;
-            d.cbin = (uint32_t)(32 * g + i);
-            topk = true;
-        }
-        if (!topk) {
-            if (p >= 1.0f) {
-                d.mode = kModeAll;
-            } else if (p <= 0.0f) {
-                d.mode = kModeTop;
-            } else {
-                // top-p: the first group (of the first 31) whose running weight
-                // through it reaches p*S, then the first bin (of its first 31)
-                // likewise; the last group / bin when none does.
-                const double thr = (double)p * S;
-                const uint64_t mg = __ballot(lane < 31 && run_g + gs >= thr);
-                const int g = mg ? (int)__builtin_ctzll(mg) : 31;
-                double run = lane_read_f64(run_g, g);
-                const double pw = lane < 32 ? W[32 * g + lane] : 0.0;
-                const uint64_t mi = __ballot(lane < 31 && run + pw >= thr);
-                const int i = mi ? (int)__builtin_ctzll(mi) : 31;
-                const double acc = i > 0 ? lane_read_f64(pw, i - 1) : 0.0;
-                const int j = 32 * g + i;
-                run = run + acc;
-                d.cbin = (uint32_t)j;
-                d.a_above = run;
-                // Inside bin j: keep a level iff its fx-sum above < (thr - run) / (e_j 2^-31).
-                const double q = (thr - run) / (edge_weight(r, j) * (1.0 / kFx));
-                uint64_t tc = (q <= 1.0) ? 1 : (uint64_t)ceil(q);
-                if (!(q < 1.8e19)) tc = ~0ull;
-                d.tc = tc;
+            int first = PER;
+            uint32_t cc = 0;
+#pragma unroll 4
+            for (int i = 0; i < PER; ++i) {
+                cc += C[PER * lane + i];
+                first = (first == PER && cbefore + cc >= (uint64_t)k) ? i : first;
             }
+            const uint64_t m = __ballot(first < PER);
+            const int L = m ? (int)__builtin_ctzll(m) : kWave - 1;
+            const int i = __builtin_amdgcn_readlane(first < PER ? first : PER - 1, L);
+            d.mode = kModeK;
+            d.cbin = (uint32_t)(PER * L + i);
+        } else if (p >= 1.0f) {
+            d.mode = kModeAll;
+        } else if (p <= 0.0f) {
+            d.mode = kModeTop;
+        } else {
+            // top-p: the first non-empty bin whose running weight reaches
+            // p * S (the last non-empty bin when rounding leaves none).
+            const double thr = (double)p * S;
+            int first = PER, last = -1;
+            double above_first = 0.0, above_last = 0.0, acc = 0.0;
+#pragma unroll 4
+            for (int i = 0; i < PER; ++i) {
+                const double wi = W[PER * lane + i];
+                const double ab = i > 0 ? before + acc : before;  // weight of the bins before
+                acc += wi;
+                const bool nonempty = wi > 0.0;
+                if (first == PER && nonempty && before + acc >= thr) {
+                    first = i;
+                    above_first = ab;
+                }
+                if (nonempty) {
+                    last = i;
+                    above_last = ab;
+                }
+            }
+            const uint64_t mf = __ballot(first < PER);
+            int L, i;
+            double ab;
+            if (mf) {
+                L = (int)__builtin_ctzll(mf);
+                i = __builtin_amdgcn_readlane(first, L);
+                ab = lane_read_f64(above_first, L);
+            } else {
+                const uint64_t ml = __ballot(last >= 0);  // bin 0 holds the max: never empty
+                L = 63 - (int)__builtin_clzll(ml);
+                i = __builtin_amdgcn_readlane(last, L);
+                ab = lane_read_f64(above_last, L);
+            }
+            const int j = PER * L + i;
+            d.cbin = (uint32_t)j;
+            d.a_above = ab;
+            // Inside bin j: keep a level iff its fx-sum above < (thr - above) / (e_j 2^-31).
+            const double q = (thr - ab) / (edge_weight(r, j) * (1.0 / kFx));
+            uint64_t tc = (q <= 1.0) ? 1 : (uint64_t)ceil(q);
+            if (!(q < 1.8e19)) tc = ~0ull;
+            d.tc = tc;
         }
         if (lane == 0) dec = d;
     }

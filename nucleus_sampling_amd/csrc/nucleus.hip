@@ -225,12 +225,12 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
         if (dtype == NUCLEUS_F32) {
             hipLaunchKernelGGL((row_kernel<kF32, true>), rows, dim3(kRowThreads), 0, s, p, rw);
             hipLaunchKernelGGL(race_kernel<kF32>, racers, dim3(kRaceThreads), 0, s, p, rw);
-            hipLaunchKernelGGL(resolve_kernel<kF32>, rows, dim3(kRaceThreads), 0, s, p, rw);
+            hipLaunchKernelGGL(resolve_kernel<kF32>, rows, dim3(kRowThreads), 0, s, p, rw);
             if (out_probs) hipLaunchKernelGGL(probs_kernel<kF32>, chunks, dim3(kRaceThreads), 0, s, p, pw);
         } else {
             hipLaunchKernelGGL((row_kernel<kBF16, true>), rows, dim3(kRowThreads), 0, s, p, rw);
             hipLaunchKernelGGL(race_kernel<kBF16>, racers, dim3(kRaceThreads), 0, s, p, rw);
-            hipLaunchKernelGGL(resolve_kernel<kBF16>, rows, dim3(kRaceThreads), 0, s, p, rw);
+            hipLaunchKernelGGL(resolve_kernel<kBF16>, rows, dim3(kRowThreads), 0, s, p, rw);
             if (out_probs) hipLaunchKernelGGL(probs_kernel<kBF16>, chunks, dim3(kRaceThreads), 0, s, p, pw);
         }
     } else {

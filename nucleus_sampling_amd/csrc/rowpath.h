@@ -13,13 +13,15 @@
 //   and an optional probability pass), or publishes the row's state for
 //   race_kernel.
 //
-// race_kernel: the race pass split over chunks of 8192 tokens, one 256-thread
-//   workgroup each, so a row that keeps most of its tokens (whose Philox
+// race_kernel: the race pass split into items of 2048 tokens, each raced by
+//   one wave on its own, so a row that keeps most of its tokens (whose Philox
 //   draws dominate) spreads over many CUs instead of holding one.  Each
-//   chunk merges its race partial into the row's state with order-free
+//   item merges its race partial into the row's state with order-free
 //   atomics (max of the packed score, sums, min) and appends its candidates
-//   to the row's list; the chunk that finishes a row last resolves it.  No
-//   workgroup ever waits for another.
+//   to the row's list.  No workgroup ever waits for another.
+//
+// resolve_kernel: one workgroup per row resolves the exact cut from the
+//   merged partials and the candidate list, and writes the outputs.
 //
 // probs_kernel: the optional probability pass, chunked the same way.
 //
@@ -224,9 +226,10 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
 }
 
 // Appends (key, idx) for the lanes with pred to the wave's own segment of an
-// LDS list (kWaveCand entries); n, the same in every lane, counts the
+// LDS list (CAP entries); n, the same in every lane, counts the
 // wave's appends, those past the segment (dropped) included.  No atomics:
 // positions come from the lanes' ranks.
+template <uint32_t CAP = kWaveCand>
 __device__ __forceinline__ void wave_append(u32x2v* seg, uint32_t& n, bool pred, uint32_t key, uint32_t idx)
 {
     const uint64_t mask = __ballot(pred);
@@ -234,7 +237,7 @@ __device__ __forceinline__ void wave_append(u32x2v* seg, uint32_t& n, bool pred,
     if (pred) {
         const uint32_t off =
             n + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        if (off < (uint32_t)kWaveCand) {
+        if (off < CAP) {
             u32x2v e;
             e.x = key;
             e.y = idx;
@@ -350,29 +353,24 @@ __device__ __forceinline__ void race_queued(const Params& p, int64_t b, bool sco
     }
 }
 
-// Appends (key, idx) for the lanes with pred to a row's list in global memory
-// (device-coherent stores): one atomic per wave on the row's counter.
-// Appends past `cap` are counted but dropped.
-__device__ __forceinline__ void global_append(uint32_t* counter, __amdgpu_buffer_rsrc_t list, uint32_t cap, bool pred,
-                                              uint32_t key, uint32_t idx)
+// A wave's staging area for candidates bound for a row's list in global
+// memory: appends go to LDS (wave_append) and are flushed with one atomic
+// on the row's counter per kStage entries, instead of one per appending
+// group (a returning device atomic stalls the wave for a microsecond).
+constexpr int kStage = 256;
+
+__device__ __forceinline__ void stage_flush(u32x2v* stage, uint32_t& sn, uint32_t* counter,
+                                            __amdgpu_buffer_rsrc_t list, uint32_t cap, uint32_t lane)
 {
-    const uint64_t mask = __ballot(pred);
-    if (mask == 0) return;
-    const int leader = __builtin_ctzll(mask);
+    if (sn == 0) return;
     uint32_t base = 0;
-    if ((int)__lane_id() == leader)
-        base = __hip_atomic_fetch_add(counter, (uint32_t)__popcll(mask), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
-    if (pred) {
-        const uint32_t off = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        if (off < cap) {
-            u32x2v e;
-            e.x = key;
-            e.y = idx;
-            __builtin_amdgcn_raw_buffer_store_b64(e, list, off * 8, 0, kSC1);
-        }
-    }
+    if (lane == 0) base = __hip_atomic_fetch_add(counter, sn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (uint32_t i = lane; i < sn; i += kWave)
+        if (base + i < cap) __builtin_amdgcn_raw_buffer_store_b64(stage[i], list, (base + i) * 8, 0, kSC1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    sn = 0;
 }
 
 struct RowShared {
@@ -388,7 +386,6 @@ struct RowShared {
         float factor[kBins];  // probability pass
     } u;
     ResolveShared rs;
-    double red[64];
     float redf[kMaxWaves];
     int redi[kMaxWaves];
     uint32_t wcand[kMaxWaves];  // candidates each wave found (past its segment too)
@@ -600,7 +597,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             }
         }
         __syncthreads();
-        const Decision d = decide(model, H, counts ? C : nullptr, rp.K, rp.P, sh.red);
+        const Decision d = decide(model, H, counts ? C : nullptr, rp.K, rp.P);
         st.mode = uniform(d.mode);
         st.cbin = uniform(d.cbin);
         st.tc = uniform(d.tc);
@@ -740,11 +737,12 @@ constexpr int kItemGroups = 8;                         // groups per lane per wo
 constexpr int kItemTokens = kWave * kItemGroups * 4;   // 2048 tokens per item
 
 // Every wave of race_kernel works alone on 2048-token items of the batch:
-// item k is chunk k / B of row k % B, and wave w of the W launched takes items
-// w, w + W, w + 2W, ...  The waves resident on a CU thus hold chunks of many
-// rows, so rows that keep many tokens (whose Philox draws dominate) and rows
+// item k is chunk c = k / B of row (k + c) % B, and wave w of the W launched
+// takes items w, w + W, w + 2W, ...  The waves resident on a CU thus hold
+// chunks of many rows, so rows that keep many tokens (whose Philox draws dominate) and rows
 // that keep few share every CU.  A wave races its item's kept tokens through
-// its ring, appends the item's candidates to the row's list and merges its
+// its ring, appends the item's candidates to the row's list (staged in LDS,
+// one atomic on the row's counter per flush) and merges its
 // race partial into the row with order-free atomics (max of the packed
 // score, sums, min).  No barrier, no waiting, no shared work counter:
 // resolve_kernel, the next launch, reads the merged results.
@@ -752,54 +750,79 @@ template <int DT>
 __global__ __launch_bounds__(kRaceThreads, 4) void race_kernel(Params p, RowWork rw)
 {
     __shared__ RaceQueue rings[kRaceThreads / kWave];
+    __shared__ u32x2v stages[kRaceThreads / kWave][kStage];
     const uint32_t lane = threadIdx.x & (kWave - 1);
     RaceQueue& rq = rings[threadIdx.x / kWave];
+    u32x2v* const stage = stages[threadIdx.x / kWave];
     const uint32_t B = (uint32_t)p.B;
     const uint32_t NI = (uint32_t)rw.N;  // items per row
     const uint32_t total = B * NI;
     const int64_t esz = DT == kF32 ? 4 : 2;
     const uint32_t waves = gridDim.x * (kRaceThreads / kWave);
-    for (uint32_t item = blockIdx.x * (kRaceThreads / kWave) + threadIdx.x / kWave; item < total; item += waves) {
-        const int64_t b = item % B;
-        const uint32_t chunk = item / B;
-        RowPathState* ps = rw.st + b;
+    // The current item's row and its published state (wave-uniform).
+    int64_t b = 0;
+    uint32_t g0 = 0;  // the item's first 4-token group
+    RowPathState* ps = nullptr;
+    RowModel model = {};
+    float keep_lo = INFINITY, cand_lo = INFINITY, c_log2e = 0.0f, wbest = 0.0f, sstar = 0.0f;
+    bool scored = false, has_cand = false;
+    __amdgpu_buffer_rsrc_t rk;
+    auto where = [&](uint32_t it, int64_t& rb, uint32_t& rg0) {
+        // Chunk c of the rows is rotated by c, so that a wave whose stride is
+        // a multiple of B still meets a different row at every item.
+        const uint32_t chunk = it / B;
+        rb = (int64_t)((it % B + chunk) % B);
+        rg0 = chunk * (uint32_t)(kItemTokens / 4);
+    };
+    auto rowp_of = [&](int64_t rb) { return (const void*)((const char*)p.logits + rb * p.stride * esz); };
+    auto open_item = [&](int64_t rb) {
+        ps = rw.st + rb;
         const uint32_t mode = uniform(ps->mode);
-        if (mode == kModeError) continue;
-        const RowModel model = uniform(*(const RowModel*)ps->model);
-        const float keep_lo = uniform(ps->keep_lo), cand_lo = uniform(ps->cand_lo);
-        const bool scored = mode != kModeGreedy, has_cand = cand_lo < keep_lo;
-        const float c_log2e = model.invT * 1.4426950408889634f;
-        const void* rowp = (const char*)p.logits + b * p.stride * esz;
-        const __amdgpu_buffer_rsrc_t rk = coherent(rw.cand + b * kCap);
+        model = uniform(*(const RowModel*)ps->model);
+        const bool live = mode != kModeError;  // error rows: no token compares >= NaN
+        keep_lo = live ? uniform(ps->keep_lo) : __builtin_nanf("");
+        cand_lo = live ? uniform(ps->cand_lo) : __builtin_nanf("");
+        scored = mode != kModeGreedy;
+        has_cand = cand_lo < keep_lo;
+        c_log2e = model.invT * 1.4426950408889634f;
+        rk = coherent(rw.cand + rb * kCap);
         // The screen starts from the best score the row has reached so far.
-        float wbest = scored ? __uint_as_float((uint32_t)(get(&ps->best) >> 32)) : 0.0f;
-        float sstar = wbest;
-        RaceAcc acc;
-        acc.init();
-        uint32_t qh = 0, qn = 0;
-        auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
-            bool keep[2][4];
+        wbest = (scored && live) ? __uint_as_float((uint32_t)(get(&ps->best) >> 32)) : 0.0f;
+        sstar = wbest;
+    };
+
+    RaceAcc acc;
+    acc.init();
+    uint32_t qh = 0, qn = 0;
+    uint32_t sn = 0;  // staged candidates, the same in every lane
+    auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
+        bool keep[2][4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) keep[h][j] = active[h] && xs[h][j] >= keep_lo;
-            race_groups<2>(p, b, scored, model, c_log2e, i0, xs, keep, acc, sstar);
-            // Share the wave's best score only when some lane improved it.
-            if (__ballot(sstar > wbest)) wbest = wave_reduce(sstar, MaxF());
-            sstar = fmaxf(sstar, wbest);
-        };
-        load_groups<DT, false, kWave, kItemGroups>(
-            p, rowp, chunk * (uint32_t)(kItemTokens / 4), lane, [&](uint32_t i0, const float* xs) {
-                const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
-                wq_push(rq, qh, qn, lane, any, i0, xs, race);
-                if (has_cand) {
+            for (int j = 0; j < 4; ++j) keep[h][j] = active[h] && xs[h][j] >= keep_lo;
+        if (scored && __ballot(sstar == 0.0f)) seed_bound(p, b, model, i0, xs, keep, acc, sstar);
+        race_groups<2>(p, b, scored, model, c_log2e, i0, xs, keep, acc, sstar);
+        // Share the wave's best score only when some lane improved it.
+        if (__ballot(sstar > wbest)) wbest = wave_reduce(sstar, MaxF());
+        sstar = fmaxf(sstar, wbest);
+    };
+    auto group = [&](uint32_t i0, const float* xs) {
+        const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
+        wq_push(rq, qh, qn, lane, any, i0, xs, race);
+        if (has_cand) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        global_append(&ps->cand_n, rk, kCap, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]),
-                                      i0 + j);
-                }
-            });
+            for (int j = 0; j < 4; ++j) {
+                if (sn + kWave > (uint32_t)kStage) stage_flush(stage, sn, &ps->cand_n, rk, kCap, lane);
+                wave_append<kStage>(stage, sn, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]), i0 + j);
+            }
+        }
+    };
+    // End of an item: race what the ring holds, hand the candidates over and
+    // merge the race partial into the row.
+    auto close_item = [&]() {
         if (qn) wq_drain(rq, qh, qn, lane, qn, race);
+        stage_flush(stage, sn, &ps->cand_n, rk, kCap, lane);
         const uint64_t best = wave_reduce(acc.best, MaxU64());
         const uint32_t count = wave_reduce(acc.count, SumU32());
         const uint32_t minkey = wave_reduce(acc.minkey, MinU32());
@@ -808,6 +831,14 @@ __global__ __launch_bounds__(kRaceThreads, 4) void race_kernel(Params p, RowWork
             __hip_atomic_fetch_add(&ps->count, count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_fetch_min(&ps->minkey, minkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        acc.init();
+    };
+
+    for (uint32_t item = blockIdx.x * (kRaceThreads / kWave) + threadIdx.x / kWave; item < total; item += waves) {
+        where(item, b, g0);
+        open_item(b);
+        load_groups<DT, false, kWave, kItemGroups>(p, rowp_of(b), g0, lane, group);
+        close_item();
     }
 }
 
@@ -819,7 +850,7 @@ struct ResolveKShared {
 // After race_kernel: one workgroup per row resolves the exact cut from the
 // merged race partial and the row's candidate list, and writes the outputs.
 template <int DT>
-__global__ __launch_bounds__(kRaceThreads) void resolve_kernel(Params p, RowWork rw)
+__global__ __launch_bounds__(kRowThreads) void resolve_kernel(Params p, RowWork rw)
 {
     __shared__ ResolveKShared sh;
     const int64_t b = blockIdx.x;
@@ -841,7 +872,7 @@ __global__ __launch_bounds__(kRaceThreads) void resolve_kernel(Params p, RowWork
     const int64_t esz = DT == kF32 ? 4 : 2;
     const void* rowp = (const char*)p.logits + b * p.stride * esz;
     if (n <= (uint32_t)kCandLds) {
-        for (uint32_t i = t; i < n; i += kRaceThreads) {
+        for (uint32_t i = t; i < n; i += kRowThreads) {
             const uint2 c = list[i];
             u32x2v e;
             e.x = c.x;
@@ -849,27 +880,27 @@ __global__ __launch_bounds__(kRaceThreads) void resolve_kernel(Params p, RowWork
             sh.cand[i] = e;
         }
         __syncthreads();
-        resolve_row<kRaceThreads>(p, b, model, rp, st, part, cl,
+        resolve_row<kRowThreads>(p, b, model, rp, st, part, cl,
                                   [&](auto&& fn) {
-                                      for (uint32_t i = t; i < n; i += kRaceThreads) {
+                                      for (uint32_t i = t; i < n; i += kRowThreads) {
                                           const u32x2v c = sh.cand[i];
                                           fn(c.x, c.y);
                                       }
                                   },
                                   sh.rs);
     } else if (n <= (uint32_t)kCap) {
-        resolve_row<kRaceThreads>(p, b, model, rp, st, part, cl,
+        resolve_row<kRowThreads>(p, b, model, rp, st, part, cl,
                                   [&](auto&& fn) {
-                                      for (uint32_t i = t; i < n; i += kRaceThreads) {
+                                      for (uint32_t i = t; i < n; i += kRowThreads) {
                                           const uint2 c = list[i];
                                           fn(c.x, c.y);
                                       }
                                   },
                                   sh.rs);
     } else {  // the crossing bin overflowed the list: visit the row in global memory
-        resolve_row<kRaceThreads>(p, b, model, rp, st, part, cl,
+        resolve_row<kRowThreads>(p, b, model, rp, st, part, cl,
                                   [&](auto&& fn) {
-                                      stream_row<DT, false, kRaceThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
+                                      stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
 #pragma unroll
                                           for (int j = 0; j < 4; ++j)
                                               if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), i0 + j);

@@ -356,12 +356,12 @@ __device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool sco
         any |= km[g] != 0;
     }
     if (!any) return;
-    float xm = INFINITY;
+    float xm = INFINITY;  // kept tokens are finite: a compare and a select do
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         acc.count += (uint32_t)__builtin_popcount(km[g]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xm = keep[g][j] ? fminf(xm, x[g][j]) : xm;
+        for (int j = 0; j < 4; ++j) xm = (keep[g][j] & (x[g][j] < xm)) ? x[g][j] : xm;
     }
     const uint32_t kmin = order_key(xm);
     acc.minkey = kmin < acc.minkey ? kmin : acc.minkey;
@@ -386,9 +386,11 @@ __device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool sco
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            // Computed for every token and masked afterwards: no branches.
             const float e_hat = __builtin_amdgcn_exp2f((x[g][j] - r.m) * c_log2e);
             const float w = fmaf((float)(0xFFFFFFFFu - philox_word(w4[g], (uint32_t)j)), 0x1p-32f, 0x1p-33f);
-            pass |= (keep[g][j] && !(w > e_hat * k)) ? (1u << (4 * g + j)) : 0u;
+            const uint32_t bit = 1u << (4 * g + j);
+            pass |= (km[g] & (1u << j) ? bit : 0u) & (w > e_hat * k ? 0u : bit);
         }
     while (pass) {
         const uint32_t k = (uint32_t)__builtin_ctz(pass);
@@ -680,7 +682,6 @@ struct TileShared {
         u32x2v cand[kCandLds];  // the row's candidates, staged for the resolver
     } u;
     ResolveShared rs;
-    double red[64];
     float redf[kThreads / kWave];
     int redi[kThreads / kWave];
     uint32_t red32[kThreads / kWave];
@@ -884,7 +885,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
                 }
             }
             __syncthreads();
-            const Decision d = decide(model, sh.u.h.hm, counts ? sh.u.h.hc : nullptr, rp.K, rp.P, sh.red);
+            const Decision d = decide(model, sh.u.h.hm, counts ? sh.u.h.hc : nullptr, rp.K, rp.P);
             if (t == 0) {
                 const __amdgpu_buffer_rsrc_t rc = coherent(ctl);
                 put(&ctl->cand_n, 0u);  // the candidates of this call are appended after this barrier
