@@ -334,7 +334,8 @@ __device__ __forceinline__ void seed_bound(const Params& p, int64_t b, const Row
 // screen never drops a possible winner), race, and publish the wave's best.
 __device__ __forceinline__ void race_queued(const Params& p, int64_t b, bool scored, const RowModel& r,
                                             float c_log2e, float keep_lo, const uint32_t i0[2], const float xs[2][4],
-                                            const bool active[2], RaceAcc& acc, float& sstar, uint32_t* shared_bits)
+                                            const bool active[2], RaceAcc& acc, float& sstar, uint32_t* shared_bits,
+                                            bool track_min)
 {
     const float shared_best = __uint_as_float(*shared_bits);
     sstar = fmaxf(sstar, shared_best);
@@ -344,7 +345,7 @@ __device__ __forceinline__ void race_queued(const Params& p, int64_t b, bool sco
 #pragma unroll
         for (int j = 0; j < 4; ++j) keep[h][j] = active[h] && xs[h][j] >= keep_lo;
     if (scored && __ballot(sstar == 0.0f)) seed_bound(p, b, r, i0, xs, keep, acc, sstar);
-    race_groups<2>(p, b, scored, r, c_log2e, i0, xs, keep, acc, sstar);
+    race_groups<2>(p, b, scored, r, c_log2e, i0, xs, keep, acc, sstar, track_min);
     // Publish only when some lane improved on the shared best (after the first
     // few groups that is rare, and the wave reduction is skipped).
     if (__ballot(sstar > shared_best)) {
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     u32x2v* const seg = sh.u.r.cand + (t / kWave) * kWaveCand;
     uint32_t wn = 0;          // the wave's candidates, the same in every lane
     auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
-        race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits);
+        race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits, !has_cand);
     };
     stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
         const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
@@ -802,7 +803,7 @@ __global__ __launch_bounds__(kRaceThreads, 4) void race_kernel(Params p, RowWork
 #pragma unroll
             for (int j = 0; j < 4; ++j) keep[h][j] = active[h] && xs[h][j] >= keep_lo;
         if (scored && __ballot(sstar == 0.0f)) seed_bound(p, b, model, i0, xs, keep, acc, sstar);
-        race_groups<2>(p, b, scored, model, c_log2e, i0, xs, keep, acc, sstar);
+        race_groups<2>(p, b, scored, model, c_log2e, i0, xs, keep, acc, sstar, !has_cand);
         // Share the wave's best score only when some lane improved it.
         if (__ballot(sstar > wbest)) wbest = wave_reduce(sstar, MaxF());
         sstar = fmaxf(sstar, wbest);

@@ -329,7 +329,9 @@ __device__ __forceinline__ uint32_t philox_word(const uint4& w4, uint32_t j)
 // Race G groups of four consecutive tokens (group g starts at token i0[g];
 // keep[g][j] marks the kept ones).  `scored` is false for greedy rows, where
 // every kept token scores 1 so that the lowest index wins.  sstar is this
-// lane's best exact score so far.  Several groups per call let the Philox
+// lane's best exact score so far.  `track_min` off skips the smallest kept
+// key: a row with crossing-bin candidates always keeps the top level of that
+// bin, below every surely kept token, so its resolver finds that key.  Several groups per call let the Philox
 // rounds of different groups interleave.
 //
 // The screen.  A token can reach sstar only if e/E >= sstar, i.e.
@@ -346,7 +348,7 @@ __device__ __forceinline__ uint32_t philox_word(const uint4& w4, uint32_t j)
 template <int G>
 __device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool scored, const RowModel& r, float c_log2e,
                                             const uint32_t i0[G], const float x[G][4], const bool keep[G][4],
-                                            RaceAcc& acc, float& sstar)
+                                            RaceAcc& acc, float& sstar, bool track_min = true)
 {
     uint32_t km[G];
     bool any = false;
@@ -356,15 +358,17 @@ __device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool sco
         any |= km[g] != 0;
     }
     if (!any) return;
-    float xm = INFINITY;  // kept tokens are finite: a compare and a select do
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        acc.count += (uint32_t)__builtin_popcount(km[g]);
+    for (int g = 0; g < G; ++g) acc.count += (uint32_t)__builtin_popcount(km[g]);
+    if (track_min) {  // uniform
+        float xm = INFINITY;  // kept tokens are finite: a compare and a select do
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xm = (keep[g][j] & (x[g][j] < xm)) ? x[g][j] : xm;
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xm = (keep[g][j] & (x[g][j] < xm)) ? x[g][j] : xm;
+        const uint32_t kmin = order_key(xm);
+        acc.minkey = kmin < acc.minkey ? kmin : acc.minkey;
     }
-    const uint32_t kmin = order_key(xm);
-    acc.minkey = kmin < acc.minkey ? kmin : acc.minkey;
     if (!scored) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -420,7 +424,7 @@ __device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool sco
 // One group (the split-row kernel's register-resident chunk).
 __device__ __forceinline__ void race_group(const Params& p, int64_t b, bool scored, const RowModel& r, float c_log2e,
                                            uint32_t i0, const float x[4], const bool keep[4], RaceAcc& acc,
-                                           float& sstar)
+                                           float& sstar, bool track_min)
 {
     const uint32_t i0s[1] = {i0};
     float xs[1][4];
@@ -430,7 +434,7 @@ __device__ __forceinline__ void race_group(const Params& p, int64_t b, bool scor
         xs[0][j] = x[j];
         ks[0][j] = keep[j];
     }
-    race_groups<1>(p, b, scored, r, c_log2e, i0s, xs, ks, acc, sstar);
+    race_groups<1>(p, b, scored, r, c_log2e, i0s, xs, ks, acc, sstar, track_min);
 }
 
 // Race one token by index (resolver candidates).
@@ -923,7 +927,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
             keep[j] = x[4 * v + j] >= keep_lo;
             ncand += (x[4 * v + j] >= cand_lo && !keep[j]) ? 1u : 0u;
         }
-        race_group(p, b, scored, model, c_log2e, i0, &x[4 * v], keep, acc, sstar);
+        race_group(p, b, scored, model, c_log2e, i0, &x[4 * v], keep, acc, sstar, !has_cands);
         if (scored) sstar = wave_reduce(sstar, MaxF());
     }
     if (has_cands) {
