@@ -71,6 +71,9 @@ class Oracle:
         vp, i64, u64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32
         L.oracle_sample.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, u64, u64, i64, i64, vp, vp]
         L.oracle_sample.restype = ctypes.c_int
+        L.oracle_sample_ex.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, u64, vp, u64, i64, i64, vp,
+                                       vp, vp]
+        L.oracle_sample_ex.restype = ctypes.c_int
         L.oracle_eval_cut.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_float, ctypes.c_float, i32,
                                       ctypes.c_float, u64, u64, ctypes.c_double, vp, vp]
         L.oracle_eval_cut.restype = ctypes.c_int
@@ -87,14 +90,17 @@ class Oracle:
         self.L = L
 
     def sample(self, logits, temperature, top_p, top_k=None, min_p=None, seed=0, step=0,
-               rows=None, want_probs=False, threads=1):
+               rows=None, want_probs=False, threads=1, seeds=None, want_logprobs=False):
         """Run the oracle on a [B, V] batch.
 
         ``logits`` is float32 or uint16 (bf16 bit patterns).  ``rows``
         (optional iterable of row indices) limits the work to those rows; the
-        other entries of the result stay zero.  Returns (rows, probs): a
+        other entries of the result stay zero.  ``seeds`` (optional [B]
+        uint64) gives each row its own race key.  Returns (rows, probs): a
         structured array of ROW_DTYPE of length B, and float64 probabilities
-        ([B, V], or [len(rows), V] in the order of ``rows``) or None.
+        ([B, V], or [len(rows), V] in the order of ``rows``) or None; with
+        ``want_logprobs``, (rows, probs, logprobs), the log-probabilities laid
+        out like the probabilities.
         """
         logits = np.ascontiguousarray(logits)
         B, V = logits.shape
@@ -103,6 +109,7 @@ class Oracle:
         P = np.ascontiguousarray(top_p, dtype=np.float32).reshape(B)
         K = None if top_k is None else np.ascontiguousarray(top_k, dtype=np.int32).reshape(B)
         MP = None if min_p is None else np.ascontiguousarray(min_p, dtype=np.float32).reshape(B)
+        S = None if seeds is None else np.ascontiguousarray(seeds, dtype=np.uint64).reshape(B)
         out = np.zeros(B, dtype=ROW_DTYPE)
         if rows is None:
             spans = [(b, b + 1) for b in range(B)] if threads > 1 else [(0, B)]
@@ -111,15 +118,17 @@ class Oracle:
         # probs[j] belongs to spans[j][0] .. (one buffer row per span row)
         nrows = sum(s1 - s0 for s0, s1 in spans)
         probs = np.zeros((nrows, V), dtype=np.float64) if want_probs else None
+        logprobs = np.zeros((nrows, V), dtype=np.float64) if want_logprobs else None
         starts = np.cumsum([0] + [s1 - s0 for s0, s1 in spans])
         L = self.L
 
         def run(j):
             s0, s1 = spans[j]
             pp = None if probs is None else probs[starts[j]:starts[j + 1]]
-            rc = L.oracle_sample(_ptr(logits), dt, B, V, V, _ptr(T), _ptr(P), _ptr(K), _ptr(MP),
-                                 ctypes.c_uint64(seed), ctypes.c_uint64(step), s0, s1,
-                                 _ptr(out), None if pp is None else pp.ctypes.data)
+            lp = None if logprobs is None else logprobs[starts[j]:starts[j + 1]]
+            rc = L.oracle_sample_ex(_ptr(logits), dt, B, V, V, _ptr(T), _ptr(P), _ptr(K), _ptr(MP),
+                                    ctypes.c_uint64(seed), _ptr(S), ctypes.c_uint64(step), s0, s1, _ptr(out),
+                                    None if pp is None else pp.ctypes.data, None if lp is None else lp.ctypes.data)
             if rc != 0:
                 raise ValueError("oracle_sample rejected its arguments")
 
@@ -129,6 +138,8 @@ class Oracle:
         else:
             for j in range(len(spans)):
                 run(j)
+        if want_logprobs:
+            return out, probs, logprobs
         return out, probs
 
     def eval_cut(self, logits_row, row, temperature, top_p, top_k, min_p, seed, step, cut, want_probs=False):

@@ -344,12 +344,20 @@ static int64_t race(const row_prep* r, const uint8_t* keep, int64_t V, uint64_t 
  * rows_out[b] receives the result of row b.  probs_out, if not NULL, is a
  * [r1 - r0, V] float64 array whose row (b - r0) receives the renormalised kept
  * distribution of row b (one-hot for greedy rows, zeros for error rows).
+ * seeds, if not NULL, gives row b its own race key seeds[b] in place of seed
+ * (a per-request seed; "Top-p (Nucleus) Sampling, in depth", "Logprobs,
+ * speculative decoding and reproducibility").  logprobs_out, if not NULL, is
+ * laid out like probs_out and receives the log-probabilities of the same
+ * processed distribution (the same section: outside the nucleus the
+ * probability is zero): ln p_i = (x_i - m)/T - ln S_keep for kept tokens, taken
+ * in the log domain so that a kept token whose weight underflows stays finite;
+ * -inf for every other token; 0 and -inf for greedy rows; NaN for error rows.
  * Returns 0, or -1 on bad arguments.
  */
-int oracle_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride,
-                  const float* temperature, const float* top_p, const int32_t* top_k,
-                  const float* min_p, uint64_t seed, uint64_t step, int64_t r0, int64_t r1,
-                  oracle_row* rows_out, double* probs_out)
+int oracle_sample_ex(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride,
+                     const float* temperature, const float* top_p, const int32_t* top_k,
+                     const float* min_p, uint64_t seed, const uint64_t* seeds, uint64_t step, int64_t r0,
+                     int64_t r1, oracle_row* rows_out, double* probs_out, double* logprobs_out)
 {
     if (V < 1 || B < 0 || r0 < 0 || r1 > B || stride < V || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
         return -1;
@@ -360,6 +368,10 @@ int oracle_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t s
         o->minp_nearest = INFINITY;
         double* prow = probs_out ? probs_out + (b - r0) * V : NULL;
         if (prow) memset(prow, 0, (size_t)V * sizeof(double));
+        double* lrow = logprobs_out ? logprobs_out + (b - r0) * V : NULL;
+        if (lrow)
+            for (int64_t i = 0; i < V; ++i) lrow[i] = -INFINITY;
+        const uint64_t row_seed = seeds ? seeds[b] : seed;
 
         float T = temperature[b], P = top_p[b], MP = min_p ? min_p[b] : 0.0f;
         int32_t K = top_k ? top_k[b] : 0;
@@ -367,6 +379,8 @@ int oracle_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t s
         prep_row(logits, dtype, V, b * stride, T, P, K, MP, &r);
         if (r.err) {
             o->status = 1; o->token = -1; o->keep_count = 0;
+            if (lrow)
+                for (int64_t i = 0; i < V; ++i) lrow[i] = NAN;
             prep_free(&r);
             continue;
         }
@@ -379,6 +393,7 @@ int oracle_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t s
             o->s_keep = 1.0;
             o->race_margin = 1.0;
             if (prow) prow[r.greedy_token] = 1.0;
+            if (lrow) lrow[r.greedy_token] = 0.0;
             prep_free(&r);
             continue;
         }
@@ -412,10 +427,15 @@ int oracle_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t s
         o->min_kept_logit = minkept;
         if (prow)
             for (int64_t i = 0; i < V; ++i) prow[i] = keep[i] ? r.e[i] / s_keep : 0.0;
+        if (lrow) {
+            const double lse = log(s_keep), Td = (double)temperature[b];
+            for (int64_t i = 0; i < V; ++i)
+                if (keep[i]) lrow[i] = (r.x[i] - r.m) / Td - lse;
+        }
 
         /* 8. The race. */
         double s1, s2;
-        o->token = (int32_t)race(&r, keep, V, seed, step, b, &s1, &s2);
+        o->token = (int32_t)race(&r, keep, V, row_seed, step, b, &s1, &s2);
         o->race_s1 = s1;
         o->race_s2 = s2;
         o->race_margin = (kept <= 1) ? 1.0 : (s1 - s2) / s1;
@@ -424,6 +444,16 @@ int oracle_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t s
         prep_free(&r);
     }
     return 0;
+}
+
+/* oracle_sample_ex with one seed for every row and no log-probabilities. */
+int oracle_sample(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride,
+                  const float* temperature, const float* top_p, const int32_t* top_k,
+                  const float* min_p, uint64_t seed, uint64_t step, int64_t r0, int64_t r1,
+                  oracle_row* rows_out, double* probs_out)
+{
+    return oracle_sample_ex(logits, dtype, B, V, stride, temperature, top_p, top_k, min_p, seed, NULL, step,
+                            r0, r1, rows_out, probs_out, NULL);
 }
 
 /*

@@ -391,5 +391,69 @@ def check_exp1(O):
     assert abs(O.exp1(2**31) - (-math.log((2**31 + 0.5) / 2**32))) < 1e-15
 
 
+def check_logprobs(O):
+    """Processed-distribution log-probabilities: ln p_i on the kept set, -inf
+    outside it (outside the nucleus the probability is zero), NaN on error
+    rows.  Pinned to the printed worked examples, a closed form, a kept token
+    whose weight underflows, and invariants on random rows."""
+    for case in golden()["cases"]:
+        if "probs" in case or "renormalized" not in case:
+            continue
+        x = _logits_of(case)
+        r, pr, lp = O.sample(x[None, :], [case["T"]], [case["p"]], want_probs=True, want_logprobs=True)
+        n = len(case["renormalized"])
+        assert np.allclose(np.exp(lp[0, :n]), case["renormalized"], atol=case["tol"]), (case["id"], lp[0, :n])
+        assert np.all(np.isneginf(lp[0][pr[0] == 0])), case["id"]
+    # T = +inf: every finite token weighs the same, ln p = -ln(n finite).
+    x = np.array([[0.5, -2.0, 3.0, -np.inf, 1.0]], dtype=np.float32)
+    r, pr, lp = O.sample(x, [np.inf], [1.0], want_probs=True, want_logprobs=True)
+    assert np.allclose(lp[0, [0, 1, 2, 4]], -math.log(4.0), atol=1e-15) and np.isneginf(lp[0, 3])
+    # p = 1 keeps a token of weight e^-800 (it underflows in double); its
+    # log-probability is -800 - ln(1 + e^-800) = -800.
+    r, pr, lp = O.sample(np.array([[0.0, -800.0]], dtype=np.float32), [1.0], [1.0], want_probs=True,
+                         want_logprobs=True)
+    assert pr[0, 1] == 0.0 and lp[0, 1] == -800.0 and lp[0, 0] == 0.0
+    # Greedy: 0 at the lowest-index max, -inf elsewhere; an error row is NaN.
+    r, pr, lp = O.sample(np.array([[1.0, 3.0, 3.0, 2.0], [1.0, np.nan, 0.0, 0.0]], dtype=np.float32),
+                         [0.0, 1.0], [0.9, 0.9], want_probs=True, want_logprobs=True)
+    assert lp[0, 1] == 0.0 and np.all(np.isneginf(lp[0, [0, 2, 3]])) and np.all(np.isnan(lp[1]))
+    # Random rows at several temperatures: the kept log-probabilities sum to one
+    # in the exponential and differ by (x_i - x_j)/T.
+    rng = np.random.default_rng(12)
+    for T in (0.3, 1.0, 2.5):
+        x = rng.normal(0.0, 2.0, (4, 200)).astype(np.float32)
+        r, pr, lp = O.sample(x, [T] * 4, [0.9] * 4, want_probs=True, want_logprobs=True)
+        for b in range(4):
+            k = pr[b] > 0
+            assert abs(np.exp(lp[b][k]).sum() - 1.0) < 1e-12
+            i, j = np.flatnonzero(k)[:2] if k.sum() > 1 else (np.flatnonzero(k)[0],) * 2
+            T32 = float(np.float32(T))  # the oracle takes T as float32
+            assert abs((lp[b, i] - lp[b, j]) - (float(x[b, i]) - float(x[b, j])) / T32) < 1e-12
+
+
+def check_row_seeds(O):
+    """Per-request race keys: row b with key seeds[b] draws what a call with
+    seed = seeds[b] draws for it, whatever the other rows' keys."""
+    rng = np.random.default_rng(3)
+    B, V = 6, 60
+    x = rng.normal(0.0, 1.0, (B, V)).astype(np.float32)
+    T, P = [1.0] * B, [0.95] * B
+    seeds = np.arange(100, 100 + B, dtype=np.uint64)
+    a, _ = O.sample(x, T, P, seed=0, step=3, seeds=seeds)
+    for b in range(B):
+        one, _ = O.sample(x, T, P, seed=int(seeds[b]), step=3, rows=[b])
+        assert one["token"][b] == a["token"][b], b
+    other = seeds.copy()
+    other[1:] += 1000
+    c, _ = O.sample(x, T, P, seed=0, step=3, seeds=other)
+    assert c["token"][0] == a["token"][0]
+    # The keys matter: 40 flat rows with distinct keys do not all draw what one
+    # common key draws.
+    flat = np.zeros((40, 30), dtype=np.float32)
+    d, _ = O.sample(flat, [1.0] * 40, [1.0] * 40, seed=5, step=0)
+    e, _ = O.sample(flat, [1.0] * 40, [1.0] * 40, seed=5, step=0, seeds=np.arange(40, dtype=np.uint64) + 9)
+    assert (d["token"] != e["token"]).any()
+
+
 ALL_FAST_CHECKS = [check_worked_examples, check_order_counterexample, check_special_cases, check_invariants,
-                   check_exp1, check_race_reproducible]
+                   check_exp1, check_race_reproducible, check_logprobs, check_row_seeds]

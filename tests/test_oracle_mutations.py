@@ -29,6 +29,13 @@ MUTATIONS = [
     ("philox counter layout", "uint32_t ctr[4] = {(uint32_t)(token >> 2), (uint32_t)row,",
      "uint32_t ctr[4] = {(uint32_t)row, (uint32_t)(token >> 2),"),
     ("uniform off by half", "double u = ((double)r + 0.5)", "double u = ((double)r + 1.0)"),
+    ("logprob not normalised", "if (keep[i]) lrow[i] = (r.x[i] - r.m) / Td - lse;",
+     "if (keep[i]) lrow[i] = (r.x[i] - r.m) / Td;"),
+    ("logprob untempered", "if (keep[i]) lrow[i] = (r.x[i] - r.m) / Td - lse;",
+     "if (keep[i]) lrow[i] = (r.x[i] - r.m) - lse;"),
+    ("logprob of every survivor", "if (keep[i]) lrow[i] = (r.x[i] - r.m) / Td - lse;",
+     "if (r.surv[i]) lrow[i] = (r.x[i] - r.m) / Td - lse;"),
+    ("row seed ignored", "const uint64_t row_seed = seeds ? seeds[b] : seed;", "const uint64_t row_seed = seed;"),
 ]
 
 

@@ -56,6 +56,14 @@ def test_race_reproducible(oracle_lib):
     P.check_race_reproducible(oracle_lib.default())
 
 
+def test_logprobs(oracle_lib):
+    P.check_logprobs(oracle_lib)
+
+
+def test_row_seeds(oracle_lib):
+    P.check_row_seeds(oracle_lib)
+
+
 def test_exp1(oracle_lib):
     P.check_exp1(oracle_lib.default())
 
