@@ -103,6 +103,19 @@ typedef struct nucleus_options {
                                     error).  For T > 0 rows the kept set is exactly
                                     {i : x_i finite and x_i >= out_min_kept_logit[b]};
                                     for greedy rows it is {out_token[b]}. */
+    /* Since version 210 (a caller built against an older header zero-fills
+     * them when it zero-initialises the struct): */
+    const uint64_t* seeds;       /* optional device [B]: per-request Philox keys; row b then
+                                    draws with key (lo, hi 32 bits of seeds[b]) instead of
+                                    the call's seed, so its draw does not depend on the rest
+                                    of the batch ("Top-p (Nucleus) Sampling, in depth",
+                                    "Logprobs, speculative decoding and reproducibility").
+                                    NULL: every row uses the call's seed. */
+    float* out_logprobs;         /* optional device [B, V]: log-probabilities of the same
+                                    processed distribution as out_probs (the same section):
+                                    (x_i - m)/T - ln S_keep on kept tokens, -inf outside the
+                                    nucleus; 0 / -inf for greedy rows; NaN on a row error.
+                                    Finite for kept tokens whose probability underflows. */
 } nucleus_options;
 
 /*

@@ -43,6 +43,8 @@ class _Options(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("out_min_kept_logit", ctypes.c_void_p),
+        ("seeds", ctypes.c_void_p),
+        ("out_logprobs", ctypes.c_void_p),
     ]
 
 
@@ -132,19 +134,23 @@ class SampleResult(NamedTuple):
     keep_count: torch.Tensor     # int32 [B]
     probs: Optional[torch.Tensor]     # float32 [B, V] or None
     min_kept_logit: Optional[torch.Tensor]  # float32 [B] or None
+    logprobs: Optional[torch.Tensor] = None  # float32 [B, V] or None
 
 
 def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, seed: int = 0, step: int = 0, *,
            want_probs: bool = False, want_min_kept: bool = False, out: Optional[SampleResult] = None,
            workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
-           single_workgroup: bool = False, split_rows: bool = False, row_race: bool = False) -> SampleResult:
+           single_workgroup: bool = False, split_rows: bool = False, row_race: bool = False,
+           seeds=None, want_logprobs: bool = False) -> SampleResult:
     """Sample one token per row of ``logits`` [B, V] (float32 or bfloat16 on a
     gfx950 device; rows may be strided, the last dimension must be dense).
 
     Launches on ``stream`` (default: the current stream) and returns without
     synchronising.  ``out`` may supply preallocated outputs; ``workspace`` a
     byte tensor of at least ``workspace_bytes(B, V, dtype)`` (by default one
-    is cached per device and stream).  ``single_workgroup`` runs every row
+    is cached per device and stream).  ``seeds`` (optional [B] integers)
+    gives every row its own Philox key; ``want_logprobs`` also returns the
+    log-probabilities of the processed distribution.  ``single_workgroup`` runs every row
     on one workgroup that re-reads the row; ``split_rows`` splits every row
     over workgroups whatever the batch size; ``row_race`` takes the
     large-batch path (a workgroup per row, the race spread over chunks)
@@ -164,12 +170,20 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     P = _vec(top_p, B, torch.float32, "top_p", dev)
     K = _vec(top_k, B, torch.int32, "top_k", dev)
     MP = _vec(min_p, B, torch.float32, "min_p", dev)
+    S = None
+    if seeds is not None:
+        # uint64 keys travel as their int64 bit patterns
+        S = torch.as_tensor([int(v) & (2**64 - 1) for v in torch.as_tensor(seeds).reshape(-1).tolist()],
+                            dtype=torch.uint64).view(torch.int64).to(dev).contiguous()
+        if S.numel() != B:
+            raise ValueError(f"seeds must have {B} elements")
     if out is None:
         out = SampleResult(
             torch.empty(B, dtype=torch.int32, device=dev),
             torch.empty(B, dtype=torch.int32, device=dev),
             torch.empty((B, V), dtype=torch.float32, device=dev) if want_probs else None,
             torch.empty(B, dtype=torch.float32, device=dev) if want_min_kept else None,
+            torch.empty((B, V), dtype=torch.float32, device=dev) if want_logprobs else None,
         )
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     flags = ((NUCLEUS_FLAG_SINGLE_WORKGROUP if single_workgroup else 0) | (NUCLEUS_FLAG_SPLIT_ROWS if split_rows else 0)
@@ -185,6 +199,8 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     opt.workspace = workspace.data_ptr() if (workspace is not None and need) else None
     opt.workspace_bytes = (workspace.numel() * workspace.element_size()) if (workspace is not None and need) else 0
     opt.out_min_kept_logit = out.min_kept_logit.data_ptr() if out.min_kept_logit is not None else None
+    opt.seeds = S.data_ptr() if S is not None else None
+    opt.out_logprobs = out.logprobs.data_ptr() if out.logprobs is not None else None
 
     def ptr(t):
         return None if t is None else t.data_ptr()

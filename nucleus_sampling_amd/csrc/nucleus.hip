@@ -118,7 +118,7 @@ bool aligned(const T* p)
 
 extern "C" {
 
-int nucleus_version(void) { return 200; }
+int nucleus_version(void) { return 210; }
 
 const char* nucleus_strerror(int code)
 {
@@ -159,7 +159,8 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     const size_t esz = dtype == NUCLEUS_F32 ? 4 : 2;
     if ((uintptr_t)logits % esz != 0 || !aligned(temperature) || !aligned(top_p) || (top_k && !aligned(top_k)) ||
         (min_p && !aligned(min_p)) || !aligned(out_token) || !aligned(out_keep_count) ||
-        (out_probs && !aligned(out_probs)) || (opt && opt->out_min_kept_logit && !aligned(opt->out_min_kept_logit)))
+        (out_probs && !aligned(out_probs)) || (opt && opt->out_min_kept_logit && !aligned(opt->out_min_kept_logit)) ||
+        (opt && opt->seeds && !aligned(opt->seeds)) || (opt && opt->out_logprobs && !aligned(opt->out_logprobs)))
         return NUCLEUS_EINVAL;
     const size_t need = path_workspace(path, B, V);
     if (need > 0 && (!opt || !opt->workspace || opt->workspace_bytes < need || (uintptr_t)opt->workspace % 256))
@@ -184,6 +185,8 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     p.out_count = out_keep_count;
     p.out_probs = out_probs;
     p.out_min_kept = opt ? opt->out_min_kept_logit : nullptr;
+    p.seeds = opt ? opt->seeds : nullptr;
+    p.out_logprobs = opt ? opt->out_logprobs : nullptr;
     const size_t vec_bytes = dtype == NUCLEUS_F32 ? 16 : 8;
     p.vec_in = ((uintptr_t)logits % vec_bytes == 0) && ((size_t)stride * esz) % vec_bytes == 0;
 
@@ -226,12 +229,12 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
             hipLaunchKernelGGL((row_kernel<kF32, true>), rows, dim3(kRowThreads), 0, s, p, rw);
             hipLaunchKernelGGL(race_kernel<kF32>, racers, dim3(kRaceThreads), 0, s, p, rw);
             hipLaunchKernelGGL(resolve_kernel<kF32>, rows, dim3(kRowThreads), 0, s, p, rw);
-            if (out_probs) hipLaunchKernelGGL(probs_kernel<kF32>, chunks, dim3(kRaceThreads), 0, s, p, pw);
+            if (out_probs || p.out_logprobs) hipLaunchKernelGGL(probs_kernel<kF32>, chunks, dim3(kRaceThreads), 0, s, p, pw);
         } else {
             hipLaunchKernelGGL((row_kernel<kBF16, true>), rows, dim3(kRowThreads), 0, s, p, rw);
             hipLaunchKernelGGL(race_kernel<kBF16>, racers, dim3(kRaceThreads), 0, s, p, rw);
             hipLaunchKernelGGL(resolve_kernel<kBF16>, rows, dim3(kRowThreads), 0, s, p, rw);
-            if (out_probs) hipLaunchKernelGGL(probs_kernel<kBF16>, chunks, dim3(kRaceThreads), 0, s, p, pw);
+            if (out_probs || p.out_logprobs) hipLaunchKernelGGL(probs_kernel<kBF16>, chunks, dim3(kRaceThreads), 0, s, p, pw);
         }
     } else {
         const RowWork none = {};

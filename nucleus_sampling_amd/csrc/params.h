@@ -21,6 +21,8 @@ struct Params {
     float* out_probs;         // [B, V] or null
     float* out_min_kept;      // [B] or null
     int vec_in;               // rows start 16-byte (f32) / 8-byte (bf16) aligned
+    const uint64_t* seeds;    // [B] per-row race keys, or null (every row uses seed_lo/hi)
+    float* out_logprobs;      // [B, V] or null
 };
 
 }  // namespace nucleus

@@ -467,7 +467,8 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     const int t = threadIdx.x;
     const int64_t esz = DT == kF32 ? 4 : 2;
     const void* rowp = (const char*)p.logits + b * p.stride * esz;
-    const bool want_probs = p.out_probs != nullptr;
+    use_row_key(p, b);
+    const bool want_probs = wants_dist(p);  // probabilities or log-probabilities
 
     // ---- pass 1: row max, NaN / +inf; for rows whose
     // need of a histogram the parameters alone decide (no min-p), also the
@@ -685,15 +686,25 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     write_outputs(p, b, st);
     if (!want_probs) return;
 
-    // ---- pass 4: renormalised probabilities
-    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kRowThreads>(model, st, sh.u.factor);
-    float* prow = p.out_probs + b * p.V;
+    // ---- pass 4: renormalised probabilities and / or log-probabilities
+    if (p.out_probs && st.mode != kModeError && st.mode != kModeGreedy)
+        prob_factors<kRowThreads>(model, st, sh.u.factor);
+    const LogNorm ln = log_norm(model, st);
+    float* prow = p.out_probs ? p.out_probs + b * p.V : nullptr;
+    float* lrow = p.out_logprobs ? p.out_logprobs + b * p.V : nullptr;
     const uint32_t V = (uint32_t)p.V;
     stream_row<DT, true, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
         float q[4];
+        if (prow) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q[j] = prob_of(st.mode, model, st, sh.u.factor, xs[j], i0 + j);
-        store_probs(prow, i0, V, q);
+            for (int j = 0; j < 4; ++j) q[j] = prob_of(st.mode, model, st, sh.u.factor, xs[j], i0 + j);
+            store_probs(prow, i0, V, q);
+        }
+        if (lrow) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) q[j] = logprob_of(st.mode, model, st, ln, xs[j], i0 + j);
+            store_probs(lrow, i0, V, q);
+        }
     });
 }
 
@@ -777,6 +788,7 @@ __global__ __launch_bounds__(kRaceThreads, 4) void race_kernel(Params p, RowWork
     };
     auto rowp_of = [&](int64_t rb) { return (const void*)((const char*)p.logits + rb * p.stride * esz); };
     auto open_item = [&](int64_t rb) {
+        use_row_key(p, rb);
         ps = rw.st + rb;
         const uint32_t mode = uniform(ps->mode);
         model = uniform(*(const RowModel*)ps->model);
@@ -856,6 +868,7 @@ __global__ __launch_bounds__(kRowThreads) void resolve_kernel(Params p, RowWork 
     __shared__ ResolveKShared sh;
     const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
+    use_row_key(p, b);
     RowPathState* ps = rw.st + b;
     RowState st = published_state(ps);
     const RowModel model = uniform(*(const RowModel*)ps->model);
@@ -935,15 +948,24 @@ __global__ __launch_bounds__(kRaceThreads) void probs_kernel(Params p, RowWork r
     st.cut_key = uniform(ps->cut_key);
     st.s_keep = uniform(ps->s_keep);
     const RowModel model = uniform(*(const RowModel*)ps->model);
-    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kRaceThreads>(model, st, factor);
-    float* prow = p.out_probs + b * p.V;
+    if (p.out_probs && st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kRaceThreads>(model, st, factor);
+    const LogNorm ln = log_norm(model, st);
+    float* prow = p.out_probs ? p.out_probs + b * p.V : nullptr;
+    float* lrow = p.out_logprobs ? p.out_logprobs + b * p.V : nullptr;
     const uint32_t V = (uint32_t)p.V;
     load_groups<DT, true, kRaceThreads, kRaceUnroll>(
         p, rowp, cid.chunk * (uint32_t)(kRaceChunk / 4), threadIdx.x, [&](uint32_t i0, const float* xs) {
             float q[4];
+            if (prow) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) q[j] = prob_of(st.mode, model, st, factor, xs[j], i0 + j);
-            store_probs(prow, i0, V, q);
+                for (int j = 0; j < 4; ++j) q[j] = prob_of(st.mode, model, st, factor, xs[j], i0 + j);
+                store_probs(prow, i0, V, q);
+            }
+            if (lrow) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) q[j] = logprob_of(st.mode, model, st, ln, xs[j], i0 + j);
+                store_probs(lrow, i0, V, q);
+            }
         });
 }
 

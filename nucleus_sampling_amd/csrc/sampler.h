@@ -286,6 +286,21 @@ struct RowParams {
     int K;
 };
 
+// Row b's race key: its own seed when the call gives one per row (a
+// per-request seed, "Top-p (Nucleus) Sampling, in depth", "Logprobs,
+// speculative decoding and reproducibility").
+__device__ __forceinline__ void use_row_key(Params& p, int64_t b)
+{
+    if (p.seeds) {
+        const uint64_t s = p.seeds[b];
+        p.seed_lo = (uint32_t)s;
+        p.seed_hi = (uint32_t)(s >> 32);
+    }
+}
+
+// Whether the call wants the renormalised distribution in any form.
+__device__ __forceinline__ bool wants_dist(const Params& p) { return p.out_probs || p.out_logprobs; }
+
 __device__ __forceinline__ RowParams row_params(const Params& p, int64_t b)
 {
     RowParams r;
@@ -663,6 +678,49 @@ __device__ __forceinline__ void prob_factors(const RowModel& r, const RowState& 
     __syncthreads();
 }
 
+// ln S_keep with S_keep = sum of exp((x_i - m)/T) over the kept tokens, split
+// into two floats.  s_keep is held in the bin model's units (weights measured
+// from the lattice point (A + 1)/s above the max, a common factor
+// exp((m s - A - 1) w) below the true weights), so
+// ln S_keep = ln s_keep + (A + 1 - m s) w.
+struct LogNorm {
+    float hi, lo;
+};
+
+__device__ __forceinline__ LogNorm log_norm(const RowModel& r, const RowState& st)
+{
+#pragma clang fp contract(off)
+    LogNorm n;
+    n.hi = n.lo = 0.0f;
+    if (st.mode == kModeError || st.mode == kModeGreedy || !(st.s_keep > 0.0)) return n;
+    const double l = log(st.s_keep) + ((r.A + 1.0) - (double)r.m * r.L.s) * r.L.w;
+    n.hi = (float)l;
+    n.lo = (float)(l - (double)n.hi);
+    return n;
+}
+
+// Log-probability of token i (logit x) in the renormalised kept distribution
+// (the processed distribution: -inf outside the nucleus, "Top-p (Nucleus)
+// Sampling, in depth", "Logprobs, speculative decoding and reproducibility"):
+// (x - m)/T - ln S_keep, with (x - m)/T carried to about one extra word as in
+// tempered_weight; 0 / -inf on greedy rows, NaN on error rows.
+__device__ __forceinline__ float logprob_of(uint32_t mode, const RowModel& r, const RowState& st, const LogNorm& n,
+                                            float x, int64_t i)
+{
+#pragma clang fp contract(off)
+    if (mode == kModeError) return __builtin_nanf("");
+    if (mode == kModeGreedy) return (uint32_t)i == st.token ? 0.0f : -INFINITY;
+    if (!(survives(r, x) && order_key(x) >= st.cut_key)) return -INFINITY;
+    if (r.invT == 0.0f) return -n.hi - n.lo;  // T = +inf: every kept token weighs the same
+    const float s = x - r.m;
+    const float q = s * r.invT;
+    const float bb = s - x;
+    const float err = (x - (s - bb)) + (-r.m - bb);  // x - m == s + err exactly
+    const float rem = fmaf(-q, r.T, s);              // s - q*T exactly
+    const float lo = (rem + err) * r.invT;
+    return (q - n.hi) + (lo - n.lo);
+}
+
 __device__ __forceinline__ float prob_of(uint32_t mode, const RowModel& r, const RowState& st, const float* factor,
                                          float x, int64_t i)
 {
@@ -761,7 +819,8 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
     const int64_t base = (int64_t)chunk * kChunk;
     RowCtl* ctl = wk.ctl + b;
     const int64_t wg = b * K + chunk;
-    const bool want_probs = p.out_probs != nullptr;
+    use_row_key(p, b);
+    const bool want_probs = wants_dist(p);  // probabilities or log-probabilities
 
     // ---- load the chunk into registers (token of x[4v+j]: lane0 + 1024 v + j)
     float x[kEPT];
@@ -1033,15 +1092,19 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
         if (!want_probs) return;
         // The resolving workgroup re-reads its chunk so that its registers are
         // free for the resolver; the others write from registers below.
-        if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kThreads>(model, st, sh.u.factor);
-        float* prow = p.out_probs + b * p.V;
+        if (p.out_probs && st.mode != kModeError && st.mode != kModeGreedy)
+            prob_factors<kThreads>(model, st, sh.u.factor);
+        const LogNorm ln = log_norm(model, st);
         for (int v = 0; v < kEPT / 4; ++v) {
             const int64_t i0 = base + ((int64_t)v * kThreads + t) * 4;
             float xs[4];
             load4<DT>(rowp, i0, p.V, p.vec_in, xs);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (i0 + j < p.V) prow[i0 + j] = prob_of(st.mode, model, st, sh.u.factor, xs[j], i0 + j);
+                if (i0 + j < p.V) {
+                    if (p.out_probs) p.out_probs[b * p.V + i0 + j] = prob_of(st.mode, model, st, sh.u.factor, xs[j], i0 + j);
+                    if (p.out_logprobs) p.out_logprobs[b * p.V + i0 + j] = logprob_of(st.mode, model, st, ln, xs[j], i0 + j);
+                }
         }
         return;
     }
@@ -1053,15 +1116,20 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
     read_state(ctl, sh.st);
     st = uniform(sh.st);
 
-    // ---- probabilities of this chunk, from registers
-    if (st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kThreads>(model, st, sh.u.factor);
-    float* prow = p.out_probs + b * p.V;
+    // ---- probabilities / log-probabilities of this chunk, from registers
+    if (p.out_probs && st.mode != kModeError && st.mode != kModeGreedy) prob_factors<kThreads>(model, st, sh.u.factor);
+    const LogNorm ln = log_norm(model, st);
 #pragma unroll
     for (int v = 0; v < kEPT / 4; ++v) {
         const uint32_t i0 = lane0 + (uint32_t)v * (kThreads * 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (i0 + j < (uint32_t)p.V) prow[i0 + j] = prob_of(st.mode, model, st, sh.u.factor, x[4 * v + j], i0 + j);
+            if (i0 + j < (uint32_t)p.V) {
+                if (p.out_probs)
+                    p.out_probs[b * p.V + i0 + j] = prob_of(st.mode, model, st, sh.u.factor, x[4 * v + j], i0 + j);
+                if (p.out_logprobs)
+                    p.out_logprobs[b * p.V + i0 + j] = logprob_of(st.mode, model, st, ln, x[4 * v + j], i0 + j);
+            }
     }
 }
 

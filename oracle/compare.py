@@ -49,6 +49,7 @@ class Report:
     near_1e6: int = 0
     near_1e7: int = 0
     max_prob_ratio: float = 0.0
+    max_logprob_ratio: float = 0.0
     failures: list = field(default_factory=list)
 
     def ok(self) -> bool:
@@ -58,22 +59,39 @@ class Report:
         return (f"rows={self.rows} exact={self.exact} greedy={self.greedy} row_errors={self.errors_ok} "
                 f"exempt_mass={self.exempt_mass} (exact {self.exempt_mass_exact}) exempt_race={self.exempt_race} "
                 f"exempt_minp={self.exempt_minp} band1e-6={self.near_1e6} band1e-7={self.near_1e7} "
-                f"max|dp|/(1e-6+1e-5p)={self.max_prob_ratio:.3g} failures={len(self.failures)}")
+                f"max|dp|/(1e-6+1e-5p)={self.max_prob_ratio:.3g} "
+                f"max|dlp|/(1e-6+1e-6|lp|)={self.max_logprob_ratio:.3g} failures={len(self.failures)}")
 
 
 def _prob_ratio(g, o):
     return float(np.max(np.abs(g - o) / (1e-6 + 1e-5 * o))) if g.size else 0.0
 
 
+# Log-probabilities: the GPU forms (x - m)/T to about 2^-48 relative and
+# ln S_keep from the bin model's sums (about 1e-7 relative in S_keep, 1e-7
+# absolute in its log), then rounds to float32 (2^-24 |lp| per operation):
+# |gpu - oracle| <= 1e-6 + 1e-6 |lp| holds with margin.  Both sides must put
+# -inf on exactly the same tokens.
+def _logprob_ratio(g, o):
+    fin = np.isfinite(o)
+    if not np.array_equal(fin, np.isfinite(g)) or not np.array_equal(np.isneginf(o), np.isneginf(g)):
+        return float("inf")
+    if not fin.any():
+        return 0.0
+    return float(np.max(np.abs(g[fin] - o[fin]) / (1e-6 + 1e-6 * np.abs(o[fin]))))
+
+
 def compare(logits, temperature, top_p, top_k, min_p, seed, step, gpu_token, gpu_count, gpu_min_kept,
             oracle_rows, gpu_probs=None, oracle_probs=None, prob_rows=None, batch_rows=None, O=None,
-            max_failures=20) -> Report:
+            max_failures=20, seeds=None, gpu_logprobs=None, oracle_logprobs=None) -> Report:
     """Compare GPU outputs with oracle results.
 
     logits: host [B, V] (float32 or uint16 bf16 bits) as given to both sides.
     gpu_*: host arrays [B]; oracle_rows: ROW_DTYPE [B].
-    gpu_probs / oracle_probs: optional [R, V] for the rows listed in prob_rows.
+    gpu_probs / oracle_probs, gpu_logprobs / oracle_logprobs: optional [R, V]
+    for the rows listed in prob_rows.
     batch_rows: the Philox row index of each row (defaults to 0..B-1).
+    seeds: optional per-row race keys (row b then uses seeds[b], not seed).
     """
     O = O or _default_oracle()
     B = logits.shape[0]
@@ -98,8 +116,12 @@ def compare(logits, temperature, top_p, top_k, min_p, seed, step, gpu_token, gpu
         j = prob_index.get(b)
         gp = gpu_probs[j] if (j is not None and gpu_probs is not None) else None
         op = oracle_probs[j] if (j is not None and oracle_probs is not None) else None
+        gl = gpu_logprobs[j] if (j is not None and gpu_logprobs is not None) else None
+        ol = oracle_logprobs[j] if (j is not None and oracle_logprobs is not None) else None
+        sb = int(seeds[b]) if seeds is not None else seed
         if o["status"] == 1:
             good = gt == -1 and gc == 0 and (gm is None or math.isnan(gm)) and (gp is None or not gp.any())
+            good &= gl is None or bool(np.all(np.isnan(gl)))
             if good:
                 rep.errors_ok += 1
             else:
@@ -110,6 +132,8 @@ def compare(logits, temperature, top_p, top_k, min_p, seed, step, gpu_token, gpu
             good = gt == o["token"] and gc == 1 and (gm is None or gm == o["min_kept_logit"])
             if gp is not None:
                 good &= gp[gt] == 1.0 and np.count_nonzero(gp) == 1
+            if gl is not None:
+                good &= gl[gt] == 0.0 and int(np.isneginf(gl).sum()) == len(gl) - 1
             if good:
                 rep.exact += 1
             else:
@@ -134,8 +158,8 @@ def compare(logits, temperature, top_p, top_k, min_p, seed, step, gpu_token, gpu
             if gm is None:
                 fail(b, "mass-band row needs the GPU's min kept logit")
                 continue
-            ev, eprobs = O.eval_cut(logits[b], rid[b], T[b], P[b], K[b], MP[b], seed, step, gm,
-                                    want_probs=gp is not None)
+            ev, eprobs = O.eval_cut(logits[b], rid[b], T[b], P[b], K[b], MP[b], sb, step, gm,
+                                    want_probs=gp is not None or gl is not None)
             if not (ev["a_cut"] < p + MASS_BAND and ev["m_cut"] >= p - MASS_BAND):
                 fail(b, f"inadmissible cut {gm}: A={ev['a_cut']:.9f} M={ev['m_cut']:.9f} p={p:.9f}")
                 continue
@@ -144,6 +168,12 @@ def compare(logits, temperature, top_p, top_k, min_p, seed, step, gpu_token, gpu
                 continue
             want_tok, s1 = int(ev["token"]), float(ev["race_s1"])
             ref_probs = eprobs
+            # (the cut's distribution in the log domain; the workloads' kept
+            # probabilities are far from underflow)
+            ref_lp = None
+            if eprobs is not None:
+                with np.errstate(divide="ignore"):
+                    ref_lp = np.where(eprobs > 0, np.log(np.where(eprobs > 0, eprobs, 1.0)), -np.inf)
             if same_set:
                 rep.exempt_mass_exact += 1
         else:
@@ -152,9 +182,10 @@ def compare(logits, temperature, top_p, top_k, min_p, seed, step, gpu_token, gpu
                 continue
             want_tok, s1 = int(o["token"]), float(o["race_s1"])
             ref_probs = op
+            ref_lp = ol
         if gt != want_tok:
             margin = float(o["race_margin"]) if not exempt_mass else None
-            sg = O.race_score(logits[b], rid[b], T[b], seed, step, gt) if 0 <= gt < logits.shape[1] else -1.0
+            sg = O.race_score(logits[b], rid[b], T[b], sb, step, gt) if 0 <= gt < logits.shape[1] else -1.0
             kept_ok = 0 <= gt < logits.shape[1] and _kept(logits[b], gt, gm)
             if kept_ok and sg >= s1 * (1.0 - RACE_BAND):
                 rep.exempt_race += 1
@@ -168,6 +199,11 @@ def compare(logits, temperature, top_p, top_k, min_p, seed, step, gpu_token, gpu
             rep.max_prob_ratio = max(rep.max_prob_ratio, r)
             if r > 1.0:
                 fail(b, f"probabilities off by {r:.3g} x tolerance")
+        if gl is not None and ref_lp is not None:
+            r = _logprob_ratio(gl.astype(np.float64), ref_lp)
+            rep.max_logprob_ratio = max(rep.max_logprob_ratio, r)
+            if r > 1.0:
+                fail(b, f"log-probabilities off by {r:.3g} x tolerance (or -inf on different tokens)")
     return rep
 
 

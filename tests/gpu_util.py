@@ -37,17 +37,20 @@ def run_gpu(w, step=0, want_probs=False, logits_dev=None, seed=None):
     return res.token.cpu().numpy(), res.keep_count.cpu().numpy(), res.min_kept_logit.cpu().numpy(), probs
 
 
-def oracle_and_compare(w, tok, cnt, mk, step=0, gpu_probs=None, prob_rows=None, threads=16, seed=None):
+def oracle_and_compare(w, tok, cnt, mk, step=0, gpu_probs=None, prob_rows=None, threads=16, seed=None,
+                       seeds=None, gpu_logprobs=None):
     import oracle
     from oracle.compare import compare
 
     s = w["seed"] if seed is None else seed
     rows, oprobs = oracle.sample(w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], seed=s,
-                                 step=step, threads=threads)
-    op = None
+                                 step=step, threads=threads, seeds=seeds)
+    op = ol = None
     if prob_rows is not None:
-        _, op = oracle.sample(w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], seed=s,
-                              step=step, rows=prob_rows, want_probs=True, threads=threads)
+        _, op, ol = oracle.sample(w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], seed=s,
+                                  step=step, rows=prob_rows, want_probs=True, threads=threads, seeds=seeds,
+                                  want_logprobs=True)
     rep = compare(w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], s, step, tok, cnt, mk,
-                  rows, gpu_probs=gpu_probs, oracle_probs=op, prob_rows=prob_rows)
+                  rows, gpu_probs=gpu_probs, oracle_probs=op, prob_rows=prob_rows, seeds=seeds,
+                  gpu_logprobs=gpu_logprobs, oracle_logprobs=ol)
     return rep, rows

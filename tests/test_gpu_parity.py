@@ -22,7 +22,8 @@ pytestmark = pytest.mark.gpu
 PATHS = [None, "single", "split", "rows"]
 
 
-def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None, path=None):
+def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None, path=None, seeds=None,
+         want_logprobs=False):
     import torch
 
     import nucleus_sampling_amd as ns
@@ -30,13 +31,18 @@ def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None, path=N
     lg = device_logits(w["logits"], w["dtype"]) if lg is None else lg
     res = ns.sample(lg, w["temperature"], w["top_p"], w["top_k"], w["min_p"],
                     seed=w["seed"] if seed is None else seed, step=step, want_probs=want_probs, want_min_kept=True,
-                    single_workgroup=path == "single", split_rows=path == "split", row_race=path == "rows")
+                    single_workgroup=path == "single", split_rows=path == "split", row_race=path == "rows",
+                    seeds=seeds, want_logprobs=want_logprobs)
     torch.cuda.synchronize()
-    probs = None
-    if want_probs:
+    probs = logprobs = None
+    if want_probs or want_logprobs:
         idx = torch.as_tensor(list(prob_rows), dtype=torch.long, device=lg.device)
-        probs = res.probs.index_select(0, idx).cpu().numpy()
-    return res.token.cpu().numpy(), res.keep_count.cpu().numpy(), res.min_kept_logit.cpu().numpy(), probs
+        if want_probs:
+            probs = res.probs.index_select(0, idx).cpu().numpy()
+        if want_logprobs:
+            logprobs = res.logprobs.index_select(0, idx).cpu().numpy()
+    out = (res.token.cpu().numpy(), res.keep_count.cpu().numpy(), res.min_kept_logit.cpu().numpy(), probs)
+    return out + (logprobs,) if want_logprobs else out
 
 
 PROB_ROWS = {1: list(range(15)), 2: [0, 1, 2, 3, 17, 40, 63], 3: [0, 1, 2, 3, 100, 255], 4: [0, 1, 2, 3, 9, 200],
@@ -287,3 +293,35 @@ def test_crossing_bin_overflow(dtype):
         b = _gpu(w, want_probs=True, prob_rows=range(B), path=path)
         assert all(np.array_equal(np.asarray(x).view(np.uint32), np.asarray(y).view(np.uint32))
                    for x, y in zip(a, b)), path
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_logprobs_and_row_seeds(n):
+    """Per-request race keys and the processed distribution's
+    log-probabilities (-inf outside the nucleus) against the oracle; every
+    path gives the same bits."""
+    w = workloads.make(n)
+    B = w["B"]
+    seeds = (np.arange(B, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15) + np.uint64(12345)).astype(np.uint64)
+    rows = PROB_ROWS[n]
+    say(f"workload {n}: per-row keys and log-probabilities for rows {rows}")
+    first = _gpu(w, want_probs=True, prob_rows=rows, seeds=seeds, want_logprobs=True)
+    tok, cnt, mk, probs, lps = first
+    rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=rows, seeds=seeds, gpu_logprobs=lps)
+    say(f"workload {n} keys + logprobs: {rep.summary()}")
+    assert rep.ok(), rep.failures
+    # The probabilities and the log-probabilities describe one distribution.
+    ok_rows = ~np.isnan(lps).all(axis=1)  # (row errors are NaN throughout)
+    with np.errstate(over="ignore"):
+        d = np.abs(np.exp(lps[ok_rows].astype(np.float64)) - probs[ok_rows])
+        assert np.all(d <= 1e-6 + 1e-5 * probs[ok_rows])
+    # The keys matter: sampled rows draw differently from the call's one seed.
+    base = _gpu(w)
+    sampled = (w["temperature"] > 0) & (cnt > 1)
+    if sampled.sum() >= 8:
+        assert (base[0][sampled] != tok[sampled]).any()
+    for path in ("single", "split", "rows"):
+        say(f"workload {n}: keys + logprobs on path {path}")
+        other = _gpu(w, want_probs=True, prob_rows=rows, seeds=seeds, want_logprobs=True, path=path)
+        assert all(np.array_equal(np.asarray(x).view(np.uint32), np.asarray(y).view(np.uint32))
+                   for x, y in zip(first, other)), path
