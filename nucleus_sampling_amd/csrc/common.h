@@ -47,8 +47,19 @@ __device__ __forceinline__ float bf16_to_float(uint16_t h)
 // as 1, 2, 3", SC'11): per round, words 0 and 2 are multiplied by the two
 // round multipliers; the new state is (hi1^c1^k0, lo1, hi0^c3^k1, lo0); the
 // key advances by the two Weyl constants between rounds.  The key is
-// wave-uniform here, so its schedule lives in scalar registers.
+// wave-uniform at every call, so its schedule lives in scalar registers, and
+// each round's two three-way XORs take one instruction each.
 // ---------------------------------------------------------------------------
+
+// a ^ b ^ k for a wave-uniform k: gfx950's three-input bitwise operation with
+// the truth table of XOR (0x96: set where an odd number of inputs is set).
+__device__ __forceinline__ uint32_t xor3_uniform(uint32_t a, uint32_t b, uint32_t k)
+{
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+    return r;
+}
+
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1)
 {
 #pragma unroll
@@ -57,7 +68,7 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;
         const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
         const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        c = make_uint4(xor3_uniform(hi1, c.y, k0), lo1, xor3_uniform(hi0, c.w, k1), lo0);
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
