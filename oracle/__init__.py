@@ -33,6 +33,13 @@ ROW_DTYPE = np.dtype(
     ],
     align=True,
 )
+REJ_DTYPE = np.dtype(
+    [
+        ("status", np.int32), ("token", np.int32), ("rounds", np.int32), ("greedy", np.int32),
+        ("band", np.float64), ("race_margin", np.float64),
+    ],
+    align=True,
+)
 CUT_DTYPE = np.dtype(
     [
         ("status", np.int32), ("token", np.int32), ("keep_count", np.int32), ("pad", np.int32),
@@ -74,6 +81,9 @@ class Oracle:
         L.oracle_sample_ex.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, u64, vp, u64, i64, i64, vp,
                                        vp, vp]
         L.oracle_sample_ex.restype = ctypes.c_int
+        L.oracle_sample_rejection.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, u64, vp, u64, i32, i64,
+                                              i64, vp]
+        L.oracle_sample_rejection.restype = ctypes.c_int
         L.oracle_eval_cut.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_float, ctypes.c_float, i32,
                                       ctypes.c_float, u64, u64, ctypes.c_double, vp, vp]
         L.oracle_eval_cut.restype = ctypes.c_int
@@ -142,6 +152,38 @@ class Oracle:
             return out, probs, logprobs
         return out, probs
 
+    def sample_rejection(self, logits, temperature, top_p, min_p=None, seed=0, step=0, seeds=None,
+                         max_rounds=64, threads=1):
+        """The rejection sampler (oracle_sample_rejection) on a [B, V] batch.
+        Returns a structured array of REJ_DTYPE of length B."""
+        logits = np.ascontiguousarray(logits)
+        B, V = logits.shape
+        dt = _dtype_code(logits)
+        T = np.ascontiguousarray(temperature, dtype=np.float32).reshape(B)
+        P = np.ascontiguousarray(top_p, dtype=np.float32).reshape(B)
+        MP = None if min_p is None else np.ascontiguousarray(min_p, dtype=np.float32).reshape(B)
+        S = None if seeds is None else np.ascontiguousarray(seeds, dtype=np.uint64).reshape(B)
+        out = np.zeros(B, dtype=REJ_DTYPE)
+        L = self.L
+
+        def run(span):
+            rc = L.oracle_sample_rejection(_ptr(logits), dt, B, V, V, _ptr(T), _ptr(P), _ptr(MP),
+                                           ctypes.c_uint64(seed), _ptr(S), ctypes.c_uint64(step), int(max_rounds),
+                                           span[0], span[1], _ptr(out))
+            if rc != 0:
+                raise ValueError("oracle_sample_rejection rejected its arguments")
+
+        n = max(1, min(threads, B))
+        edges = np.linspace(0, B, n + 1).astype(np.int64)
+        spans = [(int(edges[j]), int(edges[j + 1])) for j in range(n) if edges[j + 1] > edges[j]]
+        if len(spans) > 1:
+            with ThreadPoolExecutor(len(spans)) as ex:
+                list(ex.map(run, spans))
+        else:
+            for sp in spans:
+                run(sp)
+        return out
+
     def eval_cut(self, logits_row, row, temperature, top_p, top_k, min_p, seed, step, cut, want_probs=False):
         """Judge a keep threshold chosen elsewhere on one row (see oracle_eval_cut)."""
         logits_row = np.ascontiguousarray(logits_row)
@@ -207,6 +249,10 @@ def default() -> Oracle:
 
 def sample(*a, **k):
     return default().sample(*a, **k)
+
+
+def sample_rejection(*a, **k):
+    return default().sample_rejection(*a, **k)
 
 
 def eval_cut(*a, **k):

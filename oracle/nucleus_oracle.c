@@ -523,3 +523,122 @@ double oracle_race_score(const void* logits, int dtype, int64_t V, int64_t row_o
     double e = exp((x - m) / (double)temperature);
     return e / oracle_exp1(oracle_noise_word(seed, step, row, token));
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sort-free top-p by rejection ("Top-p (Nucleus) Sampling, in depth",       */
+/* "Sort-free top-p by rejection sampling"): a second way to draw from the   */
+/* same kept distribution, with no sort and no cut.                          */
+/* ------------------------------------------------------------------------ */
+
+/* Result of the rejection sampler for one row. */
+typedef struct {
+    int32_t status;      /* 0 = ok, 1 = row error, 2 = no token accepted within max_rounds */
+    int32_t token;       /* accepted id; -1 on a row error or with no acceptance */
+    int32_t rounds;      /* proposal rounds run (0 for greedy and error rows) */
+    int32_t greedy;      /* 1 when T <= 0 */
+    double band;         /* min over the rounds' acceptance tests of |A(t)/S - p| (+inf if none was close) */
+    double race_margin;  /* min over the rounds' proposal races of (s1 - s2)/s1 (1 for a lone proposal) */
+} oracle_rej_row;
+
+/*
+ * Rows [r0, r1) of a [B, V] batch by rejection.  Per row, with the same
+ * validation, greedy rule, weights e_i and min-p survivors as oracle_sample
+ * (top-k is not part of this variant), S = sum of e over the survivors:
+ *
+ *   the pivot starts below every logit.  Round r draws a proposal t among
+ *   the finite tokens strictly above the pivot, with probability
+ *   proportional to e: the exponential race argmax e_i / E_i over them,
+ *   lowest index on ties, with the row's noise words E_i (the same words as
+ *   oracle_sample).  t is accepted iff it survives min-p and either it is in
+ *   the top level (always kept) or p > 0 and the survivor mass strictly
+ *   above it, A(t), is below p S (the order-free top-p rule; p <= 0 keeps the
+ *   top level only).  Otherwise t and every token at or below it are out: the
+ *   pivot becomes x_t and the next round draws again.
+ *
+ * Reusing the words in every round is a valid draw: in arrival-time form
+ * (token i arrives at E_i / e_i, exponential with rate e_i) the race's
+ * winner is the first arrival, and given that the first arrivals so far were
+ * rejected tokens, the remaining tokens' waiting times are again independent
+ * exponentials with the same rates (memorylessness), so each round's
+ * proposal is proportional to e among the tokens above the pivot.  It also
+ * means the accepted token is the first kept token to arrive: exactly
+ * oracle_sample's token.  The kept set is a top set of levels above every
+ * pivot, and every round raises the pivot, so a row needs at most one round
+ * per distinct level.  rows_out[b] receives row b's result.  Returns 0, or
+ * -1 on bad arguments.
+ */
+int oracle_sample_rejection(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride,
+                            const float* temperature, const float* top_p, const float* min_p, uint64_t seed,
+                            const uint64_t* seeds, uint64_t step, int32_t max_rounds, int64_t r0, int64_t r1,
+                            oracle_rej_row* rows_out)
+{
+    if (V < 1 || B < 0 || r0 < 0 || r1 > B || stride < V || max_rounds < 1 ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return -1;
+    uint8_t* prop = (uint8_t*)malloc((size_t)V);
+    for (int64_t b = r0; b < r1; ++b) {
+        oracle_rej_row* o = &rows_out[b];
+        memset(o, 0, sizeof(*o));
+        o->band = INFINITY;
+        o->race_margin = 1.0;
+        const uint64_t key = seeds ? seeds[b] : seed;  /* the row's race key */
+        const float T = temperature[b], P = top_p[b], MP = min_p ? min_p[b] : 0.0f;
+        row_prep r;
+        prep_row(logits, dtype, V, b * stride, T, P, 0, MP, &r);
+        if (r.err) {
+            o->status = 1;
+            o->token = -1;
+            prep_free(&r);
+            continue;
+        }
+        if (r.greedy) {
+            o->greedy = 1;
+            o->token = (int32_t)r.greedy_token;
+            prep_free(&r);
+            continue;
+        }
+        double S = 0.0;
+        for (int64_t i = 0; i < V; ++i)
+            if (r.surv[i]) S += r.e[i];
+        const double Pd = (double)P;
+        double pivot = -INFINITY;
+        o->status = 2;
+        o->token = -1;
+        o->rounds = max_rounds;
+        for (int32_t round = 1; round <= max_rounds; ++round) {
+            int64_t n_prop = 0;
+            for (int64_t i = 0; i < V; ++i) {
+                prop[i] = r.x[i] > -INFINITY && r.x[i] > pivot;
+                n_prop += prop[i];
+            }
+            double s1, s2;
+            const int64_t t = race(&r, prop, V, key, step, b, &s1, &s2);
+            const double margin = n_prop > 1 ? (s1 - s2) / s1 : 1.0;
+            if (margin < o->race_margin) o->race_margin = margin;
+            const double xt = r.x[t];
+            double A = 0.0;
+            for (int64_t i = 0; i < V; ++i)
+                if (r.surv[i] && r.x[i] > xt) A += r.e[i];
+            int accept = 0;
+            if (r.surv[t]) {
+                if (xt == r.m) {
+                    accept = 1;
+                } else if (Pd > 0.0) {
+                    accept = A < Pd * S;
+                    const double d = fabs(A / S - Pd);
+                    if (d < o->band) o->band = d;
+                }
+            }
+            if (accept) {
+                o->status = 0;
+                o->token = (int32_t)t;
+                o->rounds = round;
+                break;
+            }
+            pivot = xt;
+        }
+        prep_free(&r);
+    }
+    free(prop);
+    return 0;
+}

@@ -455,5 +455,152 @@ def check_row_seeds(O):
     assert (d["token"] != e["token"]).any()
 
 
+
+
+# --------------------------------------------------------------------------
+# The rejection sampler ("Top-p (Nucleus) Sampling, in depth", "Sort-free
+# top-p by rejection sampling")
+# --------------------------------------------------------------------------
+def rejection_exact(x, T, p, mp):
+    """Exact law of the pivot process on a tiny row, by recursion over pivots
+    (independent of the oracle): a proposal is drawn proportionally to e among
+    the finite tokens above the pivot; it is accepted iff it survives min-p and
+    is in the top level or its survivor mass strictly above is < p S;
+    otherwise the pivot moves to it.  Returns (accepted-token distribution,
+    expected rounds, expected squared rounds)."""
+    x = np.asarray(x, dtype=np.float64)
+    fin = x > -np.inf
+    m = x[fin].max()
+    e = np.where(fin, np.exp(np.where(fin, x - m, 0.0) / T), 0.0)
+    surv = fin & ~(e < min(mp, 1.0)) if mp > 0 else fin.copy()
+    S = e[surv].sum()
+
+    def accepted(t):
+        if not surv[t]:
+            return False
+        if x[t] == m:
+            return True
+        return p > 0 and e[surv & (x > x[t])].sum() < p * S
+
+    memo = {}
+
+    def go(pivot):
+        if pivot in memo:
+            return memo[pivot]
+        props = np.nonzero(fin & (x > pivot))[0]
+        W = e[props].sum()
+        dist = np.zeros(len(x))
+        r1, r2 = 1.0, 1.0
+        for t in props:
+            q = e[t] / W
+            if accepted(t):
+                dist[t] += q
+            else:
+                d, a1, a2 = go(float(x[t]))
+                dist += q * d
+                r1 += q * a1          # rounds = 1 + R'
+                r2 += q * (2 * a1 + a2)  # E[(1 + R')^2] - 1 over this branch
+        memo[pivot] = (dist, r1, r2)
+        return memo[pivot]
+
+    return go(-np.inf)
+
+
+def check_rejection_pages(O):
+    """The pages' rejection run: 40,000 draws of the six-token example at
+    p = 0.9 land on the renormalised nucleus and take about 1.09 rounds."""
+    for case in golden()["rejection"]:
+        x = np.asarray(case["logits"], dtype=np.float32)
+        n, k = case["n"], len(case["target"])
+        dist, r1, r2 = rejection_exact(x, case["T"], case["p"], 0.0)
+        # The exact law is the renormalised nucleus the pages print.
+        assert np.abs(dist[:k] - case["target"]).max() < 5e-5 and dist[k:].sum() == 0.0, dist
+        assert abs(r1 - case["printed_rounds_mean"]) < 0.005, r1
+        for got, want in zip(case["printed_freqs"], case["target"]):
+            assert abs(got - want) <= 5 * math.sqrt(want * (1 - want) / n) + 1e-3
+        out = O.sample_rejection(np.tile(x, (n, 1)), np.full(n, case["T"]), np.full(n, case["p"]),
+                                 seed=2024, step=0)
+        assert (out["status"] == 0).all()
+        f = np.bincount(out["token"], minlength=len(x)) / n
+        assert f[k:].sum() == 0.0, f
+        for got, want in zip(f[:k], dist[:k]):
+            assert abs(got - want) <= 5 * math.sqrt(want * (1 - want) / n) + 1e-3, (f, dist)
+        sd = math.sqrt(max(r2 - r1 * r1, 0.0))
+        assert abs(out["rounds"].mean() - r1) <= 5 * sd / math.sqrt(n) + 1e-3, (out["rounds"].mean(), r1)
+
+
+def check_rejection_law(O, cases=24, n=12000, seed=91):
+    """Tiny random rows (ties, -inf padding, min-p, p <= 0, p >= 1): the
+    oracle's accepted-token frequencies and mean rounds match the exact law of
+    the pivot process, and that law is the renormalised kept distribution of
+    the brute-force definition."""
+    rng = np.random.default_rng(seed)
+    for c in range(cases):
+        V = int(rng.integers(2, 8))
+        x = rng.normal(0, 1.5, V)
+        if c % 3 == 0:
+            x = np.round(x * 2) / 2            # ties
+        if c % 5 == 0:
+            x[rng.integers(0, V)] = -np.inf    # a masked token
+            if not np.isfinite(x).any():
+                x[0] = 0.0
+        x = x.astype(np.float32)
+        T = float(np.float32(rng.uniform(0.4, 2.0)))
+        p = [0.0, 1.0, float(np.float32(rng.uniform(0.05, 0.99)))][c % 3 if c % 4 else 2]
+        mp = float(np.float32(rng.uniform(0.01, 0.4))) if c % 4 == 1 else 0.0
+        dist, r1, r2 = rejection_exact(x, T, p, mp)
+        keep, _, probs = brute_row(x, T, p, 0, mp)
+        assert np.allclose(dist, probs, atol=1e-12), (x, T, p, mp, dist, probs)
+        out = O.sample_rejection(np.tile(x, (n, 1)), np.full(n, T), np.full(n, p),
+                                 min_p=np.full(n, mp), seed=1000 + c, step=3)
+        assert (out["status"] == 0).all() and (out["rounds"] >= 1).all()
+        f = np.bincount(out["token"], minlength=V) / n
+        assert f[~keep].sum() == 0.0, (f, keep)
+        for got, want in zip(f, dist):
+            assert abs(got - want) <= 5 * math.sqrt(max(want * (1 - want), 0.0) / n) + 1e-3, (c, f, dist)
+        sd = math.sqrt(max(r2 - r1 * r1, 0.0))
+        assert abs(out["rounds"].mean() - r1) <= 5 * sd / math.sqrt(n) + 1e-3, (c, out["rounds"].mean(), r1)
+        levels = len(np.unique(x[np.isfinite(x)]))
+        assert out["rounds"].max() <= levels
+
+
+def check_rejection_is_the_race(O, B=200, V=400, seed=17):
+    """With the row's own noise words in every round, the accepted token is
+    the first kept token in race order: the main sampler's token, unless the
+    row sits on a boundary (mass within 1e-12 of p, or a race tie).  Greedy
+    and error rows follow the main sampler's rules with 0 rounds."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, 2, (B, V))
+    x[::3] = np.round(x[::3] * 4) / 4
+    x[1::7, : V // 3] = -np.inf
+    x = x.astype(np.float32)
+    T = rng.uniform(0.3, 2.0, B).astype(np.float32)
+    T[::11] = 0.0
+    P = rng.uniform(0.0, 1.0, B).astype(np.float32)
+    P[::13] = 1.0
+    P[5::13] = 0.0
+    MP = np.where(rng.random(B) < 0.3, rng.uniform(0.001, 0.3, B), 0.0).astype(np.float32)
+    P[13::26] = 1.5   # p > 1 acts as p = 1
+    MP[13::26] = 0.2  # with min-p: most proposals then fail min-p alone
+    x[7, 3] = np.nan
+    P[9] = np.nan
+    ref, _ = O.sample(x, T, P, None, MP, seed=99, step=4)
+    out = O.sample_rejection(x, T, P, MP, seed=99, step=4)
+    for b in range(B):
+        if ref["status"][b]:
+            assert out["status"][b] == 1 and out["token"][b] == -1 and out["rounds"][b] == 0
+            continue
+        if T[b] <= 0:
+            assert out["greedy"][b] == 1 and out["rounds"][b] == 0 and out["token"][b] == ref["token"][b]
+            continue
+        assert out["status"][b] == 0 and out["rounds"][b] >= 1
+        if out["band"][b] > 1e-12 and out["race_margin"][b] > 1e-12:
+            assert out["token"][b] == ref["token"][b], b
+        if P[b] >= 1.0 and MP[b] == 0.0:
+            assert out["rounds"][b] == 1  # every finite token is kept
+    assert (out["rounds"][T > 0] > 1).any()  # some rows did reject
+
+
 ALL_FAST_CHECKS = [check_worked_examples, check_order_counterexample, check_special_cases, check_invariants,
-                   check_exp1, check_race_reproducible, check_logprobs, check_row_seeds]
+                   check_exp1, check_race_reproducible, check_logprobs, check_row_seeds, check_rejection_pages,
+                   check_rejection_law, check_rejection_is_the_race]

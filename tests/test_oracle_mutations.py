@@ -2,7 +2,8 @@
 build each copy, and require the pins to reject every one of them.  This is
 evidence that the pins constrain each step of the oracle: the boundary
 comparison, the always-kept top level, greedy tie-breaking, the temperature,
-min-p, top-k, renormalisation, validation, Philox and the race."""
+min-p, top-k, renormalisation, validation, Philox, the race and the
+rejection sampler."""
 import os
 import shutil
 
@@ -36,6 +37,14 @@ MUTATIONS = [
     ("logprob of every survivor", "if (keep[i]) lrow[i] = (r.x[i] - r.m) / Td - lse;",
      "if (r.surv[i]) lrow[i] = (r.x[i] - r.m) / Td - lse;"),
     ("row seed ignored", "const uint64_t row_seed = seeds ? seeds[b] : seed;", "const uint64_t row_seed = seed;"),
+    ("rejection pivot inclusive", "prop[i] = r.x[i] > -INFINITY && r.x[i] > pivot;",
+     "prop[i] = r.x[i] > -INFINITY && r.x[i] >= pivot;"),
+    ("rejection mass includes the level", "if (r.surv[i] && r.x[i] > xt) A += r.e[i];",
+     "if (r.surv[i] && r.x[i] >= xt) A += r.e[i];"),
+    ("rejection top level not forced", "if (xt == r.m) {", "if (0) {"),
+    ("rejection min-p ignored", "if (r.surv[t]) {", "if (1) {"),
+    ("rejection total over all tokens", "if (r.surv[i]) S += r.e[i];", "S += r.e[i];"),
+    ("rejection pivot not raised", "pivot = xt;", "pivot = -INFINITY;"),
 ]
 
 

@@ -73,3 +73,15 @@ def test_philox_matches_rocrand(oracle_lib, tmp_path_factory):
     tuples = P.philox_tuples()
     words = P.rocrand_words(tuples, str(tmp_path_factory.mktemp("rocrand")))
     P.check_philox_against(oracle_lib.default(), tuples, words)
+
+
+def test_rejection_pages(oracle_lib):
+    P.check_rejection_pages(oracle_lib.default())
+
+
+def test_rejection_law(oracle_lib):
+    P.check_rejection_law(oracle_lib.default())
+
+
+def test_rejection_is_the_race(oracle_lib):
+    P.check_rejection_is_the_race(oracle_lib.default())
