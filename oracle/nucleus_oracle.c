@@ -550,9 +550,9 @@ typedef struct {
  *   proportional to e: the exponential race argmax e_i / E_i over them,
  *   lowest index on ties, with the row's noise words E_i (the same words as
  *   oracle_sample).  t is accepted iff it survives min-p and either it is in
- *   the top level (always kept) or p > 0 and the survivor mass strictly
- *   above it, A(t), is below p S (the order-free top-p rule; p <= 0 keeps the
- *   top level only).  Otherwise t and every token at or below it are out: the
+ *   the top level (always kept), or p >= 1 (every survivor is kept), or
+ *   p > 0 and the survivor mass strictly above it, A(t), is below p S (the
+ *   order-free top-p rule; p <= 0 keeps the top level only).  Otherwise t and every token at or below it are out: the
  *   pivot becomes x_t and the next round draws again.
  *
  * Reusing the words in every round is a valid draw: in arrival-time form
@@ -621,7 +621,7 @@ int oracle_sample_rejection(const void* logits, int dtype, int64_t B, int64_t V,
                 if (r.surv[i] && r.x[i] > xt) A += r.e[i];
             int accept = 0;
             if (r.surv[t]) {
-                if (xt == r.m) {
+                if (xt == r.m || Pd >= 1.0) {  /* p >= 1 keeps every survivor, however light */
                     accept = 1;
                 } else if (Pd > 0.0) {
                     accept = A < Pd * S;

@@ -41,7 +41,7 @@ MUTATIONS = [
      "prop[i] = r.x[i] > -INFINITY && r.x[i] >= pivot;"),
     ("rejection mass includes the level", "if (r.surv[i] && r.x[i] > xt) A += r.e[i];",
      "if (r.surv[i] && r.x[i] >= xt) A += r.e[i];"),
-    ("rejection top level not forced", "if (xt == r.m) {", "if (0) {"),
+    ("rejection top level not forced", "if (xt == r.m || Pd >= 1.0) {", "if (Pd >= 1.0) {"),
     ("rejection min-p ignored", "if (r.surv[t]) {", "if (1) {"),
     ("rejection total over all tokens", "if (r.surv[i]) S += r.e[i];", "S += r.e[i];"),
     ("rejection pivot not raised", "pivot = xt;", "pivot = -INFINITY;"),
