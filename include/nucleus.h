@@ -150,6 +150,41 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
                    uint64_t step, int32_t* out_token, int32_t* out_keep_count, float* out_probs,
                    const nucleus_options* opt);
 
+/*
+ * Sample one token per row by sort-free rejection ("Top-p (Nucleus) Sampling,
+ * in depth", "Sort-free top-p by rejection sampling"): a second algorithm for
+ * the chain above without top-k (temperature -> min-p -> top-p -> sample),
+ * which finds no cut.  Per row, a pivot starts below every logit; each round
+ * proposes the race winner argmax_i e_i / E_i over the finite tokens above
+ * the pivot, with the same Philox words E_i as nucleus_sample, and accepts it
+ * iff it survives min-p and it is in the top level, or p >= 1, or the mass of
+ * the surviving tokens strictly more probable than it is below p (measured
+ * on the survivors, renormalised).  A rejected proposal becomes the pivot.
+ * Reusing the words is a valid draw (an exponential race restricted to the
+ * tokens above the pivot proposes in proportion to their weights, whatever
+ * was rejected before), and the accepted token is the first kept token in
+ * race order: the token nucleus_sample draws with the same seed, step and
+ * parameters (top_k NULL), up to rows within rounding of a boundary.
+ *
+ * logits, B, V, temperature, top_p, min_p, seed, step: as for nucleus_sample.
+ * out_token   device [B] int32: the accepted id; the lowest-index argmax for
+ *             T <= 0; -1 on a row error (as nucleus_sample) or if no
+ *             proposal was accepted within 64 rounds (a row needs at most one
+ *             round per distinct logit value; typical rows need 1 or 2).
+ * out_rounds  device [B] int32, or NULL: rounds run (0 for greedy and error
+ *             rows, 64 when none was accepted).
+ * opt         NULL, or options with dtype, stream, row_stride and seeds used;
+ *             flags must be 0 and out_min_kept_logit and out_logprobs NULL
+ *             (NUCLEUS_EINVAL otherwise); the workspace is not used.
+ *
+ * Returns NUCLEUS_OK or a negative code, with nucleus_sample's argument rules.
+ * A row costs two passes over its logits per round (the first round's race
+ * shares the pass that finds the max).
+ */
+int nucleus_sample_rejection(const void* logits, int64_t B, int64_t V, const float* temperature,
+                             const float* top_p, const float* min_p, uint64_t seed, uint64_t step,
+                             int32_t* out_token, int32_t* out_rounds, const nucleus_options* opt);
+
 /* Device workspace, in bytes, that nucleus_sample needs for a batch of this
  * shape and dtype with no flags: batches under 128 rows of at most
  * 64 * 8192 tokens need the split-row path's (per row: a 128-byte control

@@ -19,7 +19,7 @@ from typing import NamedTuple, Optional
 
 import torch
 
-__all__ = ["sample", "workspace_bytes", "strerror", "version", "stream_read", "NucleusError", "lib", "LIB_PATH"]
+__all__ = ["sample", "sample_rejection", "RejectionResult", "workspace_bytes", "strerror", "version", "stream_read", "NucleusError", "lib", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnucleus.so")
 
@@ -61,6 +61,8 @@ def lib():
         vp, i64, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64
         L.nucleus_sample.argtypes = [vp, i64, i64, vp, vp, vp, vp, u64, u64, vp, vp, vp, ctypes.POINTER(_Options)]
         L.nucleus_sample.restype = ctypes.c_int
+        L.nucleus_sample_rejection.argtypes = [vp, i64, i64, vp, vp, vp, u64, u64, vp, vp, ctypes.POINTER(_Options)]
+        L.nucleus_sample_rejection.restype = ctypes.c_int
         L.nucleus_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32]
         L.nucleus_workspace_bytes.restype = ctypes.c_size_t
         L.nucleus_workspace_bytes_for.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32]
@@ -170,13 +172,7 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     P = _vec(top_p, B, torch.float32, "top_p", dev)
     K = _vec(top_k, B, torch.int32, "top_k", dev)
     MP = _vec(min_p, B, torch.float32, "min_p", dev)
-    S = None
-    if seeds is not None:
-        # uint64 keys travel as their int64 bit patterns
-        S = torch.as_tensor([int(v) & (2**64 - 1) for v in torch.as_tensor(seeds).reshape(-1).tolist()],
-                            dtype=torch.uint64).view(torch.int64).to(dev).contiguous()
-        if S.numel() != B:
-            raise ValueError(f"seeds must have {B} elements")
+    S = _seeds(seeds, B, dev)
     if out is None:
         out = SampleResult(
             torch.empty(B, dtype=torch.int32, device=dev),
@@ -209,6 +205,62 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
                               ctypes.c_uint64(step), ptr(out.token), ptr(out.keep_count), ptr(out.probs),
                               ctypes.byref(opt))
     _check(rc, "nucleus_sample")
+    return out
+
+
+def _seeds(seeds, B, dev):
+    if seeds is None:
+        return None
+    # uint64 keys travel as their int64 bit patterns
+    S = torch.as_tensor([int(v) & (2**64 - 1) for v in torch.as_tensor(seeds).reshape(-1).tolist()],
+                        dtype=torch.uint64).view(torch.int64).to(dev).contiguous()
+    if S.numel() != B:
+        raise ValueError(f"seeds must have {B} elements")
+    return S
+
+
+class RejectionResult(NamedTuple):
+    token: torch.Tensor   # int32 [B]; -1 on a row error or without acceptance
+    rounds: torch.Tensor  # int32 [B]: proposal rounds (0 for greedy and error rows)
+
+
+def sample_rejection(logits: torch.Tensor, temperature, top_p, min_p=None, seed: int = 0, step: int = 0, *,
+                     seeds=None, out: Optional[RejectionResult] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> RejectionResult:
+    """Sort-free top-p by rejection (``nucleus_sample_rejection``): one token
+    per row of ``logits`` [B, V] for the chain temperature -> min-p -> top-p,
+    and the number of proposal rounds each row took.  With the same seed,
+    step and parameters it draws the token ``sample`` draws (top_k None), up
+    to rows within rounding of a boundary.  Asynchronous on ``stream``."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    if not logits.is_cuda:
+        raise NucleusError("logits must be on the GPU: this library has no CPU path")
+    B, V = logits.shape
+    if V > 1 and logits.stride(1) != 1:
+        raise ValueError("the vocabulary dimension of logits must be contiguous")
+    dev = logits.device
+    code = _dtype_code(logits)
+    T = _vec(temperature, B, torch.float32, "temperature", dev)
+    P = _vec(top_p, B, torch.float32, "top_p", dev)
+    MP = _vec(min_p, B, torch.float32, "min_p", dev)
+    S = _seeds(seeds, B, dev)
+    if out is None:
+        out = RejectionResult(torch.empty(B, dtype=torch.int32, device=dev),
+                              torch.empty(B, dtype=torch.int32, device=dev))
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    opt = _Options()
+    opt.dtype = code
+    opt.stream = s.cuda_stream
+    opt.row_stride = logits.stride(0) if B > 1 else V
+    opt.seeds = S.data_ptr() if S is not None else None
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    rc = lib().nucleus_sample_rejection(ptr(logits), B, V, ptr(T), ptr(P), ptr(MP), ctypes.c_uint64(seed),
+                                        ctypes.c_uint64(step), ptr(out.token), ptr(out.rounds), ctypes.byref(opt))
+    _check(rc, "nucleus_sample_rejection")
     return out
 
 

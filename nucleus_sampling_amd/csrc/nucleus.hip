@@ -11,6 +11,7 @@
 #include "nucleus.h"
 #include "common.h"
 #include "params.h"
+#include "rejection.h"
 #include "rowpath.h"
 #include "sampler.h"
 #include "stream_read.h"
@@ -118,7 +119,7 @@ bool aligned(const T* p)
 
 extern "C" {
 
-int nucleus_version(void) { return 210; }
+int nucleus_version(void) { return 220; }
 
 const char* nucleus_strerror(int code)
 {
@@ -243,6 +244,49 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
         else
             hipLaunchKernelGGL((row_kernel<kBF16, false>), dim3((unsigned)B), dim3(kRowThreads), 0, s, p, none);
     }
+    return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
+}
+
+int nucleus_sample_rejection(const void* logits, int64_t B, int64_t V, const float* temperature, const float* top_p,
+                             const float* min_p, uint64_t seed, uint64_t step, int32_t* out_token,
+                             int32_t* out_rounds, const nucleus_options* opt)
+{
+    const int32_t dtype = opt ? opt->dtype : NUCLEUS_F32;
+    const int64_t stride = (opt && opt->row_stride) ? opt->row_stride : V;
+    if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || stride < V) return NUCLEUS_EINVAL;
+    if (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16) return NUCLEUS_EINVAL;
+    if (opt && (opt->flags || opt->out_min_kept_logit || opt->out_logprobs)) return NUCLEUS_EINVAL;
+    if (B == 0) return NUCLEUS_OK;
+    if (!logits || !temperature || !top_p || !out_token) return NUCLEUS_EINVAL;
+    const size_t esz = dtype == NUCLEUS_F32 ? 4 : 2;
+    if ((uintptr_t)logits % esz != 0 || !aligned(temperature) || !aligned(top_p) || (min_p && !aligned(min_p)) ||
+        !aligned(out_token) || (out_rounds && !aligned(out_rounds)) || (opt && opt->seeds && !aligned(opt->seeds)))
+        return NUCLEUS_EINVAL;
+    const int dev_rc = check_device();
+    if (dev_rc != NUCLEUS_OK) return dev_rc;
+
+    Params p = {};
+    p.logits = logits;
+    p.B = B;
+    p.V = V;
+    p.stride = stride;
+    p.temperature = temperature;
+    p.top_p = top_p;
+    p.top_k = nullptr;
+    p.min_p = min_p;
+    p.seed_lo = (uint32_t)seed;
+    p.seed_hi = (uint32_t)(seed >> 32);
+    p.step_lo = (uint32_t)step;
+    p.step_hi = (uint32_t)(step >> 32);
+    p.out_token = out_token;
+    p.seeds = opt ? opt->seeds : nullptr;
+    const size_t vec_bytes = dtype == NUCLEUS_F32 ? 16 : 8;
+    p.vec_in = ((uintptr_t)logits % vec_bytes == 0) && ((size_t)stride * esz) % vec_bytes == 0;
+    hipStream_t s = opt ? (hipStream_t)opt->stream : nullptr;
+    if (dtype == NUCLEUS_F32)
+        hipLaunchKernelGGL(rejection_kernel<kF32>, dim3((unsigned)B), dim3(kRowThreads), 0, s, p, out_rounds);
+    else
+        hipLaunchKernelGGL(rejection_kernel<kBF16>, dim3((unsigned)B), dim3(kRowThreads), 0, s, p, out_rounds);
     return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
 }
 

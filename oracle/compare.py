@@ -213,3 +213,88 @@ def _kept(row, tok, min_kept):
         x = np.asarray([x], np.uint16).astype(np.uint32) << 16
         x = x.view(np.float32)[0]
     return bool(np.isfinite(x) and x >= min_kept)
+
+
+@dataclass
+class RejectionReport:
+    rows: int = 0
+    exact: int = 0
+    errors_ok: int = 0
+    greedy: int = 0
+    exempt: int = 0
+    exempt_exact: int = 0
+    rounds_total: int = 0
+    rounds_max: int = 0
+    failures: list = field(default_factory=list)
+
+    def ok(self) -> bool:
+        return not self.failures
+
+    def summary(self) -> str:
+        drawn = max(self.rows - self.errors_ok - self.greedy, 1)
+        return (f"rows={self.rows} exact={self.exact} greedy={self.greedy} row_errors={self.errors_ok} "
+                f"exempt={self.exempt} (exact {self.exempt_exact}) rounds mean "
+                f"{self.rounds_total / drawn:.3f} max {self.rounds_max} failures={len(self.failures)}")
+
+
+def compare_rejection(logits, temperature, top_p, min_p, seed, step, gpu_token, gpu_rounds, orows, seeds=None):
+    """Rejection sampler outputs against oracle_sample_rejection's rows.
+
+    * row error: token -1, rounds 0.  Greedy (T <= 0): token exactly, rounds 0.
+    * otherwise, unless exempt: token and rounds exactly.
+    * exempt: some round's acceptance test lies within 1e-5 of p (|A(t)/S - p|)
+      or some round's race within 1e-6 relative of a tie.  The GPU's token must
+      then be admissible under the oracle's masses: a min-p survivor whose
+      level has survivor mass above it < p + 1e-5 (any survivor for p >= 1),
+      and its rounds in [1, 64].
+    """
+    O = _default_oracle()
+    B, V = logits.shape
+    rep = RejectionReport()
+    for b in range(B):
+        rep.rows += 1
+        o = orows[b]
+        g, gr = int(gpu_token[b]), int(gpu_rounds[b])
+        if o["status"] == 1:
+            if g == -1 and gr == 0:
+                rep.errors_ok += 1
+            else:
+                rep.failures.append((b, f"row error: gpu token {g} rounds {gr}"))
+            continue
+        if o["greedy"]:
+            rep.greedy += 1
+            if g != int(o["token"]) or gr != 0:
+                rep.failures.append((b, f"greedy: gpu {g}/{gr} oracle {int(o['token'])}"))
+            continue
+        rep.rounds_total += max(gr, 0)
+        rep.rounds_max = max(rep.rounds_max, gr)
+        exempt = o["band"] <= MASS_BAND or o["race_margin"] <= RACE_BAND or o["status"] == 2
+        if not exempt:
+            if g == int(o["token"]) and gr == int(o["rounds"]):
+                rep.exact += 1
+            else:
+                rep.failures.append((b, f"gpu {g}/{gr} rounds, oracle {int(o['token'])}/{int(o['rounds'])} "
+                                        f"(band {o['band']:.3g}, margin {o['race_margin']:.3g})"))
+            continue
+        rep.exempt += 1
+        if g == int(o["token"]) and gr == int(o["rounds"]):
+            rep.exempt_exact += 1
+            continue
+        if not (0 <= g < V and 1 <= gr <= 64):
+            rep.failures.append((b, f"exempt row: gpu token {g} rounds {gr} out of range"))
+            continue
+        row = logits[b]
+        mp = 0.0 if min_p is None else float(min_p[b])
+        s = int(seeds[b]) if seeds is not None else seed
+        if row.dtype == np.float32:
+            xt = float(row[g])
+        else:  # bf16 bits, widened exactly
+            xt = float((np.asarray([row[g]], np.uint32) << 16).view(np.float32)[0])
+        ev, _ = O.eval_cut(row, b, float(temperature[b]), float(top_p[b]), 0, mp, s, step, xt)
+        p = float(top_p[b])
+        # The token's own level must survive min-p (its survivor mass is m_cut - a_cut).
+        survives = ev["m_cut"] > ev["a_cut"] or (mp <= 0.0 and math.isfinite(xt))
+        ok = ev["status"] == 0 and survives and (p >= 1.0 or ev["a_cut"] == 0.0 or ev["a_cut"] < p + MASS_BAND)
+        if not ok:
+            rep.failures.append((b, f"exempt row: gpu token {g} not admissible (a_cut {ev['a_cut']:.6g}, p {p})"))
+    return rep

@@ -25,8 +25,8 @@ def L():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    for n in ("nucleus_sample", "nucleus_workspace_bytes", "nucleus_strerror", "nucleus_version",
-              "nucleus_stream_read"):
+    for n in ("nucleus_sample", "nucleus_sample_rejection", "nucleus_workspace_bytes", "nucleus_strerror",
+              "nucleus_version", "nucleus_stream_read"):
         assert n in names
 
 
@@ -109,3 +109,32 @@ def test_host_side_argument_errors(L):
 def test_empty_batch_launches_nothing(L):
     assert _call(L, B=0) == 0
     assert _call(L, B=0, logits=None, T=None, P=None, tok=None, cnt=None) == 0
+
+
+def _call_rej(L, logits=1 << 20, B=2, V=8, T=1 << 21, P=1 << 22, MP=None, tok=1 << 23, rounds=1 << 24, opt=None):
+    # Fake, never-dereferenced device addresses, as above.
+    return L.nucleus_sample_rejection(logits, B, V, T, P, MP, ctypes.c_uint64(0), ctypes.c_uint64(0), tok, rounds,
+                                      opt)
+
+
+def test_rejection_host_side_argument_errors(L):
+    import nucleus_sampling_amd as ns
+
+    EINVAL = -1
+    assert _call_rej(L, logits=None) == EINVAL
+    assert _call_rej(L, T=None) == EINVAL
+    assert _call_rej(L, P=None) == EINVAL
+    assert _call_rej(L, tok=None) == EINVAL
+    assert _call_rej(L, B=-1) == EINVAL
+    assert _call_rej(L, V=0) == EINVAL
+    assert _call_rej(L, V=1 << 31) == EINVAL
+    assert _call_rej(L, logits=(1 << 20) + 2) == EINVAL
+    assert _call_rej(L, MP=(1 << 25) + 2) == EINVAL
+    assert _call_rej(L, rounds=(1 << 24) + 1) == EINVAL
+    for field, value in (("dtype", 5), ("row_stride", 4), ("flags", 1), ("out_min_kept_logit", 1 << 26),
+                         ("out_logprobs", 1 << 26)):
+        opt = ns._Options()
+        setattr(opt, field, value)
+        assert _call_rej(L, opt=ctypes.byref(opt)) == EINVAL, field
+    assert _call_rej(L, B=0) == 0
+    assert _call_rej(L, B=0, logits=None, T=None, P=None, tok=None) == 0
