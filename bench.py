@@ -137,6 +137,7 @@ def main():
     ap.add_argument("--path", choices=["default", "single", "split", "rows"], default="default",
                     help="force one of the library's paths (for comparisons; the headline uses the default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rejection", action="store_true", help="skip timing the rejection sampler")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-steps", action="store_true", help="only run the timed loop (for rocprofv3)")
     ap.add_argument("--pmc-calibrate", action="store_true",
@@ -236,6 +237,38 @@ def main():
     torch.cuda.synchronize()
     read_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(rs, re_)]))
 
+    # The rejection sampler (nucleus_sample_rejection) on the same buffers:
+    # T, top-p and min-p of the workload, top-k off.
+    rej = None
+    if not args.no_rejection:
+        rout = ns.RejectionResult(torch.empty(B, dtype=torch.int32, device=dev),
+                                  torch.empty(B, dtype=torch.int32, device=dev))
+        for i in range(args.warmup):
+            ns.sample_rejection(bufs[i % nbuf], T, P, MP, seed=w["seed"], step=i, out=rout, stream=stream)
+        torch.cuda.synchronize()
+        js = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        je = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        rounds = []
+        for i in range(args.steps):
+            js[i].record(stream)
+            ns.sample_rejection(bufs[i % nbuf], T, P, MP, seed=w["seed"], step=args.warmup + i, out=rout,
+                                stream=stream)
+            je[i].record(stream)
+            if i < 8:
+                rounds.append(rout.rounds.clone())
+        torch.cuda.synchronize()
+        rj_ms = [a.elapsed_time(e) for a, e in zip(js, je)]
+        rr = torch.cat(rounds).float()
+        rr = rr[rr > 0]
+        rj_avg = float(np.mean(rj_ms))
+        rej = {"kernel": "rejection_kernel", "avg_launch_ms": rj_avg, "median_launch_ms": float(np.median(rj_ms)),
+               "rows_per_s": B / (rj_avg * 1e-3), "logits_gbps": batch_bytes / (rj_avg * 1e-3) / 1e9,
+               "frac_of_hbm_peak": batch_bytes / (rj_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+               "rounds_mean": float(rr.mean()) if rr.numel() else 0.0,
+               "rounds_max": int(rr.max()) if rr.numel() else 0,
+               "passes_per_row_mean": 2.0 * float(rr.mean()) if rr.numel() else 0.0,
+               "note": "top-k off; every row reads its logits 2 x rounds times"}
+
     avg_ms = float(np.mean(per_launch_ms))
     med_ms = float(np.median(per_launch_ms))
     achieved = batch_bytes / (avg_ms * 1e-3) / 1e9
@@ -269,6 +302,7 @@ def main():
                      "algorithmic_bytes_per_launch": batch_bytes},
         "stream_read": {"gbps": stream_gbps, "avg_ms": read_ms, "frac_of_peak": stream_gbps / PEAK_HBM_GBPS,
                         "sampler_vs_stream": achieved / stream_gbps},
+        "rejection": rej,
         "wall_s": wall,
         "kernel_hash": kernel_hash(),
     }
