@@ -40,6 +40,14 @@ REJ_DTYPE = np.dtype(
     ],
     align=True,
 )
+SPEC_DTYPE = np.dtype(
+    [
+        ("status", np.int32), ("token", np.int32), ("accepted", np.int32), ("greedy", np.int32),
+        ("p_draft", np.float64), ("q_draft", np.float64), ("u", np.float64), ("s1", np.float64),
+        ("s1_low", np.float64), ("threat", np.float64),
+    ],
+    align=True,
+)
 CUT_DTYPE = np.dtype(
     [
         ("status", np.int32), ("token", np.int32), ("keep_count", np.int32), ("pad", np.int32),
@@ -84,6 +92,9 @@ class Oracle:
         L.oracle_sample_rejection.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, u64, vp, u64, i32, i64,
                                               i64, vp]
         L.oracle_sample_rejection.restype = ctypes.c_int
+        L.oracle_spec_verify.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, u64, vp, u64,
+                                         ctypes.c_double, i64, i64, vp]
+        L.oracle_spec_verify.restype = ctypes.c_int
         L.oracle_eval_cut.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_float, ctypes.c_float, i32,
                                       ctypes.c_float, u64, u64, ctypes.c_double, vp, vp]
         L.oracle_eval_cut.restype = ctypes.c_int
@@ -184,6 +195,42 @@ class Oracle:
                 run(sp)
         return out
 
+    def spec_verify(self, logits, temperature, top_p, top_k, min_p, draft_probs, draft_token, seed=0, step=0,
+                    seeds=None, rel_tol=2e-5, threads=1):
+        """Speculative acceptance (oracle_spec_verify) on a [B, V] batch:
+        ``draft_probs`` [B, V] float32, ``draft_token`` [B].  Returns a
+        structured array of SPEC_DTYPE of length B."""
+        logits = np.ascontiguousarray(logits)
+        B, V = logits.shape
+        dt = _dtype_code(logits)
+        T = np.ascontiguousarray(temperature, dtype=np.float32).reshape(B)
+        P = np.ascontiguousarray(top_p, dtype=np.float32).reshape(B)
+        K = None if top_k is None else np.ascontiguousarray(top_k, dtype=np.int32).reshape(B)
+        MP = None if min_p is None else np.ascontiguousarray(min_p, dtype=np.float32).reshape(B)
+        Q = np.ascontiguousarray(draft_probs, dtype=np.float32).reshape(B, V)
+        D = np.ascontiguousarray(draft_token, dtype=np.int32).reshape(B)
+        S = None if seeds is None else np.ascontiguousarray(seeds, dtype=np.uint64).reshape(B)
+        out = np.zeros(B, dtype=SPEC_DTYPE)
+        L = self.L
+
+        def run(span):
+            rc = L.oracle_spec_verify(_ptr(logits), dt, B, V, V, _ptr(T), _ptr(P), _ptr(K), _ptr(MP), _ptr(Q), _ptr(D),
+                                      ctypes.c_uint64(seed), _ptr(S), ctypes.c_uint64(step), float(rel_tol),
+                                      span[0], span[1], _ptr(out))
+            if rc != 0:
+                raise ValueError("oracle_spec_verify rejected its arguments")
+
+        n = max(1, min(threads, B))
+        edges = np.linspace(0, B, n + 1).astype(np.int64)
+        spans = [(int(edges[j]), int(edges[j + 1])) for j in range(n) if edges[j + 1] > edges[j]]
+        if len(spans) > 1:
+            with ThreadPoolExecutor(len(spans)) as ex:
+                list(ex.map(run, spans))
+        else:
+            for sp in spans:
+                run(sp)
+        return out
+
     def eval_cut(self, logits_row, row, temperature, top_p, top_k, min_p, seed, step, cut, want_probs=False):
         """Judge a keep threshold chosen elsewhere on one row (see oracle_eval_cut)."""
         logits_row = np.ascontiguousarray(logits_row)
@@ -253,6 +300,10 @@ def sample(*a, **k):
 
 def sample_rejection(*a, **k):
     return default().sample_rejection(*a, **k)
+
+
+def spec_verify(*a, **k):
+    return default().spec_verify(*a, **k)
 
 
 def eval_cut(*a, **k):

@@ -642,3 +642,125 @@ int oracle_sample_rejection(const void* logits, int dtype, int64_t B, int64_t V,
     free(prop);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Speculative-decoding acceptance ("Top-p (Nucleus) Sampling, in depth",    */
+/* "Logprobs, speculative decoding and reproducibility"): a draft token d    */
+/* drawn from the draft's distribution q is accepted with probability        */
+/* min(1, p(d)/q(d)); otherwise the token is drawn from the normalised       */
+/* positive part of p - q.  p is the target's truncated, renormalised        */
+/* distribution (the kept set of oracle_sample), never the raw softmax.      */
+/* ------------------------------------------------------------------------ */
+
+/* Noise of the verification step (reading adopted; the pages fix none): the
+ * Philox key of the row, counter word 1 = row index with bit 31 set (so the
+ * words never repeat nucleus_sample's race words for the same seed and
+ * step), words 2-3 = step.  Token i of the residual draw takes word i mod 4 of
+ * counter word 0 = i / 4; the acceptance uniform is word 0 at counter word
+ * 0 = 0xFFFFFFFF, which no token reaches (i / 4 < 2^29). */
+static uint32_t spec_word(uint64_t key, uint64_t step, int64_t row, uint32_t c0, int word)
+{
+    uint32_t k[2] = {(uint32_t)key, (uint32_t)(key >> 32)};
+    uint32_t ctr[4] = {c0, (uint32_t)row | 0x80000000u, (uint32_t)step, (uint32_t)(step >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, k, out);
+    return out[word];
+}
+
+typedef struct {
+    int32_t status;     /* 0 = ok, 1 = target row error or draft token out of range, 2 = nothing to resample */
+    int32_t token;      /* output token; -1 unless status 0 */
+    int32_t accepted;   /* 1 when the draft token was accepted */
+    int32_t greedy;     /* 1 when the target row is greedy (p one-hot) */
+    double p_draft;     /* p(d), q(d) and the acceptance uniform u */
+    double q_draft;
+    double u;
+    double s1;          /* winning residual score r_i / E_i (rejections) */
+    double s1_low;      /* that score with the winner's residual lowered by tol */
+    double threat;      /* best score another token reaches with its residual raised by tol */
+} oracle_spec_row;
+
+/*
+ * Verify rows [r0, r1): target logits and chain parameters as for
+ * oracle_sample (row b's kept distribution p), draft distribution q
+ * ([B, V] float, row-major) and draft tokens d[B].  With u the acceptance
+ * uniform, the draft is accepted iff u q(d) < p(d) (probability
+ * min(1, p(d)/q(d)); q(d) = 0 accepts iff p(d) > 0).  Otherwise the token is
+ * the exponential race argmax_i r_i / E_i over r_i = max(0, p_i - q_i) > 0,
+ * lowest index on ties: a draw from the normalised residual.  The accepted
+ * or resampled token then follows p exactly, whatever q is.
+ *
+ * For judging a GPU that holds p to within tol_i = rel_tol p_i on kept tokens
+ * (exactly 0 elsewhere), s1_low and threat bound the race under that
+ * uncertainty.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_spec_verify(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride,
+                       const float* temperature, const float* top_p, const int32_t* top_k, const float* min_p,
+                       const float* draft_probs, const int32_t* draft_token, uint64_t seed, const uint64_t* seeds,
+                       uint64_t step, double rel_tol, int64_t r0, int64_t r1, oracle_spec_row* rows_out)
+{
+    if (V < 1 || B < 0 || r0 < 0 || r1 > B || stride < V || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return -1;
+    double* p = (double*)malloc((size_t)V * sizeof(double));
+    oracle_row* target = (oracle_row*)calloc((size_t)B, sizeof(oracle_row));
+    for (int64_t b = r0; b < r1; ++b) {
+        oracle_spec_row* o = &rows_out[b];
+        memset(o, 0, sizeof(*o));
+        o->token = -1;
+        /* The target's kept, renormalised distribution of row b. */
+        oracle_sample_ex(logits, dtype, B, V, stride, temperature, top_p, top_k, min_p, seed, seeds, step, b, b + 1,
+                         target, p, NULL);
+        const oracle_row tr = target[b];
+        const int32_t d = draft_token[b];
+        if (tr.status != 0 || d < 0 || d >= V) {
+            o->status = 1;
+            continue;
+        }
+        o->greedy = tr.greedy;
+        const uint64_t key = seeds ? seeds[b] : seed;
+        const float* q = draft_probs + b * V;
+        o->p_draft = p[d];
+        o->q_draft = (double)q[d];
+        o->u = ((double)spec_word(key, step, b, 0xFFFFFFFFu, 0) + 0.5) * (1.0 / 4294967296.0);
+        if (o->u * o->q_draft < o->p_draft) {
+            o->accepted = 1;
+            o->token = d;
+            continue;
+        }
+        int64_t best = -1;
+        double s1 = -1.0, threat = 0.0;
+        for (int64_t i = 0; i < V; ++i) {
+            const double r = p[i] - (double)q[i];
+            const double tol = rel_tol * p[i];
+            if (!(r > 0.0) && !(r + tol > 0.0)) continue;
+            const double E = oracle_exp1(spec_word(key, step, b, (uint32_t)(i >> 2), (int)(i & 3)));
+            if (r > 0.0) {
+                const double s = r / E;
+                if (s > s1) {
+                    if (best >= 0) {
+                        const double up = (p[best] - (double)q[best] + rel_tol * p[best]) / oracle_exp1(
+                            spec_word(key, step, b, (uint32_t)(best >> 2), (int)(best & 3)));
+                        if (up > threat) threat = up;
+                    }
+                    s1 = s;
+                    best = i;
+                    continue;
+                }
+            }
+            const double up = (r + tol) / E;
+            if (up > threat) threat = up;
+        }
+        if (best < 0) {
+            o->status = 2;
+            continue;
+        }
+        o->token = (int32_t)best;
+        o->s1 = s1;
+        o->s1_low = (p[best] - (double)q[best] - rel_tol * p[best]) /
+                    oracle_exp1(spec_word(key, step, b, (uint32_t)(best >> 2), (int)(best & 3)));
+        o->threat = threat;
+    }
+    free(target);
+    free(p);
+    return 0;
+}

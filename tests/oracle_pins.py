@@ -601,6 +601,91 @@ def check_rejection_is_the_race(O, B=200, V=400, seed=17):
     assert (out["rounds"][T > 0] > 1).any()  # some rows did reject
 
 
+
+
+# --------------------------------------------------------------------------
+# Speculative acceptance ("Top-p (Nucleus) Sampling, in depth", "Logprobs,
+# speculative decoding and reproducibility")
+# --------------------------------------------------------------------------
+def _spec_draws(O, x, T, p, k, mp, q, n, seed, step=0):
+    """n independent verifications of one row (each batch row has its own
+    Philox counter) with draft tokens drawn from q by NumPy."""
+    V = len(x)
+    qq = np.asarray(q, np.float32).astype(np.float64)
+    d = np.random.default_rng(seed).choice(V, size=n, p=qq / qq.sum())
+    out = O.spec_verify(np.tile(x, (n, 1)), np.full(n, T), np.full(n, p), np.full(n, k, np.int32), np.full(n, mp),
+                        np.tile(np.asarray(q, np.float32), (n, 1)), d, seed=seed, step=step)
+    return out, d
+
+
+def check_spec_law(O, cases=20, n=12000, seed=404):
+    """Whatever the draft q, the verified token follows the truncated target
+    p exactly (brute-force definition), the acceptance rate is
+    sum_i min(p_i, q_i), and no token outside the nucleus is ever output;
+    the pages' six-token example included."""
+    rng = np.random.default_rng(seed)
+    spec = golden()["speculative"]
+    for c in range(cases + len(spec)):
+        if c < len(spec):
+            case = spec[c]
+            x = np.asarray(case["logits"], np.float32)
+            T, p, k, mp = case["T"], case["p"], 0, 0.0
+            qx = np.exp(x.astype(np.float64) + np.asarray(case["draft_logit_shift"]))
+            nn = case["n"]
+        else:
+            V = int(rng.integers(2, 8))
+            x = rng.normal(0, 1.5, V)
+            if c % 3 == 0:
+                x = np.round(x * 2) / 2
+            x = x.astype(np.float32)
+            T = float(np.float32(rng.uniform(0.5, 2.0)))
+            p = float(np.float32(rng.uniform(0.2, 1.0)))
+            k = int(rng.integers(0, V + 1)) if c % 4 == 1 else 0
+            mp = float(np.float32(rng.uniform(0.01, 0.3))) if c % 5 == 2 else 0.0
+            qx = np.exp(rng.normal(0, 1.0, V))
+            if c % 3 == 1:
+                qx[rng.integers(0, V)] = 0.0  # the draft never proposes this token
+            nn = n
+        q = (qx / qx.sum()).astype(np.float32)
+        keep, _, target = brute_row(x, T, p, k, mp)
+        if c < len(spec):
+            assert np.abs(target[: len(spec[c]["target"])] - spec[c]["target"]).max() < 5e-5
+        out, d = _spec_draws(O, x, T, p, k, mp, q, nn, seed=1000 + c)
+        assert (out["status"] == 0).all()
+        f = np.bincount(out["token"], minlength=len(x)) / nn
+        assert f[~keep].sum() == 0.0, (c, f, keep)
+        for got, want in zip(f, target):
+            assert abs(got - want) <= 5 * math.sqrt(max(want * (1 - want), 0.0) / nn) + 1e-3, (c, f, target)
+        rate = float(np.minimum(target, q.astype(np.float64)).sum())
+        assert abs(out["accepted"].mean() - rate) <= 5 * math.sqrt(rate * (1 - rate) / nn) + 1e-3, (c, rate)
+        acc = out["accepted"] == 1
+        assert (out["token"][acc] == d[acc]).all()
+
+
+def check_spec_special(O):
+    """q = p accepts every draft; a draft that proposes only a token outside
+    the nucleus is never accepted and the output then follows p; a target
+    row error or a draft token out of range is a row error."""
+    x = np.asarray([2.0, 1.0, 0.5, -1.0, -3.0], np.float32)
+    keep, _, target = brute_row(x, 1.0, 0.8, 0, 0.0)
+    n = 20000
+    out, _ = _spec_draws(O, x, 1.0, 0.8, 0, 0.0, target, n, seed=1)
+    assert out["accepted"].mean() > 0.999
+    outside = int(np.nonzero(~keep)[0][0])
+    q = np.zeros(len(x))
+    q[outside] = 1.0
+    out, d = _spec_draws(O, x, 1.0, 0.8, 0, 0.0, q, n, seed=2)
+    assert (d == outside).all() and out["accepted"].sum() == 0
+    f = np.bincount(out["token"], minlength=len(x)) / n
+    for got, want in zip(f, target):
+        assert abs(got - want) <= 5 * math.sqrt(max(want * (1 - want), 0.0) / n) + 1e-3
+    bad = np.tile(x, (3, 1))
+    bad[0, 1] = np.nan
+    out = O.spec_verify(bad, np.ones(3), np.full(3, 0.8), None, None, np.full((3, 5), 0.2, np.float32),
+                        np.asarray([0, 5, -1]), seed=3)
+    assert (out["status"] == 1).all() and (out["token"] == -1).all()
+
+
 ALL_FAST_CHECKS = [check_worked_examples, check_order_counterexample, check_special_cases, check_invariants,
                    check_exp1, check_race_reproducible, check_logprobs, check_row_seeds, check_rejection_pages,
-                   check_rejection_law, check_rejection_is_the_race]
+                   check_rejection_law, check_rejection_is_the_race, check_spec_law, check_spec_special]

@@ -2,8 +2,8 @@
 build each copy, and require the pins to reject every one of them.  This is
 evidence that the pins constrain each step of the oracle: the boundary
 comparison, the always-kept top level, greedy tie-breaking, the temperature,
-min-p, top-k, renormalisation, validation, Philox, the race and the
-rejection sampler."""
+min-p, top-k, renormalisation, validation, Philox, the race, the
+rejection sampler and speculative acceptance."""
 import os
 import shutil
 
@@ -45,6 +45,9 @@ MUTATIONS = [
     ("rejection min-p ignored", "if (r.surv[t]) {", "if (1) {"),
     ("rejection total over all tokens", "if (r.surv[i]) S += r.e[i];", "S += r.e[i];"),
     ("rejection pivot not raised", "pivot = xt;", "pivot = -INFINITY;"),
+    ("speculative acceptance reversed", "if (o->u * o->q_draft < o->p_draft) {", "if (o->u * o->p_draft < o->q_draft) {"),
+    ("speculative acceptance ignores q", "if (o->u * o->q_draft < o->p_draft) {", "if (o->u < o->p_draft) {"),
+    ("speculative residual reversed", "const double r = p[i] - (double)q[i];", "const double r = (double)q[i] - p[i];"),
 ]
 
 

@@ -85,3 +85,11 @@ def test_rejection_law(oracle_lib):
 
 def test_rejection_is_the_race(oracle_lib):
     P.check_rejection_is_the_race(oracle_lib.default())
+
+
+def test_spec_law(oracle_lib):
+    P.check_spec_law(oracle_lib.default())
+
+
+def test_spec_special(oracle_lib):
+    P.check_spec_special(oracle_lib.default())
