@@ -185,6 +185,42 @@ int nucleus_sample_rejection(const void* logits, int64_t B, int64_t V, const flo
                              const float* top_p, const float* min_p, uint64_t seed, uint64_t step,
                              int32_t* out_token, int32_t* out_rounds, const nucleus_options* opt);
 
+/*
+ * Speculative-decoding acceptance against the truncated target ("Top-p
+ * (Nucleus) Sampling, in depth", "Logprobs, speculative decoding and
+ * reproducibility").  Per row b, the draft token d = draft_token[b], drawn
+ * from the draft's own sampling distribution q (including any truncation the
+ * draft applied), is accepted with probability min(1, p(d)/q(d)); otherwise
+ * the token is drawn from the normalised positive part of p - q.  p must be
+ * the target's truncated, renormalised distribution -- nucleus_sample's
+ * out_probs for the target logits -- not its raw softmax; the output then
+ * follows p exactly, whatever q is.
+ *
+ * Noise: the row's Philox key (seed, or opt->seeds[b]) with counter
+ * (c0, b + 2^31, step low, step high): never the words nucleus_sample uses
+ * for the same seed and step.  u = (r + 1/2) 2^-32 with r word 0 at
+ * c0 = 0xFFFFFFFF decides acceptance: u q(d) < p(d).  The residual draw is
+ * the exponential race argmax_i (p_i - q_i) / E_i over p_i > q_i, E_i from
+ * word i mod 4 at c0 = i / 4, lowest index on ties.
+ *
+ * target_probs  device [B, V] float, rows contiguous: p.
+ * draft_probs   device [B, V] float, rows contiguous: q.
+ * draft_token   device [B] int32.
+ * out_token     device [B] int32: d if accepted, else the residual draw; -1 if
+ *               d is outside [0, V) or p - q has no positive entry (a target
+ *               row error leaves p all zero).
+ * out_accepted  device [B] int32, or NULL: 1 if the draft token was accepted.
+ * opt           NULL, or options with stream and seeds used; dtype must be
+ *               NUCLEUS_F32, row_stride 0 or V, flags 0, out_min_kept_logit and
+ *               out_logprobs NULL (NUCLEUS_EINVAL otherwise).
+ *
+ * Returns NUCLEUS_OK or a negative code.  Asynchronous on opt->stream.  An
+ * accepted row reads two floats; a rejected row reads its p and q rows once.
+ */
+int nucleus_spec_verify(const float* target_probs, const float* draft_probs, const int32_t* draft_token,
+                        int64_t B, int64_t V, uint64_t seed, uint64_t step, int32_t* out_token,
+                        int32_t* out_accepted, const nucleus_options* opt);
+
 /* Device workspace, in bytes, that nucleus_sample needs for a batch of this
  * shape and dtype with no flags: batches under 128 rows of at most
  * 64 * 8192 tokens need the split-row path's (per row: a 128-byte control

@@ -19,7 +19,7 @@ from typing import NamedTuple, Optional
 
 import torch
 
-__all__ = ["sample", "sample_rejection", "RejectionResult", "workspace_bytes", "strerror", "version", "stream_read", "NucleusError", "lib", "LIB_PATH"]
+__all__ = ["sample", "sample_rejection", "RejectionResult", "spec_verify", "SpecResult", "workspace_bytes", "strerror", "version", "stream_read", "NucleusError", "lib", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnucleus.so")
 
@@ -63,6 +63,8 @@ def lib():
         L.nucleus_sample.restype = ctypes.c_int
         L.nucleus_sample_rejection.argtypes = [vp, i64, i64, vp, vp, vp, u64, u64, vp, vp, ctypes.POINTER(_Options)]
         L.nucleus_sample_rejection.restype = ctypes.c_int
+        L.nucleus_spec_verify.argtypes = [vp, vp, vp, i64, i64, u64, u64, vp, vp, ctypes.POINTER(_Options)]
+        L.nucleus_spec_verify.restype = ctypes.c_int
         L.nucleus_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32]
         L.nucleus_workspace_bytes.restype = ctypes.c_size_t
         L.nucleus_workspace_bytes_for.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32]
@@ -261,6 +263,44 @@ def sample_rejection(logits: torch.Tensor, temperature, top_p, min_p=None, seed:
     rc = lib().nucleus_sample_rejection(ptr(logits), B, V, ptr(T), ptr(P), ptr(MP), ctypes.c_uint64(seed),
                                         ctypes.c_uint64(step), ptr(out.token), ptr(out.rounds), ctypes.byref(opt))
     _check(rc, "nucleus_sample_rejection")
+    return out
+
+
+class SpecResult(NamedTuple):
+    token: torch.Tensor     # int32 [B]: the draft token if accepted, else the residual draw; -1 on errors
+    accepted: torch.Tensor  # int32 [B]: 1 if the draft token was accepted
+
+
+def spec_verify(target_probs: torch.Tensor, draft_probs: torch.Tensor, draft_token, seed: int = 0, step: int = 0, *,
+                seeds=None, out: Optional[SpecResult] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> SpecResult:
+    """Speculative acceptance (``nucleus_spec_verify``): accept each row's
+    draft token with probability min(1, p/q), else draw from the normalised
+    positive part of p - q.  ``target_probs`` must be the target's truncated
+    distribution (``sample(..., want_probs=True).probs``); ``draft_probs`` the
+    draft's sampling distribution; both float32 [B, V] on the GPU."""
+    for name, t in (("target_probs", target_probs), ("draft_probs", draft_probs)):
+        if t.dim() != 2 or t.dtype != torch.float32 or not t.is_cuda:
+            raise ValueError(f"{name} must be a float32 [B, V] tensor on the GPU")
+    if target_probs.shape != draft_probs.shape:
+        raise ValueError("target_probs and draft_probs must have the same shape")
+    B, V = target_probs.shape
+    dev = target_probs.device
+    Pt = target_probs.contiguous()
+    Qt = draft_probs.contiguous()
+    D = _vec(draft_token, B, torch.int32, "draft_token", dev)
+    S = _seeds(seeds, B, dev)
+    if out is None:
+        out = SpecResult(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    opt = _Options()
+    opt.stream = s.cuda_stream
+    opt.seeds = S.data_ptr() if S is not None else None
+    rc = lib().nucleus_spec_verify(Pt.data_ptr() if B else None, Qt.data_ptr() if B else None,
+                                   D.data_ptr() if B else None, B, V, ctypes.c_uint64(seed), ctypes.c_uint64(step),
+                                   out.token.data_ptr() if B else None, out.accepted.data_ptr() if B else None,
+                                   ctypes.byref(opt))
+    _check(rc, "nucleus_spec_verify")
     return out
 
 

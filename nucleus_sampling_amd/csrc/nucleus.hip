@@ -14,6 +14,7 @@
 #include "rejection.h"
 #include "rowpath.h"
 #include "sampler.h"
+#include "spec.h"
 #include "stream_read.h"
 #include "workspace.h"
 
@@ -119,7 +120,7 @@ bool aligned(const T* p)
 
 extern "C" {
 
-int nucleus_version(void) { return 220; }
+int nucleus_version(void) { return 230; }
 
 const char* nucleus_strerror(int code)
 {
@@ -287,6 +288,40 @@ int nucleus_sample_rejection(const void* logits, int64_t B, int64_t V, const flo
         hipLaunchKernelGGL(rejection_kernel<kF32>, dim3((unsigned)B), dim3(kRowThreads), 0, s, p, out_rounds);
     else
         hipLaunchKernelGGL(rejection_kernel<kBF16>, dim3((unsigned)B), dim3(kRowThreads), 0, s, p, out_rounds);
+    return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
+}
+
+int nucleus_spec_verify(const float* target_probs, const float* draft_probs, const int32_t* draft_token, int64_t B,
+                        int64_t V, uint64_t seed, uint64_t step, int32_t* out_token, int32_t* out_accepted,
+                        const nucleus_options* opt)
+{
+    if (B < 0 || V < 1 || V >= (int64_t(1) << 31)) return NUCLEUS_EINVAL;
+    if (opt && ((opt->row_stride && opt->row_stride != V) || opt->dtype != NUCLEUS_F32 || opt->flags ||
+                opt->out_min_kept_logit || opt->out_logprobs))
+        return NUCLEUS_EINVAL;
+    if (B == 0) return NUCLEUS_OK;
+    if (!target_probs || !draft_probs || !draft_token || !out_token) return NUCLEUS_EINVAL;
+    if (!aligned(target_probs) || !aligned(draft_probs) || !aligned(draft_token) || !aligned(out_token) ||
+        (out_accepted && !aligned(out_accepted)) || (opt && opt->seeds && !aligned(opt->seeds)))
+        return NUCLEUS_EINVAL;
+    const int dev_rc = check_device();
+    if (dev_rc != NUCLEUS_OK) return dev_rc;
+    SpecParams sp = {};
+    sp.target = target_probs;
+    sp.draft = draft_probs;
+    sp.draft_token = draft_token;
+    sp.B = B;
+    sp.V = V;
+    sp.seed_lo = (uint32_t)seed;
+    sp.seed_hi = (uint32_t)(seed >> 32);
+    sp.step_lo = (uint32_t)step;
+    sp.step_hi = (uint32_t)(step >> 32);
+    sp.seeds = opt ? opt->seeds : nullptr;
+    sp.out_token = out_token;
+    sp.out_accepted = out_accepted;
+    sp.vec = (V % 4 == 0) && (uintptr_t)target_probs % 16 == 0 && (uintptr_t)draft_probs % 16 == 0;
+    hipStream_t s = opt ? (hipStream_t)opt->stream : nullptr;
+    hipLaunchKernelGGL(spec_kernel, dim3((unsigned)B), dim3(kSpecThreads), 0, s, sp);
     return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
 }
 

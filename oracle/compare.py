@@ -298,3 +298,100 @@ def compare_rejection(logits, temperature, top_p, min_p, seed, step, gpu_token, 
         if not ok:
             rep.failures.append((b, f"exempt row: gpu token {g} not admissible (a_cut {ev['a_cut']:.6g}, p {p})"))
     return rep
+
+
+SPEC_REL_TOL = 2e-5  # relative uncertainty of the GPU's kept probabilities (p within 1e-5 p, plus fp32 rounding)
+
+
+@dataclass
+class SpecReport:
+    rows: int = 0
+    exact: int = 0
+    accepted: int = 0
+    errors_ok: int = 0
+    exempt_cut: int = 0
+    exempt_accept: int = 0
+    exempt_race: int = 0
+    failures: list = field(default_factory=list)
+
+    def ok(self) -> bool:
+        return not self.failures
+
+    def summary(self) -> str:
+        return (f"rows={self.rows} exact={self.exact} accepted={self.accepted} row_errors={self.errors_ok} "
+                f"exempt_cut={self.exempt_cut} exempt_accept={self.exempt_accept} exempt_race={self.exempt_race} "
+                f"failures={len(self.failures)}")
+
+
+def compare_spec(draft_probs, draft_token, gpu_token, gpu_accepted, gpu_keep_count, gpu_p_at_token, orows,
+                 otarget):
+    """Speculative verification outputs against oracle_spec_verify's rows.
+
+    * row error (oracle status 1): token -1, not accepted.  Nothing to
+      resample (status 2): token -1.
+    * the GPU's target kept a different set than the oracle (a row within
+      the mass band of its cut): the output must be valid for the GPU's own p:
+      the draft token if accepted, else a token with p > q.
+    * the acceptance test within SPEC_REL_TOL p(d) of its boundary: valid as
+      above.  Otherwise acceptance exactly; an accepted row outputs d.
+    * a rejected row outputs the oracle's residual winner, unless another
+      token's score, with its residual raised by SPEC_REL_TOL p, comes within
+      1e-6 of the winner's lowered score: then valid as above.
+    ``gpu_p_at_token[b]`` is the GPU's p at its output token.
+    """
+    rep = SpecReport()
+    B = len(orows)
+    for b in range(B):
+        rep.rows += 1
+        o = orows[b]
+        g, ga = int(gpu_token[b]), int(gpu_accepted[b])
+        d = int(draft_token[b])
+
+        def valid():
+            if ga == 1:
+                return g == d
+            return 0 <= g < draft_probs.shape[1] and float(gpu_p_at_token[b]) > float(draft_probs[b, g])
+
+        if o["status"] == 1:
+            if g == -1 and ga == 0:
+                rep.errors_ok += 1
+            else:
+                rep.failures.append((b, f"row error: gpu {g}/{ga}"))
+            continue
+        if int(gpu_keep_count[b]) != int(otarget["keep_count"][b]):
+            rep.exempt_cut += 1
+            if not valid():
+                rep.failures.append((b, f"different cut: gpu output {g}/{ga} not valid"))
+            continue
+        gap = abs(o["u"] * o["q_draft"] - o["p_draft"])
+        if gap <= SPEC_REL_TOL * o["p_draft"] + 1e-12:
+            rep.exempt_accept += 1
+            if not valid():
+                rep.failures.append((b, f"acceptance boundary: gpu output {g}/{ga} not valid"))
+            continue
+        if ga != int(o["accepted"]):
+            rep.failures.append((b, f"acceptance: gpu {ga}, oracle {int(o['accepted'])} (gap {gap:.3g})"))
+            continue
+        if ga == 1:
+            rep.accepted += 1
+            if g == d:
+                rep.exact += 1
+            else:
+                rep.failures.append((b, f"accepted but gpu token {g} != draft {d}"))
+            continue
+        if o["status"] == 2:
+            if g == -1:
+                rep.exact += 1
+            else:
+                rep.failures.append((b, f"nothing to resample, gpu token {g}"))
+            continue
+        if o["threat"] * (1 + 1e-6) >= o["s1_low"] * (1 - 1e-6):
+            rep.exempt_race += 1
+            if not valid():
+                rep.failures.append((b, f"race boundary: gpu output {g} not valid"))
+            continue
+        if g == int(o["token"]):
+            rep.exact += 1
+        else:
+            rep.failures.append((b, f"residual draw: gpu {g}, oracle {int(o['token'])}"))
+    return rep

@@ -25,8 +25,8 @@ def L():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    for n in ("nucleus_sample", "nucleus_sample_rejection", "nucleus_workspace_bytes", "nucleus_strerror",
-              "nucleus_version", "nucleus_stream_read"):
+    for n in ("nucleus_sample", "nucleus_sample_rejection", "nucleus_spec_verify", "nucleus_workspace_bytes",
+              "nucleus_strerror", "nucleus_version", "nucleus_stream_read"):
         assert n in names
 
 
@@ -138,3 +138,24 @@ def test_rejection_host_side_argument_errors(L):
         assert _call_rej(L, opt=ctypes.byref(opt)) == EINVAL, field
     assert _call_rej(L, B=0) == 0
     assert _call_rej(L, B=0, logits=None, T=None, P=None, tok=None) == 0
+
+
+def _call_spec(L, P=1 << 20, Q=1 << 21, D=1 << 22, B=2, V=8, tok=1 << 23, acc=1 << 24, opt=None):
+    # Fake, never-dereferenced device addresses, as above.
+    return L.nucleus_spec_verify(P, Q, D, B, V, ctypes.c_uint64(0), ctypes.c_uint64(0), tok, acc, opt)
+
+
+def test_spec_host_side_argument_errors(L):
+    import nucleus_sampling_amd as ns
+
+    EINVAL = -1
+    for kw in (dict(P=None), dict(Q=None), dict(D=None), dict(tok=None), dict(B=-1), dict(V=0), dict(V=1 << 31),
+               dict(P=(1 << 20) + 2), dict(Q=(1 << 21) + 1), dict(D=(1 << 22) + 2), dict(acc=(1 << 24) + 1)):
+        assert _call_spec(L, **kw) == EINVAL, kw
+    for field, value in (("dtype", 1), ("row_stride", 9), ("flags", 4), ("out_min_kept_logit", 1 << 26),
+                         ("out_logprobs", 1 << 26)):
+        opt = ns._Options()
+        setattr(opt, field, value)
+        assert _call_spec(L, opt=ctypes.byref(opt)) == EINVAL, field
+    assert _call_spec(L, B=0) == 0
+    assert _call_spec(L, B=0, P=None, Q=None, D=None, tok=None) == 0

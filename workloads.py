@@ -131,3 +131,39 @@ def make(n: int, rows=None):
     logits = f32_to_bf16_bits(L) if DTYPES[n] == "bf16" else L
     return dict(logits=logits, dtype=DTYPES[n], temperature=T, top_p=P, top_k=K, min_p=MP,
                 seed=philox_seed(n), rows=ids, name=NAMES[n], B=len(ids), V=V)
+
+
+def make_draft(w: dict, noise: float = 0.7, keep_top: int = 64, seed: int = 0):
+    """A draft model's sampling distribution and its sampled tokens for the
+    rows of workload dict ``w`` (for speculative-decoding verification):
+    q = softmax((x + N(0, noise)) / Td) per row, Td = T (0.7 on greedy rows),
+    -inf logits get q = 0; odd rows are truncated to the draft's own top
+    ``keep_top`` tokens and renormalised (a draft that applies truncation).
+    The draft token of each row is drawn from q.  Returns (q float32 [B, V],
+    d int32 [B]).  Each row has its own PCG64 stream (seed, 77, row)."""
+    x = w["logits"]
+    x = bf16_bits_to_f32(x) if w["dtype"] == "bf16" else x
+    B, V = x.shape
+    q = np.zeros((B, V), np.float32)
+    d = np.zeros(B, np.int32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, 77, b])
+        T = float(w["temperature"][b])
+        Td = T if T > 0 and np.isfinite(T) else 0.7
+        row = x[b].astype(np.float64)
+        fin = np.isfinite(row)
+        z = np.where(fin, row + rng.normal(0.0, noise, V), -np.inf) / Td
+        if not fin.any():
+            z = rng.normal(0.0, 1.0, V)
+        z = z - z[np.isfinite(z)].max()
+        e = np.where(np.isfinite(z), np.exp(z), 0.0)
+        if b % 2 == 1 and keep_top < V:
+            cut = np.partition(e, V - keep_top)[V - keep_top]
+            e = np.where(e >= cut, e, 0.0)
+        qq = (e / e.sum()).astype(np.float32)
+        q[b] = qq
+        c = np.cumsum(qq.astype(np.float64))
+        d[b] = min(int(np.searchsorted(c, rng.random() * c[-1], side="right")), V - 1)
+        while d[b] > 0 and qq[d[b]] == 0.0:  # land on a token the draft can propose
+            d[b] -= 1
+    return q, d
