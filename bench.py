@@ -138,6 +138,7 @@ def main():
                     help="force one of the library's paths (for comparisons; the headline uses the default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rejection", action="store_true", help="skip timing the rejection sampler")
+    ap.add_argument("--no-spec", action="store_true", help="skip timing speculative verification")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-steps", action="store_true", help="only run the timed loop (for rocprofv3)")
     ap.add_argument("--pmc-calibrate", action="store_true",
@@ -269,6 +270,40 @@ def main():
                "passes_per_row_mean": 2.0 * float(rr.mean()) if rr.numel() else 0.0,
                "note": "top-k off; every row reads its logits 2 x rounds times"}
 
+    # Speculative verification (nucleus_spec_verify) of a synthetic draft
+    # against the kept distribution of the first buffer's rows.
+    spec = None
+    if not args.no_spec:
+        q_np, d_np = workloads.make_draft(w, seed=args.workload)
+        qd = torch.from_numpy(q_np).to(dev)
+        dd = torch.from_numpy(d_np).to(dev)
+        pres = ns.sample(bufs[0], T, P, K, MP, seed=w["seed"], step=0, want_probs=True, stream=stream)
+        sout = ns.SpecResult(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+        for i in range(args.warmup):
+            ns.spec_verify(pres.probs, qd, dd, seed=w["seed"], step=i, out=sout, stream=stream)
+        torch.cuda.synchronize()
+        ss = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        se = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        acc_rows = 0
+        for i in range(args.steps):
+            ss[i].record(stream)
+            ns.spec_verify(pres.probs, qd, dd, seed=w["seed"], step=args.warmup + i, out=sout, stream=stream)
+            se[i].record(stream)
+            if i == 0:
+                acc_rows = int(sout.accepted.sum())
+        torch.cuda.synchronize()
+        sp_ms = [a.elapsed_time(e) for a, e in zip(ss, se)]
+        sp_avg = float(np.mean(sp_ms))
+        # Algorithmic bytes: a rejected row reads its p and q rows (8 B per token).
+        sp_bytes = (B - acc_rows) * V * 8 + B * 8
+        spec = {"kernel": "spec_kernel", "avg_launch_ms": sp_avg, "median_launch_ms": float(np.median(sp_ms)),
+                "rows_per_s": B / (sp_avg * 1e-3), "accepted_rows": acc_rows,
+                "algorithmic_bytes_per_launch": sp_bytes,
+                "achieved_gbps": sp_bytes / (sp_avg * 1e-3) / 1e9,
+                "frac_of_hbm_peak": sp_bytes / (sp_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                "note": "draft q = softmax of noisy logits (odd rows truncated to 64 tokens); p from nucleus_sample"}
+        del qd, pres
+
     avg_ms = float(np.mean(per_launch_ms))
     med_ms = float(np.median(per_launch_ms))
     achieved = batch_bytes / (avg_ms * 1e-3) / 1e9
@@ -303,6 +338,7 @@ def main():
         "stream_read": {"gbps": stream_gbps, "avg_ms": read_ms, "frac_of_peak": stream_gbps / PEAK_HBM_GBPS,
                         "sampler_vs_stream": achieved / stream_gbps},
         "rejection": rej,
+        "speculative": spec,
         "wall_s": wall,
         "kernel_hash": kernel_hash(),
     }

@@ -210,16 +210,25 @@ int nucleus_sample_rejection(const void* logits, int64_t B, int64_t V, const flo
  *               d is outside [0, V) or p - q has no positive entry (a target
  *               row error leaves p all zero).
  * out_accepted  device [B] int32, or NULL: 1 if the draft token was accepted.
- * opt           NULL, or options with stream and seeds used; dtype must be
- *               NUCLEUS_F32, row_stride 0 or V, flags 0, out_min_kept_logit and
- *               out_logprobs NULL (NUCLEUS_EINVAL otherwise).
+ * opt           required for B > 0: stream, seeds and the workspace (at least
+ *               nucleus_spec_workspace_bytes(B, V) bytes, 256-byte aligned,
+ *               no initial value needed; NUCLEUS_EWORKSPACE otherwise) are
+ *               used; dtype must be NUCLEUS_F32, row_stride 0 or V, flags 0,
+ *               out_min_kept_logit and out_logprobs NULL (NUCLEUS_EINVAL
+ *               otherwise).
  *
- * Returns NUCLEUS_OK or a negative code.  Asynchronous on opt->stream.  An
- * accepted row reads two floats; a rejected row reads its p and q rows once.
+ * Returns NUCLEUS_OK or a negative code.  Asynchronous on opt->stream; calls
+ * that may overlap need different workspaces.  An accepted row reads two
+ * floats; a rejected row reads its p and q rows once, in 8192-token chunks
+ * spread over the device.
  */
 int nucleus_spec_verify(const float* target_probs, const float* draft_probs, const int32_t* draft_token,
                         int64_t B, int64_t V, uint64_t seed, uint64_t step, int32_t* out_token,
                         int32_t* out_accepted, const nucleus_options* opt);
+
+/* Device workspace, in bytes, that nucleus_spec_verify needs: 8 bytes per
+ * 8192-token chunk of every row.  0 for invalid shapes. */
+size_t nucleus_spec_workspace_bytes(int64_t B, int64_t V);
 
 /* Device workspace, in bytes, that nucleus_sample needs for a batch of this
  * shape and dtype with no flags: batches under 128 rows of at most

@@ -65,6 +65,8 @@ def lib():
         L.nucleus_sample_rejection.restype = ctypes.c_int
         L.nucleus_spec_verify.argtypes = [vp, vp, vp, i64, i64, u64, u64, vp, vp, ctypes.POINTER(_Options)]
         L.nucleus_spec_verify.restype = ctypes.c_int
+        L.nucleus_spec_workspace_bytes.argtypes = [i64, i64]
+        L.nucleus_spec_workspace_bytes.restype = ctypes.c_size_t
         L.nucleus_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32]
         L.nucleus_workspace_bytes.restype = ctypes.c_size_t
         L.nucleus_workspace_bytes_for.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32]
@@ -272,7 +274,7 @@ class SpecResult(NamedTuple):
 
 
 def spec_verify(target_probs: torch.Tensor, draft_probs: torch.Tensor, draft_token, seed: int = 0, step: int = 0, *,
-                seeds=None, out: Optional[SpecResult] = None,
+                seeds=None, out: Optional[SpecResult] = None, workspace: Optional[torch.Tensor] = None,
                 stream: Optional[torch.cuda.Stream] = None) -> SpecResult:
     """Speculative acceptance (``nucleus_spec_verify``): accept each row's
     draft token with probability min(1, p/q), else draw from the normalised
@@ -293,9 +295,14 @@ def spec_verify(target_probs: torch.Tensor, draft_probs: torch.Tensor, draft_tok
     if out is None:
         out = SpecResult(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
     s = stream if stream is not None else torch.cuda.current_stream(dev)
+    need = lib().nucleus_spec_workspace_bytes(B, V)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = workspace_for(dev, s, need)
     opt = _Options()
     opt.stream = s.cuda_stream
     opt.seeds = S.data_ptr() if S is not None else None
+    opt.workspace = workspace.data_ptr() if (workspace is not None and need) else None
+    opt.workspace_bytes = (workspace.numel() * workspace.element_size()) if (workspace is not None and need) else 0
     rc = lib().nucleus_spec_verify(Pt.data_ptr() if B else None, Qt.data_ptr() if B else None,
                                    D.data_ptr() if B else None, B, V, ctypes.c_uint64(seed), ctypes.c_uint64(step),
                                    out.token.data_ptr() if B else None, out.accepted.data_ptr() if B else None,

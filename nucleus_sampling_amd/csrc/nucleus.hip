@@ -291,6 +291,12 @@ int nucleus_sample_rejection(const void* logits, int64_t B, int64_t V, const flo
     return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
 }
 
+size_t nucleus_spec_workspace_bytes(int64_t B, int64_t V)
+{
+    if (B < 0 || V < 1 || V >= (int64_t(1) << 31)) return 0;
+    return align256((size_t)B * (size_t)((V + kSpecChunk - 1) / kSpecChunk) * 8);
+}
+
 int nucleus_spec_verify(const float* target_probs, const float* draft_probs, const int32_t* draft_token, int64_t B,
                         int64_t V, uint64_t seed, uint64_t step, int32_t* out_token, int32_t* out_accepted,
                         const nucleus_options* opt)
@@ -304,6 +310,10 @@ int nucleus_spec_verify(const float* target_probs, const float* draft_probs, con
     if (!aligned(target_probs) || !aligned(draft_probs) || !aligned(draft_token) || !aligned(out_token) ||
         (out_accepted && !aligned(out_accepted)) || (opt && opt->seeds && !aligned(opt->seeds)))
         return NUCLEUS_EINVAL;
+    const size_t need = nucleus_spec_workspace_bytes(B, V);
+    if (!opt || !opt->workspace || opt->workspace_bytes < need || (uintptr_t)opt->workspace % 256)
+        return NUCLEUS_EWORKSPACE;
+    if (B * ((V + kSpecChunk - 1) / kSpecChunk) >= (int64_t(1) << 31)) return NUCLEUS_EINVAL;
     const int dev_rc = check_device();
     if (dev_rc != NUCLEUS_OK) return dev_rc;
     SpecParams sp = {};
@@ -320,8 +330,11 @@ int nucleus_spec_verify(const float* target_probs, const float* draft_probs, con
     sp.out_token = out_token;
     sp.out_accepted = out_accepted;
     sp.vec = (V % 4 == 0) && (uintptr_t)target_probs % 16 == 0 && (uintptr_t)draft_probs % 16 == 0;
+    sp.C = (int)((V + kSpecChunk - 1) / kSpecChunk);
+    sp.part = (uint64_t*)opt->workspace;
     hipStream_t s = opt ? (hipStream_t)opt->stream : nullptr;
-    hipLaunchKernelGGL(spec_kernel, dim3((unsigned)B), dim3(kSpecThreads), 0, s, sp);
+    hipLaunchKernelGGL(spec_chunk_kernel, dim3((unsigned)(B * sp.C)), dim3(kSpecThreads), 0, s, sp);
+    hipLaunchKernelGGL(spec_finish_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s, sp);
     return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
 }
 

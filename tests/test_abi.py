@@ -159,3 +159,10 @@ def test_spec_host_side_argument_errors(L):
         assert _call_spec(L, opt=ctypes.byref(opt)) == EINVAL, field
     assert _call_spec(L, B=0) == 0
     assert _call_spec(L, B=0, P=None, Q=None, D=None, tok=None) == 0
+    assert _call_spec(L) == -2  # no workspace
+    opt = ns._Options()
+    opt.workspace, opt.workspace_bytes = 1 << 27, 8  # too small
+    assert _call_spec(L, opt=ctypes.byref(opt)) == -2
+    assert L.nucleus_spec_workspace_bytes(256, 128256) == 256 * 16 * 8
+    assert L.nucleus_spec_workspace_bytes(3, 1) == 256
+    assert L.nucleus_spec_workspace_bytes(-1, 8) == 0 and L.nucleus_spec_workspace_bytes(2, 0) == 0
