@@ -95,6 +95,8 @@ class Oracle:
         L.oracle_spec_verify.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, u64, vp, u64,
                                          ctypes.c_double, i64, i64, vp]
         L.oracle_spec_verify.restype = ctypes.c_int
+        L.oracle_preprocess.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp]
+        L.oracle_preprocess.restype = ctypes.c_int
         L.oracle_eval_cut.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_float, ctypes.c_float, i32,
                                       ctypes.c_float, u64, u64, ctypes.c_double, vp, vp]
         L.oracle_eval_cut.restype = ctypes.c_int
@@ -231,6 +233,27 @@ class Oracle:
                 run(sp)
         return out
 
+    def preprocess(self, logits, hist=None, repetition=None, frequency=None, presence=None, allowed=None):
+        """The pre-chain (oracle_preprocess): penalised, masked fp32 logits
+        [B, V].  ``hist`` [B, H] int32 (-1 padded), penalties [B] float32,
+        ``allowed`` [B, ceil(V/32)] uint32 bit masks."""
+        logits = np.ascontiguousarray(logits)
+        B, V = logits.shape
+        Hs = None if hist is None else np.ascontiguousarray(hist, dtype=np.int32).reshape(B, -1)
+        H = 0 if Hs is None else Hs.shape[1]
+
+        def vec(a):
+            return None if a is None else np.ascontiguousarray(a, dtype=np.float32).reshape(B)
+
+        R, F, Pp = vec(repetition), vec(frequency), vec(presence)
+        M = None if allowed is None else np.ascontiguousarray(allowed, dtype=np.uint32).reshape(B, (V + 31) // 32)
+        out = np.empty((B, V), np.float32)
+        rc = self.L.oracle_preprocess(_ptr(logits), _dtype_code(logits), B, V, V, _ptr(Hs), H, _ptr(R), _ptr(F),
+                                      _ptr(Pp), _ptr(M), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_preprocess rejected its arguments")
+        return out
+
     def eval_cut(self, logits_row, row, temperature, top_p, top_k, min_p, seed, step, cut, want_probs=False):
         """Judge a keep threshold chosen elsewhere on one row (see oracle_eval_cut)."""
         logits_row = np.ascontiguousarray(logits_row)
@@ -304,6 +327,10 @@ def sample_rejection(*a, **k):
 
 def spec_verify(*a, **k):
     return default().spec_verify(*a, **k)
+
+
+def preprocess(*a, **k):
+    return default().preprocess(*a, **k)
 
 
 def eval_cut(*a, **k):

@@ -764,3 +764,54 @@ int oracle_spec_verify(const void* logits, int dtype, int64_t B, int64_t V, int6
     free(p);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* The pre-chain ("Top-p (Nucleus) Sampling, in depth", "Where top-p sits in  */
+/* the sampler chain"; "What do temperature, top-k and top-p ...", "What      */
+/* interviewers probe next"): penalties on the raw logits, then the grammar   */
+/* mask, before temperature and the filters.  The pages name the penalties   */
+/* but give no formulas; the readings adopted are the common definitions:    */
+/*                                                                          */
+/*   c_i     = occurrences of token i in the row's history (duplicates count) */
+/*   repetition (rho > 0, 1 = off), for c_i > 0:                             */
+/*             x <- x / rho if x > 0, else x * rho                            */
+/*   frequency (a_f) and presence (a_p), for c_i > 0, after repetition:       */
+/*             x <- x - (a_f * c_i + a_p)                                     */
+/*   mask    : token i allowed iff bit (i mod 32) of word i / 32 is set;      */
+/*             a disallowed token becomes -inf (after the penalties)          */
+/*                                                                          */
+/* Every step is one IEEE float operation in the order written (no fused     */
+/* multiply-add), so the processed logits are exact fp32 values any          */
+/* implementation reproduces; the sampler then runs on them unchanged.       */
+/* ------------------------------------------------------------------------ */
+int oracle_preprocess(const void* logits, int dtype, int64_t B, int64_t V, int64_t stride, const int32_t* hist,
+                      int64_t H, const float* repetition, const float* frequency, const float* presence,
+                      const uint32_t* allowed, float* out)
+{
+    if (V < 1 || B < 0 || stride < V || H < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    const int64_t words = (V + 31) / 32;
+    int32_t* count = (int32_t*)calloc((size_t)V, sizeof(int32_t));
+    for (int64_t b = 0; b < B; ++b) {
+        memset(count, 0, (size_t)V * sizeof(int32_t));
+        for (int64_t h = 0; h < H && hist; ++h) {
+            const int32_t tok = hist[b * H + h];
+            if (tok >= 0 && tok < V) count[tok] += 1;  /* -1 pads; ids outside [0, V) are ignored */
+        }
+        const float rho = repetition ? repetition[b] : 1.0f;
+        const float af = frequency ? frequency[b] : 0.0f;
+        const float ap = presence ? presence[b] : 0.0f;
+        for (int64_t i = 0; i < V; ++i) {
+            float x = (float)widen(logits, dtype, b * stride + i);
+            if (count[i] > 0) {
+                volatile float y = x > 0.0f ? x / rho : x * rho;
+                volatile float pen = af * (float)count[i];
+                pen = pen + ap;
+                x = y - pen;
+            }
+            if (allowed && !((allowed[b * words + i / 32] >> (i % 32)) & 1u)) x = -INFINITY;
+            out[b * V + i] = x;
+        }
+    }
+    free(count);
+    return 0;
+}

@@ -686,6 +686,79 @@ def check_spec_special(O):
     assert (out["status"] == 1).all() and (out["token"] == -1).all()
 
 
+
+
+# --------------------------------------------------------------------------
+# The pre-chain: penalties and the grammar mask ("Top-p (Nucleus) Sampling,
+# in depth", "Where top-p sits in the sampler chain"; "What do temperature,
+# top-k and top-p ...", "What interviewers probe next")
+# --------------------------------------------------------------------------
+def check_preprocess_values(O):
+    """Values worked by hand from the definitions: repetition 2, frequency
+    0.25, presence 0.5; history [0, 1, 1, 3]; token 4 disallowed.
+      token 0: x = 2 > 0 -> 2 / 2 = 1; minus 0.25 * 1 + 0.5 -> 0.25
+      token 1: x = -1 -> -1 * 2 = -2; seen twice: minus 0.25 * 2 + 0.5 -> -3
+      token 3: x = 3 -> 1.5; minus 0.75 -> 0.75
+      tokens 2 and 5 are not in the history; token 4 is masked."""
+    x = np.asarray([[2.0, -1.0, 0.5, 3.0, -2.0, 1.0]], np.float32)
+    out = O.preprocess(x, hist=np.asarray([[0, 1, 1, 3, -1, 17]]), repetition=[2.0], frequency=[0.25],
+                       presence=[0.5], allowed=np.asarray([[0b101111]], np.uint32))
+    assert np.array_equal(out, np.asarray([[0.25, -3.0, 0.5, 0.75, -np.inf, 1.0]], np.float32)), out
+    # Bit i of word i / 32: token 33 is bit 1 of the second word.
+    x = np.zeros((1, 40), np.float32)
+    m = np.asarray([[0xFFFFFFFF, 0xFFFFFFFD]], np.uint32)
+    out = O.preprocess(x, allowed=m)
+    assert np.isneginf(out[0, 33]) and np.isfinite(out[0, np.arange(40) != 33]).all()
+
+
+def check_preprocess_identity_and_invariants(O, seed=12):
+    """No penalty and no mask changes nothing, bit for bit (bf16 widened
+    exactly); tokens outside the history keep their logits; with rho >= 1 and
+    non-negative a_f, a_p a history token never rises."""
+    rng = np.random.default_rng(seed)
+    B, V, H = 6, 300, 40
+    x = rng.normal(0, 3, (B, V)).astype(np.float32)
+    hist = rng.integers(-1, V, (B, H)).astype(np.int32)
+    out = O.preprocess(x, hist=hist, repetition=np.ones(B), frequency=np.zeros(B), presence=np.zeros(B))
+    assert np.array_equal(out.view(np.uint32), x.view(np.uint32))
+    import workloads
+    xb = workloads.f32_to_bf16_bits(x)
+    assert np.array_equal(O.preprocess(xb), workloads.bf16_bits_to_f32(xb))
+    rep = rng.uniform(1.0, 2.0, B).astype(np.float32)
+    fr = rng.uniform(0, 1, B).astype(np.float32)
+    pr = rng.uniform(0, 1, B).astype(np.float32)
+    out = O.preprocess(x, hist=hist, repetition=rep, frequency=fr, presence=pr)
+    for b in range(B):
+        seen = np.zeros(V, bool)
+        seen[hist[b][hist[b] >= 0]] = True
+        assert np.array_equal(out[b, ~seen], x[b, ~seen])
+        assert (out[b, seen] <= x[b, seen]).all()
+        # Presence alone lowers every seen token by exactly a_p (where that is exact).
+    one = O.preprocess(x[:1], hist=np.asarray([[5, 5, 5]]), frequency=[0.5])
+    assert one[0, 5] == np.float32(x[0, 5] - np.float32(1.5))
+
+
+def check_chain_order(O):
+    """Masks come before top-p: a nucleus never holds a forbidden token, even
+    when the forbidden tokens carry most of the mass ("Where top-p sits in the
+    sampler chain").  Repetition penalties act on raw logits and change the
+    greedy choice too ("What interviewers probe next")."""
+    x = np.asarray([[5.0, 4.8, 1.0, 0.9, 0.5, 0.2, 0.1, 0.0]], np.float32)
+    allowed = np.asarray([[0b11111100]], np.uint32)  # the two heavy tokens are forbidden
+    xp = O.preprocess(x, allowed=allowed)
+    n = 4000
+    out, _ = O.sample(np.tile(xp, (n, 1)), np.ones(n), np.full(n, 0.5), seed=8)
+    assert (out["status"] == 0).all() and (out["token"] >= 2).all()
+    assert (out["keep_count"] >= 1).all()
+    raw, _ = O.sample(np.tile(x, (n, 1)), np.ones(n), np.full(n, 0.5), seed=8)
+    assert (raw["token"] < 2).all()  # the same chain without the mask keeps only forbidden tokens
+    g = np.asarray([[3.0, 2.5, 1.0]], np.float32)
+    gp = O.preprocess(g, hist=np.asarray([[0]]), repetition=[2.0])
+    assert O.sample(g, [0.0], [1.0])[0]["token"][0] == 0
+    assert O.sample(gp, [0.0], [1.0])[0]["token"][0] == 1
+
+
 ALL_FAST_CHECKS = [check_worked_examples, check_order_counterexample, check_special_cases, check_invariants,
                    check_exp1, check_race_reproducible, check_logprobs, check_row_seeds, check_rejection_pages,
-                   check_rejection_law, check_rejection_is_the_race, check_spec_law, check_spec_special]
+                   check_rejection_law, check_rejection_is_the_race, check_spec_law, check_spec_special,
+                   check_preprocess_values, check_preprocess_identity_and_invariants, check_chain_order]

@@ -48,6 +48,11 @@ MUTATIONS = [
     ("speculative acceptance reversed", "if (o->u * o->q_draft < o->p_draft) {", "if (o->u * o->p_draft < o->q_draft) {"),
     ("speculative acceptance ignores q", "if (o->u * o->q_draft < o->p_draft) {", "if (o->u < o->p_draft) {"),
     ("speculative residual reversed", "const double r = p[i] - (double)q[i];", "const double r = (double)q[i] - p[i];"),
+    ("repetition divides negative logits", "volatile float y = x > 0.0f ? x / rho : x * rho;",
+     "volatile float y = x / rho;"),
+    ("duplicates counted once", "if (tok >= 0 && tok < V) count[tok] += 1;", "if (tok >= 0 && tok < V) count[tok] = 1;"),
+    ("presence per occurrence", "pen = pen + ap;", "pen = pen + ap * (float)count[i];"),
+    ("mask bits reversed", "(allowed[b * words + i / 32] >> (i % 32)) & 1u", "(allowed[b * words + i / 32] >> (31 - i % 32)) & 1u"),
 ]
 
 

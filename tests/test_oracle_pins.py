@@ -93,3 +93,15 @@ def test_spec_law(oracle_lib):
 
 def test_spec_special(oracle_lib):
     P.check_spec_special(oracle_lib.default())
+
+
+def test_preprocess_values(oracle_lib):
+    P.check_preprocess_values(oracle_lib.default())
+
+
+def test_preprocess_identity_and_invariants(oracle_lib):
+    P.check_preprocess_identity_and_invariants(oracle_lib.default())
+
+
+def test_chain_order(oracle_lib):
+    P.check_chain_order(oracle_lib.default())
