@@ -139,6 +139,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rejection", action="store_true", help="skip timing the rejection sampler")
     ap.add_argument("--no-spec", action="store_true", help="skip timing speculative verification")
+    ap.add_argument("--no-prechain", action="store_true", help="skip timing the pre-chain")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-steps", action="store_true", help="only run the timed loop (for rocprofv3)")
     ap.add_argument("--pmc-calibrate", action="store_true",
@@ -304,6 +305,36 @@ def main():
                 "note": "draft q = softmax of noisy logits (odd rows truncated to 64 tokens); p from nucleus_sample"}
         del qd, pres
 
+    # The same batch with the pre-chain (history of 256 tokens per row,
+    # penalties, a grammar mask forbidding ~20% of the vocabulary).
+    prech = None
+    if not args.no_prechain:
+        pc = workloads.make_prechain(w, hist_len=256, seed=args.workload)
+        hist_d = torch.from_numpy(pc["history"]).to(dev)
+        rp_d, fp_d, pp_d = (torch.from_numpy(pc[k]).to(dev) for k in ("repetition", "frequency", "presence"))
+        am_d = torch.from_numpy(pc["allowed"].view(np.int32)).to(dev)
+
+        def pstep(i):
+            ns.sample(bufs[i % nbuf], T, P, K, MP, seed=w["seed"], step=i, out=out, stream=stream, history=hist_d,
+                      repetition_penalty=rp_d, frequency_penalty=fp_d, presence_penalty=pp_d, allowed_mask=am_d)
+
+        for i in range(args.warmup):
+            pstep(i)
+        torch.cuda.synchronize()
+        ps_ = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        pe_ = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        for i in range(args.steps):
+            ps_[i].record(stream)
+            pstep(args.warmup + i)
+            pe_[i].record(stream)
+        torch.cuda.synchronize()
+        pc_ms = [a.elapsed_time(e) for a, e in zip(ps_, pe_)]
+        pc_avg = float(np.mean(pc_ms))
+        prech = {"kernel": "row_kernel (pre-chain)", "avg_launch_ms": pc_avg, "median_launch_ms": float(np.median(pc_ms)),
+                 "rows_per_s": B / (pc_avg * 1e-3), "logits_gbps": batch_bytes / (pc_avg * 1e-3) / 1e9,
+                 "frac_of_hbm_peak": batch_bytes / (pc_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                 "note": "history 256 tokens per row, repetition/frequency/presence penalties, mask ~20% forbidden"}
+
     avg_ms = float(np.mean(per_launch_ms))
     med_ms = float(np.median(per_launch_ms))
     achieved = batch_bytes / (avg_ms * 1e-3) / 1e9
@@ -339,6 +370,7 @@ def main():
                         "sampler_vs_stream": achieved / stream_gbps},
         "rejection": rej,
         "speculative": spec,
+        "prechain": prech,
         "wall_s": wall,
         "kernel_hash": kernel_hash(),
     }

@@ -116,6 +116,27 @@ typedef struct nucleus_options {
                                     (x_i - m)/T - ln S_keep on kept tokens, -inf outside the
                                     nucleus; 0 / -inf for greedy rows; NaN on a row error.
                                     Finite for kept tokens whose probability underflows. */
+    /* Since version 240: the pre-chain, applied to the raw logits before
+     * everything above ("Top-p (Nucleus) Sampling, in depth", "Where top-p
+     * sits in the sampler chain"; penalties on raw logits so they change the
+     * greedy choice too, "What do temperature, top-k and top-p ...", "What
+     * interviewers probe next").  With c_i the occurrences of token i in the
+     * row's history, for c_i > 0:  y = x / rho if x > 0 else x * rho, then
+     * x' = y - (a_f * c_i + a_p); then x' = -inf where the mask forbids i.
+     * Each step is one fp32 operation in that order (no fused multiply-add).
+     * The sampler (validation included) sees only x'.  Any of these fields
+     * set selects the one-workgroup-per-row path (NUCLEUS_FLAG_SPLIT_ROWS and
+     * NUCLEUS_FLAG_ROW_RACE are then NUCLEUS_EINVAL); NULL / 0 leaves the
+     * logits as they are. */
+    const int32_t* history;            /* optional device [B, history_len] int32: each row's earlier
+                                          tokens, -1 padded (ids outside [0, V) are ignored) */
+    int64_t history_len;               /* 0 .. 1024 */
+    const float* repetition_penalty;   /* optional device [B]: rho (> 0; 1 = off) */
+    const float* frequency_penalty;    /* optional device [B]: a_f (0 = off) */
+    const float* presence_penalty;     /* optional device [B]: a_p (0 = off) */
+    const uint32_t* allowed_mask;      /* optional device [B, ceil(V/32)] uint32: token i allowed iff
+                                          bit (i mod 32) of word i / 32 is set (a grammar / JSON
+                                          constraint); needs V <= 175104 */
 } nucleus_options;
 
 /*

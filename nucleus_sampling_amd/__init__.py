@@ -45,6 +45,12 @@ class _Options(ctypes.Structure):
         ("out_min_kept_logit", ctypes.c_void_p),
         ("seeds", ctypes.c_void_p),
         ("out_logprobs", ctypes.c_void_p),
+        ("history", ctypes.c_void_p),
+        ("history_len", ctypes.c_int64),
+        ("repetition_penalty", ctypes.c_void_p),
+        ("frequency_penalty", ctypes.c_void_p),
+        ("presence_penalty", ctypes.c_void_p),
+        ("allowed_mask", ctypes.c_void_p),
     ]
 
 
@@ -147,7 +153,8 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
            want_probs: bool = False, want_min_kept: bool = False, out: Optional[SampleResult] = None,
            workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
            single_workgroup: bool = False, split_rows: bool = False, row_race: bool = False,
-           seeds=None, want_logprobs: bool = False) -> SampleResult:
+           seeds=None, want_logprobs: bool = False, history=None, repetition_penalty=None,
+           frequency_penalty=None, presence_penalty=None, allowed_mask=None) -> SampleResult:
     """Sample one token per row of ``logits`` [B, V] (float32 or bfloat16 on a
     gfx950 device; rows may be strided, the last dimension must be dense).
 
@@ -162,6 +169,12 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     large-batch path (a workgroup per row, the race spread over chunks)
     whatever the batch size.  All give the same results, bit for bit; they
     exist for verification.
+
+    The pre-chain (``include/nucleus.h``): ``history`` [B, H] token ids
+    (-1 padded, H <= 1024) with ``repetition_penalty`` / ``frequency_penalty``
+    / ``presence_penalty`` [B], and ``allowed_mask`` [B, ceil(V/32)] 32-bit
+    words (bit i % 32 of word i // 32 allows token i), applied to the raw
+    logits before the chain.
     """
     if logits.dim() != 2:
         raise ValueError("logits must be [B, V]")
@@ -177,6 +190,18 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     K = _vec(top_k, B, torch.int32, "top_k", dev)
     MP = _vec(min_p, B, torch.float32, "min_p", dev)
     S = _seeds(seeds, B, dev)
+    Hs = None
+    if history is not None:
+        Hs = torch.as_tensor(history).to(dev).to(torch.int32).reshape(B, -1).contiguous()
+    RP = _vec(repetition_penalty, B, torch.float32, "repetition_penalty", dev)
+    FP = _vec(frequency_penalty, B, torch.float32, "frequency_penalty", dev)
+    PP = _vec(presence_penalty, B, torch.float32, "presence_penalty", dev)
+    AM = None
+    if allowed_mask is not None:
+        am = torch.as_tensor(allowed_mask)
+        if am.dtype == torch.uint32:
+            am = am.view(torch.int32)
+        AM = am.to(dev).to(torch.int32).reshape(B, (V + 31) // 32).contiguous()
     if out is None:
         out = SampleResult(
             torch.empty(B, dtype=torch.int32, device=dev),
@@ -201,6 +226,13 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     opt.out_min_kept_logit = out.min_kept_logit.data_ptr() if out.min_kept_logit is not None else None
     opt.seeds = S.data_ptr() if S is not None else None
     opt.out_logprobs = out.logprobs.data_ptr() if out.logprobs is not None else None
+    if Hs is not None and Hs.shape[1] > 0:
+        opt.history = Hs.data_ptr()
+        opt.history_len = Hs.shape[1]
+    opt.repetition_penalty = RP.data_ptr() if RP is not None else None
+    opt.frequency_penalty = FP.data_ptr() if FP is not None else None
+    opt.presence_penalty = PP.data_ptr() if PP is not None else None
+    opt.allowed_mask = AM.data_ptr() if AM is not None else None
 
     def ptr(t):
         return None if t is None else t.data_ptr()

@@ -116,11 +116,18 @@ bool aligned(const T* p)
     return ((uintptr_t)p % alignof(T)) == 0;
 }
 
+// Whether a call asks for the pre-chain (penalties or a grammar mask).
+bool has_prechain(const nucleus_options* opt)
+{
+    return opt && (opt->allowed_mask || opt->history_len != 0 || opt->history || opt->repetition_penalty ||
+                   opt->frequency_penalty || opt->presence_penalty);
+}
+
 }  // namespace
 
 extern "C" {
 
-int nucleus_version(void) { return 230; }
+int nucleus_version(void) { return 240; }
 
 const char* nucleus_strerror(int code)
 {
@@ -154,7 +161,19 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     const int64_t stride = (opt && opt->row_stride) ? opt->row_stride : V;
     if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || stride < V) return NUCLEUS_EINVAL;
     if (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16) return NUCLEUS_EINVAL;
-    const int path = choose_path(B, V, opt ? opt->flags : 0);
+    const bool pre = has_prechain(opt);
+    if (pre) {
+        if (opt->history_len < 0 || opt->history_len > kHistMax || (opt->history_len > 0 && !opt->history))
+            return NUCLEUS_EINVAL;
+        if (opt->allowed_mask && (V + 31) / 32 > kMaskWordsMax) return NUCLEUS_EINVAL;
+        if (opt->flags & (NUCLEUS_FLAG_SPLIT_ROWS | NUCLEUS_FLAG_ROW_RACE)) return NUCLEUS_EINVAL;
+        if ((opt->history && !aligned(opt->history)) || (opt->repetition_penalty && !aligned(opt->repetition_penalty)) ||
+            (opt->frequency_penalty && !aligned(opt->frequency_penalty)) ||
+            (opt->presence_penalty && !aligned(opt->presence_penalty)) ||
+            (opt->allowed_mask && !aligned(opt->allowed_mask)))
+            return NUCLEUS_EINVAL;
+    }
+    const int path = pre ? (choose_path(B, V, opt->flags) < 0 ? -1 : kPathFused) : choose_path(B, V, opt ? opt->flags : 0);
     if (path < 0) return NUCLEUS_EINVAL;
     if (B == 0) return NUCLEUS_OK;
     if (!logits || !temperature || !top_p || !out_token || !out_keep_count) return NUCLEUS_EINVAL;
@@ -189,6 +208,12 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     p.out_min_kept = opt ? opt->out_min_kept_logit : nullptr;
     p.seeds = opt ? opt->seeds : nullptr;
     p.out_logprobs = opt ? opt->out_logprobs : nullptr;
+    p.hist = pre ? opt->history : nullptr;
+    p.hist_len = pre ? opt->history_len : 0;
+    p.rep_pen = pre ? opt->repetition_penalty : nullptr;
+    p.freq_pen = pre ? opt->frequency_penalty : nullptr;
+    p.pres_pen = pre ? opt->presence_penalty : nullptr;
+    p.allowed = pre ? opt->allowed_mask : nullptr;
     const size_t vec_bytes = dtype == NUCLEUS_F32 ? 16 : 8;
     p.vec_in = ((uintptr_t)logits % vec_bytes == 0) && ((size_t)stride * esz) % vec_bytes == 0;
 
@@ -240,7 +265,11 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
         }
     } else {
         const RowWork none = {};
-        if (dtype == NUCLEUS_F32)
+        if (pre && dtype == NUCLEUS_F32)
+            hipLaunchKernelGGL((row_kernel<kF32, false, true>), dim3((unsigned)B), dim3(kRowThreads), 0, s, p, none);
+        else if (pre)
+            hipLaunchKernelGGL((row_kernel<kBF16, false, true>), dim3((unsigned)B), dim3(kRowThreads), 0, s, p, none);
+        else if (dtype == NUCLEUS_F32)
             hipLaunchKernelGGL((row_kernel<kF32, false>), dim3((unsigned)B), dim3(kRowThreads), 0, s, p, none);
         else
             hipLaunchKernelGGL((row_kernel<kBF16, false>), dim3((unsigned)B), dim3(kRowThreads), 0, s, p, none);
@@ -256,7 +285,7 @@ int nucleus_sample_rejection(const void* logits, int64_t B, int64_t V, const flo
     const int64_t stride = (opt && opt->row_stride) ? opt->row_stride : V;
     if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || stride < V) return NUCLEUS_EINVAL;
     if (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16) return NUCLEUS_EINVAL;
-    if (opt && (opt->flags || opt->out_min_kept_logit || opt->out_logprobs)) return NUCLEUS_EINVAL;
+    if (opt && (opt->flags || opt->out_min_kept_logit || opt->out_logprobs || has_prechain(opt))) return NUCLEUS_EINVAL;
     if (B == 0) return NUCLEUS_OK;
     if (!logits || !temperature || !top_p || !out_token) return NUCLEUS_EINVAL;
     const size_t esz = dtype == NUCLEUS_F32 ? 4 : 2;
@@ -303,7 +332,7 @@ int nucleus_spec_verify(const float* target_probs, const float* draft_probs, con
 {
     if (B < 0 || V < 1 || V >= (int64_t(1) << 31)) return NUCLEUS_EINVAL;
     if (opt && ((opt->row_stride && opt->row_stride != V) || opt->dtype != NUCLEUS_F32 || opt->flags ||
-                opt->out_min_kept_logit || opt->out_logprobs))
+                opt->out_min_kept_logit || opt->out_logprobs || has_prechain(opt)))
         return NUCLEUS_EINVAL;
     if (B == 0) return NUCLEUS_OK;
     if (!target_probs || !draft_probs || !draft_token || !out_token) return NUCLEUS_EINVAL;

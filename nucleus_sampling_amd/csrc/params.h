@@ -23,6 +23,13 @@ struct Params {
     int vec_in;               // rows start 16-byte (f32) / 8-byte (bf16) aligned
     const uint64_t* seeds;    // [B] per-row race keys, or null (every row uses seed_lo/hi)
     float* out_logprobs;      // [B, V] or null
+    // The pre-chain (penalties, grammar mask); read only by row_kernel<..., true>.
+    const int32_t* hist;      // [B, hist_len] token ids, -1 padded, or null
+    int64_t hist_len;
+    const float* rep_pen;     // [B] or null (1)
+    const float* freq_pen;    // [B] or null (0)
+    const float* pres_pen;    // [B] or null (0)
+    const uint32_t* allowed;  // [B, ceil(V/32)] bit masks, or null (all allowed)
 };
 
 }  // namespace nucleus

@@ -29,6 +29,9 @@
 // so all paths take the same decisions, bit for bit.
 #pragma once
 
+#include <type_traits>
+
+#include "prechain.h"
 #include "sampler.h"
 
 namespace nucleus {
@@ -155,8 +158,8 @@ __device__ __forceinline__ void mask_whole(uint32_t g0, uint32_t t, uint32_t nfu
 // kRowUnroll / 2 groups per thread, the next one's loads in flight while f
 // runs on the current one.  The row's partial last group (V not a multiple
 // of 4) takes one more call after the loop, loaded token by token.
-template <int DT, bool NTL, int NT, class F, class First>
-__device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&& f, First&& first)
+template <int DT, bool NTL, int NT, class F, class First, class XF>
+__device__ __forceinline__ void stream_row_x(const Params& p, const void* rowp, F&& f, First&& first, XF&& xf)
 {
     const uint32_t V = (uint32_t)p.V;
     const uint32_t ng = (V + 3) >> 2, nfull = V >> 2;
@@ -170,6 +173,11 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
         for (uint32_t g0 = 0; g0 < nfull; g0 += 2 * step) {
             issue_whole<DT, NTL, NT, H>(rowp, g0 + step, t, nfull, xb);
             mask_whole<NT, H>(g0, t, nfull, xa);
+#pragma unroll
+            for (int u = 0; u < H; ++u) {
+                const uint32_t g = g0 + (uint32_t)u * NT + t;
+                xf(g < nfull ? g << 2 : past, xa[u]);
+            }
             if (g0 == 0) {  // uniform
                 float mx = -INFINITY;
 #pragma unroll
@@ -189,6 +197,7 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
 #pragma unroll
             for (int u = 0; u < H; ++u) {
                 const uint32_t g = g0 + step + (uint32_t)u * NT + t;
+                xf(g < nfull ? g << 2 : past, xb[u]);
                 f(g < nfull ? g << 2 : past, xb[u]);
             }
         }
@@ -202,21 +211,30 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
                                                     : bf16_to_float(((const uint16_t*)rowp)[i]))
                                       : -INFINITY;
             }
+            xf(own ? nfull << 2 : past, x);
             f(own ? nfull << 2 : past, x);
         }
     } else {  // unaligned rows: token by token
         {
             float x[4];
             load4<DT>(rowp, (int64_t)t << 2, V, 0, x);
+            xf(t < ng ? t << 2 : past, x);
             first(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
         }
         for (uint32_t g0 = 0; g0 < ng; g0 += NT) {
             const uint32_t g = g0 + t;
             float x[4];
             load4<DT>(rowp, (int64_t)g << 2, V, 0, x);  // -inf past V
+            xf(g < ng ? g << 2 : past, x);
             f(g < ng ? g << 2 : past, x);
         }
     }
+}
+
+template <int DT, bool NTL, int NT, class F, class First>
+__device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&& f, First&& first)
+{
+    stream_row_x<DT, NTL, NT>(p, rowp, f, first, [](uint32_t, float*) {});
 }
 
 template <int DT, bool NTL, int NT, class F>
@@ -394,6 +412,10 @@ struct RowShared {
     uint32_t sstar_bits;  // best exact race score found so far in the workgroup (bits of a float >= 0)
 };
 
+struct RowSharedPre : RowShared {
+    PreShared pre;
+};
+
 // Row max and error flag over the workgroup: wave reductions, then one
 // exchange through LDS.
 template <int NT>
@@ -459,16 +481,27 @@ __device__ __forceinline__ void publish_row(RowPathState* ps, const RowState& st
 // One workgroup of kRowThreads per row.  PUBLISH = false: the whole row
 // (passes 1-2, race + candidates, resolver, optional probabilities);
 // PUBLISH = true: passes 1-2, then the row's state goes to rw for race_kernel.
-template <int DT, bool PUBLISH>
+template <int DT, bool PUBLISH, bool PRE = false>
 __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork rw)
 {
-    __shared__ RowShared sh;
+    __shared__ std::conditional_t<PRE, RowSharedPre, RowShared> sh;
     const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
     const int64_t esz = DT == kF32 ? 4 : 2;
     const void* rowp = (const char*)p.logits + b * p.stride * esz;
     use_row_key(p, b);
     const bool want_probs = wants_dist(p);  // probabilities or log-probabilities
+    // The pre-chain (penalties, grammar mask) is applied to every buffer of
+    // every pass as it arrives.
+    PreRow pre = {};
+    if constexpr (PRE) {
+        static_assert(sizeof(sh.u) >= kHistMax * sizeof(uint32_t), "the history sort fits the pass buffers");
+        pre = pre_setup<kRowThreads>(p, b, sh.pre, (uint32_t*)&sh.u);  // before the passes use sh.u
+    }
+    auto xf = [&](uint32_t i0, float* x) __attribute__((always_inline)) {
+        if constexpr (PRE) pre_apply(pre, sh.pre, i0, x);
+    };
+    auto nofirst = [](float) {};
 
     // ---- pass 1: row max, NaN / +inf; for rows whose
     // need of a histogram the parameters alone decide (no min-p), also the
@@ -489,7 +522,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     double base = 0.0;    // uniform: cell held by window slot 0 (slot k holds cell base - k)
     uint64_t tail_w = 0;  // cells below the window: all in the last bin
     uint32_t tail_c = 0;
-    stream_row<DT, false, kRowThreads>(
+    stream_row_x<DT, false, kRowThreads>(
         p, rowp,
         [&](uint32_t, const float* xs) {
 #pragma unroll
@@ -528,7 +561,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             // Cells are exact integers in double below 2^53; a provisional
             // max of -inf or +inf leaves the window unplaced.
             win = m1 > -INFINITY && fabs(base) < 0x1p50;
-        });
+        }, xf);
     block_extremes<kRowThreads>(lmax, bad, sh.redf, sh.redi);
     RowState st;
     st.mode = uniform(first_mode(bad != 0, lmax, rp.T, rp.P, rp.MP, rp.K, want_probs));
@@ -576,7 +609,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             // registers and added once per wave instead of by LDS atomics.
             tail_w = 0;
             tail_c = 0;
-            stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t, const float* xs) {
+            stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t, const float* xs) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (survives(model, xs[j])) {
@@ -590,7 +623,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
                         }
                     }
                 }
-            });
+            }, nofirst, xf);
             tail_w = wave_reduce(tail_w, SumU64());
             tail_c = wave_reduce(tail_c, SumU32());
             if (lane == 0 && tail_c) {
@@ -631,7 +664,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
         race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits, !has_cand);
     };
-    stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
+    stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
         const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
         wq_push(rq, qh, qn, lane, any, i0, xs, race);
         if (has_cand) {
@@ -639,7 +672,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             for (int j = 0; j < 4; ++j)
                 wave_append(seg, wn, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]), i0 + j);
         }
-    });
+    }, nofirst, xf);
     if (qn) wq_drain(rq, qh, qn, lane, qn, race);
     if (lane == 0) sh.wcand[t / kWave] = wn;
     acc = block_race<kRowThreads>(acc, sh.rs);  // (its barriers publish wcand)
@@ -675,11 +708,11 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     } else {  // more candidates than a wave's segment holds: visit the row in global memory
         resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
                                  [&](auto&& fn) {
-                                     stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
+                                     stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
 #pragma unroll
                                          for (int j = 0; j < 4; ++j)
                                              if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), i0 + j);
-                                     });
+                                     }, nofirst, xf);
                                  },
                                  sh.rs);
     }
@@ -693,7 +726,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     float* prow = p.out_probs ? p.out_probs + b * p.V : nullptr;
     float* lrow = p.out_logprobs ? p.out_logprobs + b * p.V : nullptr;
     const uint32_t V = (uint32_t)p.V;
-    stream_row<DT, true, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
+    stream_row_x<DT, true, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
         float q[4];
         if (prow) {
 #pragma unroll
@@ -705,7 +738,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             for (int j = 0; j < 4; ++j) q[j] = logprob_of(st.mode, model, st, ln, xs[j], i0 + j);
             store_probs(lrow, i0, V, q);
         }
-    });
+    }, nofirst, xf);
 }
 
 // The chunk a race_kernel / probs_kernel workgroup covers.  Dispatch is

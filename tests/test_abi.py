@@ -166,3 +166,24 @@ def test_spec_host_side_argument_errors(L):
     assert L.nucleus_spec_workspace_bytes(256, 128256) == 256 * 16 * 8
     assert L.nucleus_spec_workspace_bytes(3, 1) == 256
     assert L.nucleus_spec_workspace_bytes(-1, 8) == 0 and L.nucleus_spec_workspace_bytes(2, 0) == 0
+
+
+def test_prechain_host_side_argument_errors(L):
+    import nucleus_sampling_amd as ns
+
+    EINVAL = -1
+
+    def opt(**kw):
+        o = ns._Options()
+        for k, v in kw.items():
+            setattr(o, k, v)
+        return ctypes.byref(o)
+
+    assert _call(L, opt=opt(history=1 << 26, history_len=1025)) == EINVAL       # history too long
+    assert _call(L, opt=opt(history_len=4)) == EINVAL                           # length without ids
+    assert _call(L, opt=opt(history=(1 << 26) + 2, history_len=4)) == EINVAL    # misaligned ids
+    assert _call(L, opt=opt(allowed_mask=1 << 26, flags=2)) == EINVAL           # not on the split path
+    assert _call(L, opt=opt(allowed_mask=1 << 26, flags=4)) == EINVAL           # nor the chunked race
+    assert _call(L, V=175105, opt=opt(allowed_mask=1 << 26)) == EINVAL          # mask too long to stage
+    assert _call_rej(L, opt=opt(allowed_mask=1 << 26)) == EINVAL                # other entry points refuse it
+    assert _call_spec(L, opt=opt(repetition_penalty=1 << 26, workspace=1 << 27, workspace_bytes=1 << 20)) == EINVAL

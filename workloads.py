@@ -167,3 +167,42 @@ def make_draft(w: dict, noise: float = 0.7, keep_top: int = 64, seed: int = 0):
         while d[b] > 0 and qq[d[b]] == 0.0:  # land on a token the draft can propose
             d[b] -= 1
     return q, d
+
+
+def make_prechain(w: dict, hist_len: int = 256, seed: int = 0):
+    """Synthetic pre-chain inputs for the rows of workload dict ``w``: a
+    generated-token history per row (tokens drawn from the row's highest
+    logits and at random, duplicates included, -1 padded to ``hist_len``),
+    repetition / frequency / presence penalties (a quarter of the rows
+    without any), and a grammar bit mask forbidding about a fifth of the
+    vocabulary at random plus, on every third row, the row's top token (all
+    tokens allowed on every fifth row).  Returns a dict of NumPy arrays:
+    history [B, H] int32, repetition / frequency / presence [B] float32,
+    allowed [B, ceil(V/32)] uint32."""
+    x = w["logits"]
+    x = bf16_bits_to_f32(x) if w["dtype"] == "bf16" else x
+    B, V = x.shape
+    W = (V + 31) // 32
+    hist = np.full((B, hist_len), -1, np.int32)
+    rep = np.ones(B, np.float32)
+    fr = np.zeros(B, np.float32)
+    pr = np.zeros(B, np.float32)
+    allowed = np.full((B, W), 0xFFFFFFFF, np.uint32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, 91, b])
+        n = int(rng.integers(0, hist_len + 1))
+        top = np.argsort(-np.nan_to_num(x[b].astype(np.float64), nan=-np.inf))[: max(1, min(V, 32))]
+        picks = np.where(rng.random(n) < 0.6, rng.choice(top, n), rng.integers(0, V, n))
+        hist[b, :n] = picks
+        if b % 4 != 3:
+            rep[b] = np.float32(rng.choice([1.0, 1.1, 1.3, 2.0]))
+            fr[b] = np.float32(rng.uniform(0, 0.5))
+            pr[b] = np.float32(rng.uniform(0, 0.5))
+        if b % 5 != 4:
+            bits = rng.random(W * 32) >= 0.2
+            if b % 3 == 0:
+                bits[int(top[0])] = False
+            bits[V:] = True
+            words = np.packbits(bits.reshape(W, 32)[:, ::-1], axis=1, bitorder="big").view(">u4").astype(np.uint32)
+            allowed[b] = words.reshape(W)
+    return dict(history=hist, repetition=rep, frequency=fr, presence=pr, allowed=allowed)
