@@ -479,16 +479,19 @@ __device__ __forceinline__ float lowest_in_bins_below(const RowModel& r, uint32_
     uint32_t k = order_key(est > -3.4028234663852886e38f ? est : -3.4028234663852886e38f);
     k = k < kmin ? kmin : (k > kmax ? kmax : k);
     uint32_t lo, hi;  // below(lo) is false, below(hi) is true
+    // Steps double up to 2^31 and then stay there, so every step moves and
+    // the gallop reaches kmin (not below) or kmax (below: the max is in bin
+    // 0) from any start.
     if (below(k)) {
         hi = k;
-        for (uint32_t step = 1;; step <<= 1) {
+        for (uint32_t step = 1;; step = step < 0x80000000u ? step << 1 : step) {
             lo = (hi - kmin > step) ? hi - step : kmin;
             if (!below(lo)) break;
             hi = lo;
         }
     } else {
         lo = k;
-        for (uint32_t step = 1;; step <<= 1) {
+        for (uint32_t step = 1;; step = step < 0x80000000u ? step << 1 : step) {
             hi = (kmax - lo > step) ? lo + step : kmax;
             if (below(hi)) break;
             lo = hi;
