@@ -126,8 +126,8 @@ typedef struct nucleus_options {
      * Each step is one fp32 operation in that order (no fused multiply-add).
      * The sampler (validation included) sees only x'.  Any of these fields
      * set selects the one-workgroup-per-row path (NUCLEUS_FLAG_SPLIT_ROWS and
-     * NUCLEUS_FLAG_ROW_RACE are then NUCLEUS_EINVAL); NULL / 0 leaves the
-     * logits as they are. */
+     * NUCLEUS_FLAG_ROW_RACE are then NUCLEUS_EINVAL) and needs V <= 166912;
+     * NULL / 0 leaves the logits as they are. */
     const int32_t* history;            /* optional device [B, history_len] int32: each row's earlier
                                           tokens, -1 padded (ids outside [0, V) are ignored) */
     int64_t history_len;               /* 0 .. 1024 */
@@ -136,7 +136,7 @@ typedef struct nucleus_options {
     const float* presence_penalty;     /* optional device [B]: a_p (0 = off) */
     const uint32_t* allowed_mask;      /* optional device [B, ceil(V/32)] uint32: token i allowed iff
                                           bit (i mod 32) of word i / 32 is set (a grammar / JSON
-                                          constraint); needs V <= 175104 */
+                                          constraint) */
 } nucleus_options;
 
 /*

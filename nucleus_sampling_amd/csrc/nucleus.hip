@@ -165,7 +165,7 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     if (pre) {
         if (opt->history_len < 0 || opt->history_len > kHistMax || (opt->history_len > 0 && !opt->history))
             return NUCLEUS_EINVAL;
-        if (opt->allowed_mask && (V + 31) / 32 > kMaskWordsMax) return NUCLEUS_EINVAL;
+        if ((V + 31) / 32 > kMaskWordsMax) return NUCLEUS_EINVAL;  // the per-token bits are staged in LDS
         if (opt->flags & (NUCLEUS_FLAG_SPLIT_ROWS | NUCLEUS_FLAG_ROW_RACE)) return NUCLEUS_EINVAL;
         if ((opt->history && !aligned(opt->history)) || (opt->repetition_penalty && !aligned(opt->repetition_penalty)) ||
             (opt->frequency_penalty && !aligned(opt->frequency_penalty)) ||

@@ -14,11 +14,16 @@
 //
 // The row kernel applies this to every register buffer as it arrives, in
 // every pass, so the sampler sees only processed logits and never a second
-// copy of the row.  Per row, the workgroup stages in LDS the row's mask words
-// and a hash table of the history: the ids are sorted (bitonic sort, one per
-// thread), each distinct id with its count goes into one of 512 buckets of
-// four packed (id + 1, count) words (a full bucket spills into the next), so
-// a token's count is one 16-byte LDS read, rarely two.
+// copy of the row.  Per row, the workgroup stages in LDS a hash table of the
+// history and a bit per token: the ids are sorted (bitonic sort, one per
+// thread), each distinct id with its count and its own mask bit goes into one
+// of 512 buckets of four packed words (a full bucket spills into the next);
+// the staged bits are the mask (all set without one) with every history id
+// cleared.  A token whose bit is set is passed as it is, after one 4-byte LDS
+// read per four tokens.  A token whose bit is clear is forbidden unless an
+// 8K-bit filter of hashed history ids says it may be in the history; then it
+// probes the table (one 16-byte read, rarely two): found, it is penalised and
+// its own mask bit applied; not found, it is forbidden.
 #pragma once
 
 #include "common.h"
@@ -28,11 +33,13 @@ namespace nucleus {
 
 constexpr int kHistMax = 1024;        // history entries per row
 constexpr int kHistBuckets = 512;     // hash buckets of 4 entries: load <= 1/2
-constexpr int kMaskWordsMax = 5472;   // mask words staged per row: V <= 175104
+constexpr int kFilterWords = 256;     // 8192 filter bits
+constexpr int kMaskWordsMax = 5216;   // mask words staged per row: V <= 166912
 
 struct PreShared {
-    uint4 table[kHistBuckets];             // entries ((id + 1) << 11) | count, 0 = empty
-    uint32_t mask[kMaskWordsMax];
+    uint4 table[kHistBuckets];             // entries (allowed << 31) | ((id + 1) << 11) | count, 0 = empty
+    uint32_t filter[kFilterWords];         // history ids hashed
+    uint32_t mask[kMaskWordsMax];          // pass bits: allowed and not in the history
 };
 
 struct PreRow {
@@ -43,6 +50,7 @@ struct PreRow {
 };
 
 __device__ __forceinline__ uint32_t pre_bucket(uint32_t i) { return (i * 0x9E3779B1u) >> 23; }
+__device__ __forceinline__ uint32_t pre_filter_bit(uint32_t i) { return (i * 0x85EBCA77u) >> 19; }
 
 // Stages row b's history table and mask in LDS.  `hs` is kHistMax words of
 // LDS free until the call returns (the sort's space).  All NT threads; ends
@@ -69,10 +77,9 @@ __device__ __forceinline__ PreRow pre_setup(const Params& p, int64_t b, PreShare
         hs[t] = v;
     }
     for (uint32_t i = t; i < (uint32_t)kHistBuckets; i += NT) ps.table[i] = make_uint4(0, 0, 0, 0);
-    if (r.mask) {
-        const uint32_t W = (r.V + 31) >> 5;
-        for (uint32_t i = t; i < W; i += NT) ps.mask[i] = p.allowed[b * (int64_t)W + i];
-    }
+    for (uint32_t i = t; i < (uint32_t)kFilterWords; i += NT) ps.filter[i] = 0;
+    const uint32_t W = (r.V + 31) >> 5;
+    for (uint32_t i = t; i < W; i += NT) ps.mask[i] = r.mask ? p.allowed[b * (int64_t)W + i] : 0xFFFFFFFFu;
     if (r.pen) {  // uniform
         // Bitonic sort, ascending.
         for (uint32_t k = 2; k <= (uint32_t)kHistMax; k <<= 1)
@@ -96,7 +103,11 @@ __device__ __forceinline__ PreRow pre_setup(const Params& p, int64_t b, PreShare
         if (v != 0xFFFFFFFFu && (t == 0 || hs[t - 1] != v)) {
             uint32_t n = 1;
             while (t + n < (uint32_t)kHistMax && hs[t + n] == v) ++n;
-            const uint32_t e = ((v + 1u) << 11) | n;
+            const uint32_t allowed = r.mask ? (p.allowed[b * (int64_t)W + (v >> 5)] >> (v & 31)) & 1u : 1u;
+            const uint32_t e = (allowed << 31) | ((v + 1u) << 11) | n;
+            atomicAnd(&ps.mask[v >> 5], ~(1u << (v & 31)));  // history ids take the slow path
+            const uint32_t h = pre_filter_bit(v);
+            atomicOr(&ps.filter[h >> 5], 1u << (h & 31));
             uint32_t* slots = (uint32_t*)ps.table;
             uint32_t s0 = pre_bucket(v) * 4;
             for (uint32_t k = 0; k < 4u * kHistBuckets; ++k) {  // at most 1024 ids in 2048 slots: ends
@@ -109,20 +120,21 @@ __device__ __forceinline__ PreRow pre_setup(const Params& p, int64_t b, PreShare
     return r;
 }
 
-// Occurrences of token i in the row's history (0 if none).
-__device__ __forceinline__ uint32_t pre_count(const PreShared& ps, uint32_t i)
+// Token i's table entry: (allowed << 31) | ((i + 1) << 11) | count, or 0 if
+// i is not in the row's history.
+__device__ __forceinline__ uint32_t pre_entry(const PreShared& ps, uint32_t i)
 {
     const uint32_t key = i + 1u;
     uint32_t bk = pre_bucket(i);
     for (int k = 0; k < kHistBuckets; ++k) {
         const uint4 e = ps.table[bk];
-        uint32_t c = 0;
-        c = (e.x >> 11) == key ? (e.x & 2047u) : c;
-        c = (e.y >> 11) == key ? (e.y & 2047u) : c;
-        c = (e.z >> 11) == key ? (e.z & 2047u) : c;
-        c = (e.w >> 11) == key ? (e.w & 2047u) : c;
+        uint32_t f = 0;
+        f = ((e.x >> 11) & 0xFFFFFu) == key ? e.x : f;
+        f = ((e.y >> 11) & 0xFFFFFu) == key ? e.y : f;
+        f = ((e.z >> 11) & 0xFFFFFu) == key ? e.z : f;
+        f = ((e.w >> 11) & 0xFFFFFu) == key ? e.w : f;
         // Found, or the bucket has room (an insertion would have stopped here).
-        if (c || e.x == 0 || e.y == 0 || e.z == 0 || e.w == 0) return c;
+        if (f || e.x == 0 || e.y == 0 || e.z == 0 || e.w == 0) return f;
         bk = (bk + 1) & (kHistBuckets - 1);
     }
     return 0;
@@ -134,22 +146,22 @@ __device__ __forceinline__ void pre_apply(const PreRow& r, const PreShared& ps, 
 {
 #pragma clang fp contract(off)
     if (i0 >= r.V) return;
-    if (r.pen) {
+    const uint32_t bits = ps.mask[i0 >> 5] >> (i0 & 31);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t c = pre_count(ps, i0 + (uint32_t)j);
-            if (c) {
-                const float y = x[j] > 0.0f ? __fdiv_rn(x[j], r.rho) : x[j] * r.rho;
-                float pen = r.af * (float)c;
-                pen = pen + r.ap;
-                x[j] = y - pen;
-            }
+    for (int j = 0; j < 4; ++j) {
+        if ((bits >> j) & 1u) continue;  // allowed and not in the history: unchanged
+        const uint32_t h = pre_filter_bit(i0 + (uint32_t)j);
+        const bool maybe = r.pen && ((ps.filter[h >> 5] >> (h & 31)) & 1u);
+        const uint32_t e = maybe ? pre_entry(ps, i0 + (uint32_t)j) : 0u;
+        if (e) {
+            const uint32_t c = e & 2047u;
+            const float y = x[j] > 0.0f ? __fdiv_rn(x[j], r.rho) : x[j] * r.rho;
+            float pen = r.af * (float)c;
+            pen = pen + r.ap;
+            x[j] = (e >> 31) ? y - pen : -INFINITY;
+        } else {
+            x[j] = -INFINITY;  // forbidden
         }
-    }
-    if (r.mask) {
-        const uint32_t bits = ps.mask[i0 >> 5] >> (i0 & 31);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = ((bits >> j) & 1u) ? x[j] : -INFINITY;
     }
 }
 

@@ -184,6 +184,7 @@ def test_prechain_host_side_argument_errors(L):
     assert _call(L, opt=opt(history=(1 << 26) + 2, history_len=4)) == EINVAL    # misaligned ids
     assert _call(L, opt=opt(allowed_mask=1 << 26, flags=2)) == EINVAL           # not on the split path
     assert _call(L, opt=opt(allowed_mask=1 << 26, flags=4)) == EINVAL           # nor the chunked race
-    assert _call(L, V=175105, opt=opt(allowed_mask=1 << 26)) == EINVAL          # mask too long to stage
+    assert _call(L, V=166913, opt=opt(allowed_mask=1 << 26)) == EINVAL          # bits too long to stage
+    assert _call(L, V=166913, opt=opt(presence_penalty=1 << 26)) == EINVAL
     assert _call_rej(L, opt=opt(allowed_mask=1 << 26)) == EINVAL                # other entry points refuse it
     assert _call_spec(L, opt=opt(repetition_penalty=1 << 26, workspace=1 << 27, workspace_bytes=1 << 20)) == EINVAL
