@@ -42,10 +42,11 @@ def _processed(w, pc):
     return dict(w, logits=xp, dtype="f32")
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_prechain_workload_parity(n):
     say(f"pre-chain, workload {n} ({workloads.NAMES[n]}) shape={workloads.SHAPES[n]}: generating")
-    w = workloads.make(n)
+    # The flat workload's first 256 rows (V = 152064) keep the host-side inputs quick.
+    w = workloads.make(n, rows=range(256)) if n == 5 else workloads.make(n)
     pc = workloads.make_prechain(w, hist_len=1024 if n == 3 else 256, seed=n)
     rows = [0, 1, 2, 3, 4, 5, 9, w["B"] - 1]
     say(f"pre-chain, workload {n}: sampling on cuda:0")
