@@ -18,6 +18,7 @@ bounded sample of the same rows.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -29,10 +30,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "sampled rows/sec and logits HBM GB/s (% of peak) at B=256, V=128256 fp32"
-KERNEL_SOURCES = ["nucleus_sampling_amd/csrc/nucleus.hip", "nucleus_sampling_amd/csrc/sampler.h",
-                  "nucleus_sampling_amd/csrc/model.h", "nucleus_sampling_amd/csrc/select.h",
-                  "nucleus_sampling_amd/csrc/workspace.h", "nucleus_sampling_amd/csrc/common.h",
-                  "nucleus_sampling_amd/csrc/params.h"]
+# Every source of the library: a change to any of them invalidates committed counters.
+KERNEL_SOURCES = sorted(os.path.relpath(p, ROOT) for p in glob.glob(
+    os.path.join(ROOT, "nucleus_sampling_amd", "csrc", "*")) if p.endswith((".h", ".hip")))
 
 
 def kernel_hash() -> str:
@@ -122,9 +122,15 @@ def cpu_baseline(w, seconds: float, threads: int):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    # One thread on the first 16 rows, for the single-core figure.
+    t1 = time.perf_counter()
+    oracle.sample(w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], seed=w["seed"], rows=range(16),
+                  threads=1)
+    single = 16 / (time.perf_counter() - t1)
     return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "single_thread_rows_per_s": single,
             "sample": f"{passes} pass(es) over the {w['B']} rows of the benchmark batch ({rows} rows, {dt:.1f} s, "
-                      f"float64 stable-sort oracle, {threads} threads, one row per task)"}
+                      f"float64 stable-sort oracle, {threads} threads, one row per task); single thread: 16 rows"}
 
 
 def main():
@@ -364,7 +370,8 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic_from_profile(w["name"], batch_bytes),
                      "kernel": kernel, "path": args.path, "avg_launch_ms": avg_ms,
-                     "median_launch_ms": med_ms,
+                     "median_launch_ms": med_ms, "p10_launch_ms": float(np.percentile(per_launch_ms, 10)),
+                     "p90_launch_ms": float(np.percentile(per_launch_ms, 90)),
                      "algorithmic_bytes_per_launch": batch_bytes},
         "stream_read": {"gbps": stream_gbps, "avg_ms": read_ms, "frac_of_peak": stream_gbps / PEAK_HBM_GBPS,
                         "sampler_vs_stream": achieved / stream_gbps},
