@@ -44,14 +44,41 @@ struct SumF64 {
     __device__ double operator()(double a, double b) const { return a + b; }
 };
 
+constexpr float kChainDelta = 0.015625f;  // round 1 keeps every score >= 1/64 of the best
+constexpr int kChainCap = 512;              // kept scores per wave
+constexpr int kChainMax = 4;                // proposals tested by one pass
+
 struct RejShared {
-    RaceQueue rq[kRowThreads / kWave];
+    union {
+        RaceQueue rq[kRowThreads / kWave];             // race passes
+        u32x2v list[kRowThreads / kWave][kChainCap];   // round 1's high scores: (score bits, index)
+    } u;
     ResolveShared rs;
     float redf[kMaxWaves];
     int redi[kMaxWaves];
     double redd[kMaxWaves];
-    uint32_t sstar_bits;  // best exact race score so far in the workgroup
+    uint32_t wn[kMaxWaves];  // high scores kept per wave; 0xFFFFFFFF if some were lost
+    uint32_t sstar_bits;     // best exact race score so far in the workgroup
 };
+
+// Drops the wave's kept scores below thr (all lanes; n the same in every
+// lane).  Survivors keep their order.
+__device__ __forceinline__ void chain_compact(u32x2v* seg, uint32_t& n, float thr, uint32_t lane)
+{
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    uint32_t m = 0;
+    for (uint32_t base = 0; base < n; base += kWave) {
+        const uint32_t i = base + lane;
+        const u32x2v e = i < n ? seg[i] : u32x2v{0u, 0u};
+        const bool keep = i < n && __uint_as_float(e.x) >= thr;
+        const uint64_t mask = __ballot(keep);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        if (keep) seg[m + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] = e;
+        m += (uint32_t)__popcll(mask);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+    n = m;
+}
 
 template <int DT>
 __device__ __forceinline__ float logit_at(const void* rowp, uint32_t i)
@@ -73,7 +100,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void rejection_kernel(Params p, int
     use_row_key(p, b);
     const RowParams rp = row_params(p, b);
     const uint32_t lane = (uint32_t)t & (kWave - 1);
-    RaceQueue& rq = sh.rq[t / kWave];
+    RaceQueue& rq = sh.u.rq[t / kWave];
     const bool tempered = rp.T > 0.0f;  // false for T <= 0 and NaN
 
     // One race over the tokens with x >= lo (scored: e/E against the
@@ -100,6 +127,10 @@ __global__ __launch_bounds__(kRowThreads, 1) void rejection_kernel(Params p, int
 
     // ---- round 1's race, fused with the row max and the NaN / +inf check:
     // every finite token races against the max of the first tokens loaded.
+    // Every token scoring at least 1/64 of the best score so far is kept in
+    // its wave's list (the list drops entries that fall below 1/64 of the
+    // rising best when it fills), so at the end it holds every token scoring
+    // at least 1/64 of the final best: the next proposals, below.
     float lmax = -INFINITY;
     int bad = 0;
     bool racing = false;  // uniform
@@ -108,11 +139,11 @@ __global__ __launch_bounds__(kRowThreads, 1) void rejection_kernel(Params p, int
     RaceAcc acc;
     acc.init();
     float sstar = 0.0f;
-    uint32_t qh = 0, qn = 0;
+    u32x2v* const seg = sh.u.list[t / kWave];
+    uint32_t wn = 0;     // the wave's kept scores, as last read (the same in every lane)
+    bool lost = false;   // the wave ran out of room for scores it must keep (uniform in the wave)
     if (t == 0) sh.sstar_bits = 0;
-    auto race1 = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
-        race_queued(p, b, true, ref, c1, -FLT_MAX, i0, xs, active, acc, sstar, &sh.sstar_bits, false);
-    };
+    if (lane == 0) sh.wn[t / kWave] = 0;  // (published to the wave by the first hook's barriers)
     stream_row<DT, false, kRowThreads>(
         p, rowp,
         [&](uint32_t i0, const float* xs) {
@@ -121,9 +152,58 @@ __global__ __launch_bounds__(kRowThreads, 1) void rejection_kernel(Params p, int
                 bad |= !(xs[j] < INFINITY);  // NaN or +inf
                 lmax = fmaxf(lmax, xs[j]);
             }
-            if (racing) {
-                const bool any = (xs[0] >= -FLT_MAX) | (xs[1] >= -FLT_MAX) | (xs[2] >= -FLT_MAX) | (xs[3] >= -FLT_MAX);
-                wq_push(rq, qh, qn, lane, any, i0, xs, race1);
+            if (!racing) return;  // uniform
+            // Screen against 1/64 of the best score any wave has reached: a
+            // token is scored exactly unless it provably scores below that
+            // (the sampler's screen, race_groups, with the bound scaled).
+            const float shared = __uint_as_float(sh.sstar_bits);
+            const float bnd = fmaxf(sstar, shared);
+            const float thr = kChainDelta * bnd;  // exact: a power of two
+            const float kk = thr > 0.0f ? __builtin_amdgcn_rcpf(thr) * (1.0001f / (1.0f - 1e-4f)) : INFINITY;
+            const uint4 w4 = philox4x32_10(make_uint4(i0 >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
+            uint32_t pass = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x = xs[j];
+                const bool fin = x >= -FLT_MAX && x <= FLT_MAX;
+                const float e_hat = __builtin_amdgcn_exp2f((x - ref.m) * c1);
+                const float w = fmaf((float)(0xFFFFFFFFu - philox_word(w4, (uint32_t)j)), 0x1p-32f, 0x1p-33f);
+                pass |= (fin && !(w > e_hat * kk)) ? (1u << j) : 0u;
+            }
+            // Room for this call's appends (at most 4 per lane), compacting
+            // the list first if needed (uniform in the wave).
+            if (!lost) {
+                wn = sh.wn[t / kWave];
+                if (wn > (uint32_t)kChainCap - 4 * kWave) {
+                    chain_compact(seg, wn, thr, lane);
+                    if (lane == 0) sh.wn[t / kWave] = wn;
+                    lost = wn > (uint32_t)kChainCap - 4 * kWave;
+                }
+            }
+            while (pass) {
+                const uint32_t j = (uint32_t)__builtin_ctz(pass);
+                pass &= pass - 1u;
+                float x = xs[0];
+                x = j == 1 ? xs[1] : x;
+                x = j == 2 ? xs[2] : x;
+                x = j == 3 ? xs[3] : x;
+                const float sc = exact_score(x, ref.m, ref.T, ref.invT, philox_word(w4, j));
+                const uint64_t pk = race_pack(sc, i0 + j);
+                acc.best = pk > acc.best ? pk : acc.best;
+                sstar = fmaxf(sstar, sc);
+                if (sc >= thr && !lost) {
+                    const uint32_t off = atomicAdd(&sh.wn[t / kWave], 1u);
+                    if (off < (uint32_t)kChainCap) {
+                        u32x2v e;
+                        e.x = __float_as_uint(sc);
+                        e.y = i0 + j;
+                        seg[off] = e;
+                    }
+                }
+            }
+            if (__ballot(sstar > shared)) {
+                const float wave_best = wave_reduce(sstar, MaxF());
+                if (lane == 0) atomicMax(&sh.sstar_bits, __float_as_uint(wave_best));
             }
         },
         [&](float mx) {
@@ -135,10 +215,15 @@ __global__ __launch_bounds__(kRowThreads, 1) void rejection_kernel(Params p, int
                 c1 = ref.invT * 1.4426950408889634f;
             }
         });
-    if (racing && qn) wq_drain(rq, qh, qn, lane, qn, race1);
-    block_extremes<kRowThreads>(lmax, bad, sh.redf, sh.redi);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane == 0 && lost) sh.wn[t / kWave] = 0xFFFFFFFFu;
+    block_extremes<kRowThreads>(lmax, bad, sh.redf, sh.redi);  // (its barriers publish wn)
     const float m = uniform(lmax);
     uint64_t best = racing ? block_race<kRowThreads>(acc, sh.rs).best : 0;
+    bool chain_ok = racing;
+#pragma unroll
+    for (int w = 0; w < kRowThreads / kWave; ++w) chain_ok &= sh.wn[w] != 0xFFFFFFFFu;
+    chain_ok = uniform((uint32_t)chain_ok) != 0;
 
     int32_t token = -1, rounds = 0;
     if (bad || rp.T != rp.T || rp.P != rp.P || rp.MP != rp.MP || !(m > -INFINITY)) {
@@ -151,13 +236,84 @@ __global__ __launch_bounds__(kRowThreads, 1) void rejection_kernel(Params p, int
         // Scores against the first tokens' max stay finite while the true max
         // is at most 64 T above it (e <= e^64, E >= 2^-34); otherwise race again
         // against the true max.
-        if (!racing || (double)(m - ref.m) * (double)ref.invT > 64.0) best = race_pass(true, -FLT_MAX, model);
+        if (!racing || (double)(m - ref.m) * (double)ref.invT > 64.0) {
+            best = race_pass(true, -FLT_MAX, model);
+            chain_ok = false;
+        }
         const float cw = model.invT * 1.4426950408889634f;
+        auto accepts = [&](float xt, double a, double S) {
+            return survives(model, xt) && (xt == m || rp.P >= 1.0f || (rp.P > 0.0f && a < (double)rp.P * S));
+        };
         double S = 0.0;
-        for (int r = 1;; ++r) {
-            const uint32_t tok = uniform((uint32_t)~(uint32_t)best);
-            if (tok >= (uint32_t)p.V) break;  // no proposal (cannot happen: the max is above every pivot)
-            const float xt = uniform(logit_at<DT>(rowp, tok));
+        bool have_S = false;
+        int r0 = 1;
+        bool done = false;
+        if (chain_ok) {
+            // ---- the next proposals without racing again.  Round k + 1
+            // proposes the best score among tokens above round k's logit; if
+            // any token kept above that logit scores >= 1/64 of the best, the
+            // best of them is that proposal (every token scoring that much was
+            // kept).  Up to four proposals, then one pass tests them all.
+            const float s1 = __uint_as_float((uint32_t)(best >> 32));
+            const float thr1 = kChainDelta * s1;
+            uint32_t tok[kChainMax];
+            float xk[kChainMax];
+            int K = 1;
+            tok[0] = uniform((uint32_t)~(uint32_t)best);
+            xk[0] = uniform(logit_at<DT>(rowp, tok[0]));
+            const uint32_t wv = (uint32_t)t / kWave;
+            const uint32_t nw = sh.wn[wv];
+#pragma unroll
+            for (int k = 1; k < kChainMax; ++k) {
+                uint64_t g = 0;
+                for (uint32_t i = lane; i < nw; i += kWave) {
+                    const u32x2v e = sh.u.list[wv][i];
+                    const float sc = __uint_as_float(e.x);
+                    if (sc >= thr1 && logit_at<DT>(rowp, e.y) > xk[K - 1]) {
+                        const uint64_t pk = race_pack(sc, e.y);
+                        g = pk > g ? pk : g;
+                    }
+                }
+                g = uniform(block_reduce<kRowThreads>(g, MaxU64(), sh.rs.red64));
+                if (g == 0 || K < k) break;  // no kept token above: the list cannot tell
+                tok[K] = (uint32_t)~(uint32_t)g;
+                xk[K] = uniform(logit_at<DT>(rowp, tok[K]));
+                ++K;
+            }
+            float xs4[kChainMax];
+#pragma unroll
+            for (int k = 0; k < kChainMax; ++k) xs4[k] = k < K ? xk[k] : INFINITY;
+            double a[kChainMax] = {0.0, 0.0, 0.0, 0.0}, s = 0.0;
+            stream_row<DT, false, kRowThreads>(p, rowp, [&](uint32_t, const float* xs) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v = xs[j];
+                    const float e = __builtin_amdgcn_exp2f((v - model.m) * cw);
+                    const double w = survives(model, v) ? (double)e : 0.0;
+                    s += w;
+#pragma unroll
+                    for (int k = 0; k < kChainMax; ++k) a[k] += v > xs4[k] ? w : 0.0;
+                }
+            });
+            S = block_reduce<kRowThreads>(s, SumF64(), sh.redd);
+            have_S = true;
+#pragma unroll
+            for (int k = 0; k < kChainMax; ++k) a[k] = block_reduce<kRowThreads>(a[k], SumF64(), sh.redd);
+            for (int k = 0; k < K && !done; ++k)
+                if (accepts(xk[k], a[k], S)) {
+                    token = (int32_t)tok[k];
+                    rounds = k + 1;
+                    done = true;
+                }
+            if (!done) {
+                r0 = K + 1;
+                best = race_pass(true, next_up(xk[K - 1]), model);
+            }
+        }
+        for (int r = r0; !done; ++r) {
+            const uint32_t tk = uniform((uint32_t)~(uint32_t)best);
+            if (tk >= (uint32_t)p.V) break;  // no proposal (cannot happen: the max is above every pivot)
+            const float xt = uniform(logit_at<DT>(rowp, tk));
             // ---- the acceptance test: survivor mass strictly above x_t (and,
             // the first time, the total survivor mass S)
             double a = 0.0, s = 0.0;
@@ -172,15 +328,16 @@ __global__ __launch_bounds__(kRowThreads, 1) void rejection_kernel(Params p, int
                 }
             });
             a = block_reduce<kRowThreads>(a, SumF64(), sh.redd);
-            if (r == 1) S = block_reduce<kRowThreads>(s, SumF64(), sh.redd);
-            const bool accept =
-                survives(model, xt) && (xt == m || rp.P >= 1.0f || (rp.P > 0.0f && a < (double)rp.P * S));
-            if (accept) {
-                token = (int32_t)tok;
+            if (!have_S) {
+                S = block_reduce<kRowThreads>(s, SumF64(), sh.redd);
+                have_S = true;
+            }
+            if (accepts(xt, a, S)) {
+                token = (int32_t)tk;
                 rounds = r;
                 break;
             }
-            if (r == kMaxRounds) {
+            if (r >= kMaxRounds) {
                 rounds = r;
                 break;
             }
