@@ -153,3 +153,20 @@ def test_rejection_empty_batch():
     res = ns.sample_rejection(lg, torch.zeros(0), torch.zeros(0))
     torch.cuda.synchronize()
     assert res.token.numel() == 0
+
+
+def test_rejection_long_chains():
+    """Zipf rows with p of 0, 1e-4 and 0.01 need many rounds: the first
+    proposals come from round 1's list of high scores, the rest from race
+    passes over the tokens above the pivot.  Token and rounds must still match
+    the oracle's sequential rounds."""
+    w = workloads.make(3, rows=range(64))
+    B = w["B"]
+    w["top_p"] = np.asarray([[0.0, 1e-4, 0.01, 0.05][b % 4] for b in range(B)], np.float32)
+    say("rejection long chains")
+    tok, rounds, lg = _rej(w)
+    rep, orows = _check(w, tok, rounds)
+    say(f"rejection long chains: {rep.summary()}")
+    assert rep.ok(), rep.failures[:10]
+    assert rounds.max() > 4  # past the list's four proposals
+    assert len(_agree_with_main(tok, _main_tokens(w, lg), orows)) == 0
