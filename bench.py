@@ -164,7 +164,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); rows are independent, so a batch "
-              "shards across GPUs with no communication, but this build measures one GPU.", file=sys.stderr)
+              "shards across GPUs with no communication; this benchmark measures one GPU.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
