@@ -668,9 +668,17 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
         const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
         wq_push(rq, qh, qn, lane, any, i0, xs, race);
         if (has_cand) {
+            bool c[4];
+            bool anyc = false;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                wave_append(seg, wn, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]), i0 + j);
+            for (int j = 0; j < 4; ++j) {
+                c[j] = xs[j] >= cand_lo && xs[j] < keep_lo;
+                anyc |= c[j];
+            }
+            if (__ballot(anyc)) {  // uniform: most of a row's groups hold no crossing-bin token
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wave_append(seg, wn, c[j], order_key(xs[j]), i0 + j);
+            }
         }
     }, nofirst, xf);
     if (qn) wq_drain(rq, qh, qn, lane, qn, race);

@@ -464,6 +464,27 @@ __device__ __forceinline__ void race_one(const Params& p, int64_t b, const RowMo
     acc.minkey = key < acc.minkey ? key : acc.minkey;
 }
 
+// race_one behind race_groups' screen against a bound score s0, passed as
+// k0 = (1 + 1e-4) / ((1 - 1e-4) s0) (INFINITY for no bound): a token whose
+// 1 - u exceeds e_hat k0 scores below s0 and cannot win; it is counted and
+// its key kept, but not scored.
+__device__ __forceinline__ void race_one_screened(const Params& p, int64_t b, const RowModel& r, uint32_t key,
+                                                  uint32_t idx, RaceAcc& acc, float c_log2e, float k0)
+{
+    const uint4 w4 = philox4x32_10(make_uint4(idx >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
+    const uint32_t word = philox_word(w4, idx & 3);
+    const float x = key_value(key);
+    const float e_hat = __builtin_amdgcn_exp2f((x - r.m) * c_log2e);
+    const float w = fmaf((float)(0xFFFFFFFFu - word), 0x1p-32f, 0x1p-33f);
+    if (!(w > e_hat * k0)) {
+        const float s = exact_score(x, r.m, r.T, r.invT, word);
+        const uint64_t pk = race_pack(s, idx);
+        acc.best = pk > acc.best ? pk : acc.best;
+    }
+    acc.count += 1;
+    acc.minkey = key < acc.minkey ? key : acc.minkey;
+}
+
 // The smallest finite logit whose bin is < c (c >= 1).  Bins fall as logits
 // rise (the row max is in bin 0), so over order keys this is the boundary
 // between keys with bin >= c and keys with bin < c.  The search starts from
@@ -611,8 +632,14 @@ __device__ __forceinline__ void resolve_row(const Params& p, int64_t b, const Ro
         const uint32_t cut = sr.level;
         RaceAcc c;
         c.init();
+        // Kept candidates are screened against the surely kept tokens' best
+        // score (race_groups' screen): one that cannot reach it is counted
+        // without its exact score.
+        const float s0 = __uint_as_float((uint32_t)(part.best >> 32));
+        const float k0 = s0 > 0.0f ? __builtin_amdgcn_rcpf(s0) * (1.0001f / (1.0f - 1e-4f)) : INFINITY;
+        const float c_log2e = r.invT * 1.4426950408889634f;
         visit([&](uint32_t key, uint32_t idx) {
-            if (key >= cut) race_one(p, b, r, key, idx, c);
+            if (key >= cut) race_one_screened(p, b, r, key, idx, c, c_log2e, k0);
         });
         c = block_race<NT>(c, rs);
         acc.best = c.best > acc.best ? c.best : acc.best;
