@@ -395,8 +395,8 @@ __device__ __forceinline__ void stage_flush(u32x2v* stage, uint32_t& sn, uint32_
 struct RowShared {
     union {
         struct {  // histogram: a window of lattice cells (bins from decide on)
-            uint64_t hm[kWin];
-            uint32_t hc[kWin];
+            uint64_t hm[kWin + kRowThreads];  // the window, then one slot per thread
+            uint32_t hc[kWin + kRowThreads];
         } h;
         struct {  // race pass
             u32x2v cand[kRowCand];
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     const bool fused = hist_before_max(rp, want_probs);
     const Lattice lat = uniform(make_lattice(fused ? rp.T : 1.0f));
     if (fused)
-        for (int i = t; i < kWin; i += kRowThreads) {
+        for (int i = t; i < kWin + kRowThreads; i += kRowThreads) {
             sh.u.h.hm[i] = 0;
             sh.u.h.hc[i] = 0;
         }
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     int bad = 0;
     bool win = false;     // uniform: the window is placed
     double base = 0.0;    // uniform: cell held by window slot 0 (slot k holds cell base - k)
-    uint64_t tail_w = 0;  // cells below the window: all in the last bin
+    uint64_t tail_w = 0;  // the second pass: tokens of the last bin, summed in registers
     uint32_t tail_c = 0;
     stream_row_x<DT, false, kRowThreads>(
         p, rowp,
@@ -534,23 +534,22 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             if (win) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    // Branch-free but for the LDS atomics.  NaN and -inf
-                    // are no tokens; k < 0 lies above the window (the row is
-                    // then redone).
+                    // Branch-free.  A token in the window goes to its cell's
+                    // slot; every other value goes to this thread's own slot
+                    // past the window, which folds into the last bin: the
+                    // tail below the window (all of it in the last bin), a
+                    // token above the window (the row is then redone, bins
+                    // straight from the model), and NaN / -inf, which are no
+                    // tokens and add zero.
                     const float v = xs[j];
                     const bool fin = v > -INFINITY;
                     float f;
                     const double k = base - lattice_cell(lat, v, f);
                     const uint32_t fx = cell_fx(lat, f);
-                    const bool tail = fin && k >= (double)kWin;
-                    const bool in = fin && k >= 0.0 && k < (double)kWin;
-                    tail_w += tail ? fx : 0u;
-                    tail_c += tail ? 1u : 0u;
-                    if (in) {
-                        const int slot = (int)k;
-                        atomicAdd((unsigned long long*)&sh.u.h.hm[slot], (unsigned long long)fx);
-                        if (counts) atomicAdd(&sh.u.h.hc[slot], 1u);
-                    }
+                    const bool in = k >= 0.0 && k < (double)kWin;
+                    const uint32_t slot = in ? (uint32_t)k : (uint32_t)(kWin + t);
+                    atomicAdd((unsigned long long*)&sh.u.h.hm[slot], (unsigned long long)(fin ? fx : 0u));
+                    if (counts) atomicAdd(&sh.u.h.hc[slot], fin ? 1u : 0u);
                 }
             }
         },
@@ -585,13 +584,13 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             const uint32_t off = (uint32_t)offd;
             uint64_t fw = 0;
             uint32_t fc = 0;
-            for (uint32_t k = off + kBins + t; k < (uint32_t)kWin; k += kRowThreads) {
+            for (uint32_t k = off + kBins + t; k < (uint32_t)(kWin + kRowThreads); k += kRowThreads) {
                 fw += H[k];
                 fc += C[k];
             }
-            fw = wave_reduce(fw + tail_w, SumU64());
-            fc = wave_reduce(fc + tail_c, SumU32());
-            if (lane == 0 && fc) {
+            fw = wave_reduce(fw, SumU64());
+            fc = wave_reduce(fc, SumU32());
+            if (lane == 0 && (fw || fc)) {
                 atomicAdd((unsigned long long*)&H[off + kBins - 1], (unsigned long long)fw);
                 if (counts) atomicAdd(&C[off + kBins - 1], fc);
             }
