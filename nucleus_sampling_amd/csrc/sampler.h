@@ -351,12 +351,17 @@ __device__ __forceinline__ uint32_t philox_word(const uint4& w4, uint32_t j)
 //
 // The screen.  A token can reach sstar only if e/E >= sstar, i.e.
 // E <= e/sstar; and E = -ln u >= w = 1 - u.  So a token with
-// w > e_up/sstar, e_up = e_hat (1 + 1e-4) >= e, cannot reach sstar (e_hat =
-// exp2 of the scaled logit difference is within 3e-5 of e while |argument|
-// <= 126; below that the token cannot win against the row max, whose score is
-// at least 1/23).  w comes from the 32-bit word to within 1.2e-7 relative and
-// 1/sstar from the hardware reciprocal to within 2^-23, so rejecting when
-// w (1 - 1e-4) > e_up / sstar never drops a token that can reach sstar, ties
+// log2 w > log2 e - log2 sstar cannot reach sstar; the test runs in log2
+// units, with no transcendental per token:
+//  - log2 w from below: w >= n 2^-32 with n = ~word, and for the float nf
+//    of n, log2 nf >= bits(nf) 2^-23 - 127 (log2(1 + f) >= f on [0, 1)), so
+//    L = bits(nf) 2^-23 - 159 - 5e-5 <= log2 w, the 5e-5 covering the
+//    roundings of n, of bits(nf) to a float and of the fused add;
+//  - log2 e - log2 sstar = (x - m) c - log2 sstar, c = log2(e) / T, formed
+//    as fma(x - m, c, -log2 sstar - 2e-3): its roundings, the hardware log2
+//    and the exact scorer's own errors (about 1e-7 relative) stay below
+//    1e-4, far inside the 2e-3 margin.
+// So rejecting when L > R never drops a token that can reach sstar, ties
 // included.  The bound w <= E is loose only when w is large, i.e. only for
 // tokens whose e is a sizeable share of sstar; the many small tokens of a wide
 // nucleus pass only when u is within e/sstar of 1, where w and E agree.
@@ -397,19 +402,20 @@ __device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool sco
 #pragma unroll
     for (int g = 0; g < G; ++g)
         w4[g] = philox4x32_10(make_uint4(i0[g] >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
-    // e_up / sstar = e_hat * k, k = (1 + 1e-4) / sstar; with no score yet
-    // (sstar = 0) every kept token passes.
-    const float k = sstar > 0.0f ? __builtin_amdgcn_rcpf(sstar) * (1.0001f / (1.0f - 1e-4f)) : INFINITY;
+    // q = -log2 sstar - margin; with no score yet (sstar = 0) every kept
+    // token passes.
+    const float q = sstar > 0.0f ? -__builtin_amdgcn_logf(sstar) - 2e-3f : INFINITY;
     uint32_t pass = 0;
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             // Computed for every token and masked afterwards: no branches.
-            const float e_hat = __builtin_amdgcn_exp2f((x[g][j] - r.m) * c_log2e);
-            const float w = fmaf((float)(0xFFFFFFFFu - philox_word(w4[g], (uint32_t)j)), 0x1p-32f, 0x1p-33f);
+            const float R = fmaf(x[g][j] - r.m, c_log2e, q);
+            const float nf = (float)(~philox_word(w4[g], (uint32_t)j));
+            const float L = fmaf((float)__float_as_uint(nf), 0x1p-23f, -159.00005f);
             const uint32_t bit = 1u << (4 * g + j);
-            pass |= (km[g] & (1u << j) ? bit : 0u) & (w > e_hat * k ? 0u : bit);
+            pass |= (km[g] & (1u << j) ? bit : 0u) & (L > R ? 0u : bit);
         }
     while (pass) {
         const uint32_t k = (uint32_t)__builtin_ctz(pass);
