@@ -155,20 +155,22 @@ __global__ __launch_bounds__(kRowThreads, 1) void rejection_kernel(Params p, int
             if (!racing) return;  // uniform
             // Screen against 1/64 of the best score any wave has reached: a
             // token is scored exactly unless it provably scores below that
-            // (the sampler's screen, race_groups, with the bound scaled).
+            // (the sampler's log2 screen, race_groups, with the bound scaled).
             const float shared = __uint_as_float(sh.sstar_bits);
             const float bnd = fmaxf(sstar, shared);
             const float thr = kChainDelta * bnd;  // exact: a power of two
-            const float kk = thr > 0.0f ? __builtin_amdgcn_rcpf(thr) * (1.0001f / (1.0f - 1e-4f)) : INFINITY;
+            const float q = thr > 0.0f ? -__builtin_amdgcn_logf(thr) - 2e-3f : INFINITY;
             const uint4 w4 = philox4x32_10(make_uint4(i0 >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
             uint32_t pass = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float x = xs[j];
                 const bool fin = x >= -FLT_MAX && x <= FLT_MAX;
-                const float e_hat = __builtin_amdgcn_exp2f((x - ref.m) * c1);
-                const float w = fmaf((float)(0xFFFFFFFFu - philox_word(w4, (uint32_t)j)), 0x1p-32f, 0x1p-33f);
-                pass |= (fin && !(w > e_hat * kk)) ? (1u << j) : 0u;
+                // race_groups' screen in log2 units, against thr.
+                const float R = fmaf(x - ref.m, c1, q);
+                const float nf = (float)(~philox_word(w4, (uint32_t)j));
+                const float L = fmaf((float)__float_as_uint(nf), 0x1p-23f, -159.00005f);
+                pass |= (fin && !(L > R)) ? (1u << j) : 0u;
             }
             // Room for this call's appends (at most 4 per lane), compacting
             // the list first if needed (uniform in the wave).
