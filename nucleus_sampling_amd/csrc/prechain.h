@@ -15,9 +15,9 @@
 // The row kernel applies this to every register buffer as it arrives, in
 // every pass, so the sampler sees only processed logits and never a second
 // copy of the row.  Per row, the workgroup stages in LDS a hash table of the
-// history and a bit per token: the ids are sorted (bitonic sort, one per
-// thread), each distinct id with its count and its own mask bit goes into one
-// of 512 buckets of four packed words (a full bucket spills into the next);
+// history and a bit per token: each distinct id with its count and its own
+// mask bit goes into one of 512 buckets of four packed words (a full bucket
+// spills into the next), every thread inserting its own history entry;
 // the staged bits are the mask (all set without one) with every history id
 // cleared.  A token whose bit is set is passed as it is, after one 4-byte LDS
 // read per four tokens.  A token whose bit is clear is forbidden unless an
@@ -52,13 +52,19 @@ struct PreRow {
 __device__ __forceinline__ uint32_t pre_bucket(uint32_t i) { return (i * 0x9E3779B1u) >> 23; }
 __device__ __forceinline__ uint32_t pre_filter_bit(uint32_t i) { return (i * 0x85EBCA77u) >> 19; }
 
-// Stages row b's history table and mask in LDS.  `hs` is kHistMax words of
-// LDS free until the call returns (the sort's space).  All NT threads; ends
-// with a barrier.
+// Stages row b's history table and mask in LDS.  All NT threads (one
+// history entry each); ends with a barrier.
+//
+// Each thread inserts its own history id: it walks the slots from the id's
+// bucket on, claims the first empty one by compare-and-swap, or, meeting a
+// slot that already holds the id, adds one to that entry's count.  Slots are
+// never emptied, so every slot between an id's bucket and its entry is full
+// whatever order the threads ran in, which is what the lookup relies on; the
+// counts are sums, so the table's contents do not depend on that order.
 template <int NT>
-__device__ __forceinline__ PreRow pre_setup(const Params& p, int64_t b, PreShared& ps, uint32_t* hs)
+__device__ __forceinline__ PreRow pre_setup(const Params& p, int64_t b, PreShared& ps)
 {
-    static_assert(NT == kHistMax, "the bitonic sort takes one history entry per thread");
+    static_assert(NT == kHistMax, "one history entry per thread");
     const uint32_t t = threadIdx.x;
     PreRow r;
     r.V = (uint32_t)p.V;
@@ -68,51 +74,33 @@ __device__ __forceinline__ PreRow pre_setup(const Params& p, int64_t b, PreShare
     const uint32_t H = (uint32_t)p.hist_len;
     r.pen = p.hist && H > 0 && !(r.rho == 1.0f && r.af == 0.0f && r.ap == 0.0f);
     r.mask = p.allowed != nullptr;
-    {
-        uint32_t v = 0xFFFFFFFFu;
-        if (r.pen && t < H) {
-            const int32_t tok = p.hist[b * (int64_t)H + t];
-            if (tok >= 0 && (uint32_t)tok < r.V) v = (uint32_t)tok;
-        }
-        hs[t] = v;
+    uint32_t v = 0xFFFFFFFFu;
+    if (r.pen && t < H) {
+        const int32_t tok = p.hist[b * (int64_t)H + t];
+        if (tok >= 0 && (uint32_t)tok < r.V) v = (uint32_t)tok;
     }
     for (uint32_t i = t; i < (uint32_t)kHistBuckets; i += NT) ps.table[i] = make_uint4(0, 0, 0, 0);
     for (uint32_t i = t; i < (uint32_t)kFilterWords; i += NT) ps.filter[i] = 0;
     const uint32_t W = (r.V + 31) >> 5;
     for (uint32_t i = t; i < W; i += NT) ps.mask[i] = r.mask ? p.allowed[b * (int64_t)W + i] : 0xFFFFFFFFu;
-    if (r.pen) {  // uniform
-        // Bitonic sort, ascending.
-        for (uint32_t k = 2; k <= (uint32_t)kHistMax; k <<= 1)
-            for (uint32_t j = k >> 1; j > 0; j >>= 1) {
-                __syncthreads();
-                const uint32_t o = t ^ j;
-                if (o > t) {
-                    const uint32_t a = hs[t], c = hs[o];
-                    const bool up = (t & k) == 0;
-                    if ((a > c) == up) {
-                        hs[t] = c;
-                        hs[o] = a;
-                    }
-                }
-            }
-        __syncthreads();
-        // The first thread of each run of equal ids inserts the id with the
-        // run's length: a compare-and-swap into the first empty slot from its
-        // bucket on (distinct ids only, so no slot is ever counted twice).
-        const uint32_t v = hs[t];
-        if (v != 0xFFFFFFFFu && (t == 0 || hs[t - 1] != v)) {
-            uint32_t n = 1;
-            while (t + n < (uint32_t)kHistMax && hs[t + n] == v) ++n;
-            const uint32_t allowed = r.mask ? (p.allowed[b * (int64_t)W + (v >> 5)] >> (v & 31)) & 1u : 1u;
-            const uint32_t e = (allowed << 31) | ((v + 1u) << 11) | n;
-            atomicAnd(&ps.mask[v >> 5], ~(1u << (v & 31)));  // history ids take the slow path
-            const uint32_t h = pre_filter_bit(v);
-            atomicOr(&ps.filter[h >> 5], 1u << (h & 31));
-            uint32_t* slots = (uint32_t*)ps.table;
-            uint32_t s0 = pre_bucket(v) * 4;
-            for (uint32_t k = 0; k < 4u * kHistBuckets; ++k) {  // at most 1024 ids in 2048 slots: ends
-                const uint32_t s = (s0 + k) & (4u * kHistBuckets - 1);
-                if (atomicCAS(&slots[s], 0u, e) == 0u) break;
+    __syncthreads();
+    if (v != 0xFFFFFFFFu) {
+        const uint32_t allowed = r.mask ? (p.allowed[b * (int64_t)W + (v >> 5)] >> (v & 31)) & 1u : 1u;
+        const uint32_t key = (v + 1u) << 11;
+        const uint32_t e = (allowed << 31) | key | 1u;
+        atomicAnd(&ps.mask[v >> 5], ~(1u << (v & 31)));  // history ids take the slow path
+        const uint32_t h = pre_filter_bit(v);
+        atomicOr(&ps.filter[h >> 5], 1u << (h & 31));
+        uint32_t* slots = (uint32_t*)ps.table;
+        const uint32_t s0 = pre_bucket(v) * 4;
+        // At most 1024 ids in 2048 slots: an empty or matching slot is met.
+        for (uint32_t k = 0; k < 4u * kHistBuckets; ++k) {
+            const uint32_t sl = (s0 + k) & (4u * kHistBuckets - 1);
+            const uint32_t old = atomicCAS(&slots[sl], 0u, e);
+            if (old == 0u) break;
+            if ((old & 0x7FFFF800u) == key) {  // the id's entry: count one more
+                atomicAdd(&slots[sl], 1u);
+                break;
             }
         }
     }
@@ -141,18 +129,40 @@ __device__ __forceinline__ uint32_t pre_entry(const PreShared& ps, uint32_t i)
 }
 
 // Applies the pre-chain to tokens i0 .. i0 + 3 (i0 a multiple of 4; values at
-// or past V are -inf already and stay so).
+// or past V are -inf already and stay so).  A group with a staged bit clear
+// reads its four filter words together, with no branch between them, so it
+// waits for LDS once; only tokens the filter cannot clear take the table
+// probe.
 __device__ __forceinline__ void pre_apply(const PreRow& r, const PreShared& ps, uint32_t i0, float* x)
 {
 #pragma clang fp contract(off)
     if (i0 >= r.V) return;
     const uint32_t bits = ps.mask[i0 >> 5] >> (i0 & 31);
+    if ((bits & 0xFu) == 0xFu) return;  // all four allowed and not in the history
+    uint32_t slow = 0;  // bit j: token i0 + j may be in the history
+    if (r.pen) {        // uniform
+        uint32_t f[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t h = pre_filter_bit(i0 + (uint32_t)j);
+            f[j] = ps.filter[h >> 5] >> (h & 31);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) slow |= (f[j] & ~(bits >> j) & 1u) << j;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        if ((bits >> j) & 1u) continue;  // allowed and not in the history: unchanged
-        const uint32_t h = pre_filter_bit(i0 + (uint32_t)j);
-        const bool maybe = r.pen && ((ps.filter[h >> 5] >> (h & 31)) & 1u);
-        const uint32_t e = maybe ? pre_entry(ps, i0 + (uint32_t)j) : 0u;
+        // A staged bit set: unchanged.  Clear, and not possibly in the
+        // history: forbidden.
+        const bool pass = (bits >> j) & 1u;
+        const bool maybe = (slow >> j) & 1u;
+        x[j] = pass || maybe ? x[j] : -INFINITY;
+    }
+    if (!slow) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (!((slow >> j) & 1u)) continue;
+        const uint32_t e = pre_entry(ps, i0 + (uint32_t)j);
         if (e) {
             const uint32_t c = e & 2047u;
             const float y = x[j] > 0.0f ? __fdiv_rn(x[j], r.rho) : x[j] * r.rho;

@@ -495,8 +495,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     // every pass as it arrives.
     PreRow pre = {};
     if constexpr (PRE) {
-        static_assert(sizeof(sh.u) >= kHistMax * sizeof(uint32_t), "the history sort fits the pass buffers");
-        pre = pre_setup<kRowThreads>(p, b, sh.pre, (uint32_t*)&sh.u);  // before the passes use sh.u
+        pre = pre_setup<kRowThreads>(p, b, sh.pre);
     }
     auto xf = [&](uint32_t i0, float* x) __attribute__((always_inline)) {
         if constexpr (PRE) pre_apply(pre, sh.pre, i0, x);
