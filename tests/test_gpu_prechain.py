@@ -103,6 +103,48 @@ def test_prechain_strided_and_edge_rows():
     assert tok[0] >= 0
 
 
+def _bucket(ids):
+    """The kernel's table bucket of each id (multiplicative hash, top 9 bits)."""
+    return ((ids.astype(np.uint64) * np.uint64(0x9E3779B1)) & np.uint64(0xFFFFFFFF)) >> np.uint64(23)
+
+
+def test_prechain_colliding_history():
+    """Histories built against the table: one id 1024 times (the largest
+    count), 1024 distinct ids from 16 of the 512 buckets (chains of spills
+    hundreds of slots long, inserted by 1024 threads at once), colliding ids
+    twice each with some of them forbidden, and pads and ids outside [0, V).
+    Every token is kept (p = 1), so each token's probability shows its
+    processed logit: a lost, doubled or misplaced entry moves it."""
+    rng = np.random.default_rng(31)
+    B, V, H = 4, 65536, 1024
+    L = rng.normal(0.0, 2.0, (B, V)).astype(np.float32)
+    ids = np.arange(V)
+    near = ids[_bucket(ids) < 16]
+    assert len(near) >= H
+    hist = np.full((B, H), -1, np.int32)
+    hist[0, :] = 777
+    hist[1, :] = rng.permutation(near)[:H]
+    pair = rng.permutation(near)[:H // 2]
+    hist[2, :] = rng.permutation(np.concatenate([pair, pair]))
+    hist[3, :600] = rng.integers(0, V, 600)
+    hist[3, 600:700] = V + rng.integers(0, 50, 100)
+    hist[3, 700:800] = -5
+    allow = rng.random((B, V)) >= 0.2
+    allow[0, 777] = True                 # the count of 1024 shows
+    allow[2, hist[2, : H // 4]] = False  # a quarter of row 2's ids forbidden
+    allowed = (allow.reshape(B, V // 32, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(-1)
+    allowed = allowed.astype(np.uint32)
+    pc = dict(history=hist, repetition=np.full(B, 1.3, np.float32), frequency=np.full(B, 0.05, np.float32),
+              presence=np.full(B, 0.2, np.float32), allowed=allowed)
+    w = dict(logits=L, dtype="f32", temperature=np.ones(B, np.float32), top_p=np.ones(B, np.float32), top_k=None,
+             min_p=None, seed=12, B=B, V=V)
+    say("pre-chain colliding histories")
+    tok, cnt, mk, probs, _ = _gpu(w, pc, rows=range(B))
+    rep, _ = oracle_and_compare(_processed(w, pc), tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(B)))
+    say(f"pre-chain colliding histories: {rep.summary()}")
+    assert rep.ok(), rep.failures
+
+
 def test_prechain_rejects_other_paths():
     import torch
 
