@@ -42,6 +42,16 @@ __device__ __forceinline__ float bf16_to_float(uint16_t h)
     return __uint_as_float((uint32_t)h << 16);
 }
 
+// Double to int32, rounding toward zero and saturating at the int32 range
+// (NaN gives 0): gfx950's conversion, defined for every input, where a C cast
+// of an out-of-range value is not.
+__device__ __forceinline__ int32_t cvt_i32_sat(double x)
+{
+    int32_t r;
+    asm("v_cvt_i32_f64 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
 // as 1, 2, 3", SC'11): per round, words 0 and 2 are multiplied by the two

@@ -103,10 +103,13 @@ __device__ __forceinline__ double lattice_cell(const Lattice& L, float x, float&
 }
 
 // Integer weight of a token relative to its cell's upper edge, in (0, 2^31].
+// The clamp at 0 changes no finite token's weight (the cubic is positive on
+// (0, 1]); it gives 0 for f = NaN, which is what -inf yields, so a -inf
+// value adds nothing wherever it is binned.
 __device__ __forceinline__ uint32_t cell_fx(const Lattice& L, float f)
 {
 #pragma clang fp contract(off)
-    return (uint32_t)fmaf(fmaf(fmaf(L.c3, f, L.c2), f, L.c1), f, L.c0);
+    return (uint32_t)fmaxf(fmaf(fmaf(fmaf(L.c3, f, L.c2), f, L.c1), f, L.c0), 0.0f);
 }
 
 // Bin of cell a in a row whose max is in cell A.

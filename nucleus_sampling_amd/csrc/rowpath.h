@@ -539,16 +539,16 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
                     // tail below the window (all of it in the last bin), a
                     // token above the window (the row is then redone, bins
                     // straight from the model), and NaN / -inf, which are no
-                    // tokens and add zero.
+                    // tokens and add zero (cell_fx gives them 0; any slot
+                    // the saturating conversion picks for them is in range).
                     const float v = xs[j];
-                    const bool fin = v > -INFINITY;
                     float f;
                     const double k = base - lattice_cell(lat, v, f);
                     const uint32_t fx = cell_fx(lat, f);
-                    const bool in = k >= 0.0 && k < (double)kWin;
-                    const uint32_t slot = in ? (uint32_t)k : (uint32_t)(kWin + t);
-                    atomicAdd((unsigned long long*)&sh.u.h.hm[slot], (unsigned long long)(fin ? fx : 0u));
-                    if (counts) atomicAdd(&sh.u.h.hc[slot], fin ? 1u : 0u);
+                    const uint32_t ki = (uint32_t)cvt_i32_sat(k);  // k is a whole number
+                    const uint32_t slot = ki < (uint32_t)kWin ? ki : (uint32_t)(kWin + t);
+                    atomicAdd((unsigned long long*)&sh.u.h.hm[slot], (unsigned long long)fx);
+                    if (counts) atomicAdd(&sh.u.h.hc[slot], v > -INFINITY ? 1u : 0u);
                 }
             }
         },
