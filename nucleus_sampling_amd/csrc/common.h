@@ -42,6 +42,16 @@ __device__ __forceinline__ float bf16_to_float(uint16_t h)
     return __uint_as_float((uint32_t)h << 16);
 }
 
+// 2 rej + (a > b): the compare writes VCC and the add takes it as its carry
+// in, so a lane's compare results pack into a bit mask at two instructions
+// each (false for NaN, as a C compare).
+__device__ __forceinline__ uint32_t shift_in_gt(uint32_t rej, float a, float b)
+{
+    uint32_t r;
+    asm("v_cmp_gt_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %3, %3, vcc" : "=v"(r) : "v"(a), "v"(b), "v"(rej) : "vcc");
+    return r;
+}
+
 // Double to int32, rounding toward zero and saturating at the int32 range
 // (NaN gives 0): gfx950's conversion, defined for every input, where a C cast
 // of an out-of-range value is not.

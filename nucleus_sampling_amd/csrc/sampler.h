@@ -405,18 +405,21 @@ __device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool sco
     // q = -log2 sstar - margin; with no score yet (sstar = 0) every kept
     // token passes.
     const float q = sstar > 0.0f ? -__builtin_amdgcn_logf(sstar) - 2e-3f : INFINITY;
-    uint32_t pass = 0;
+    // Computed for every token and masked afterwards: no branches.  Tokens
+    // go in from the last, so token 4 g + j's verdict ends at bit 4 g + j.
+    uint32_t rej = 0, kall = 0;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = G - 1; g >= 0; --g) {
+        kall = (kall << 4) | km[g];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // Computed for every token and masked afterwards: no branches.
+        for (int j = 3; j >= 0; --j) {
             const float R = fmaf(x[g][j] - r.m, c_log2e, q);
             const float nf = (float)(~philox_word(w4[g], (uint32_t)j));
             const float L = fmaf((float)__float_as_uint(nf), 0x1p-23f, -159.00005f);
-            const uint32_t bit = 1u << (4 * g + j);
-            pass |= (km[g] & (1u << j) ? bit : 0u) & (L > R ? 0u : bit);
+            rej = shift_in_gt(rej, L, R);
         }
+    }
+    uint32_t pass = kall & ~rej;
     while (pass) {
         const uint32_t k = (uint32_t)__builtin_ctz(pass);
         pass &= pass - 1u;
