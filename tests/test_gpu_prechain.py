@@ -145,6 +145,23 @@ def test_prechain_colliding_history():
     assert rep.ok(), rep.failures
 
 
+def test_prechain_largest_vocabulary():
+    """V = 166912, the most the pre-chain stages: the mask fills its LDS
+    words to the last one.  Every token's probability against the oracle."""
+    rng = np.random.default_rng(41)
+    B, V = 4, 166912
+    w = _random_batch(rng, B, V, "f32")
+    w["top_p"] = np.asarray([1.0, 0.9, 0.5, 1.0], np.float32)
+    pc = workloads.make_prechain(w, hist_len=1024, seed=41)
+    pc["allowed"][:, -1] = np.uint32(0x0000FFFF)  # the last word's top half forbidden
+    say(f"pre-chain V={V}")
+    tok, cnt, mk, probs, _ = _gpu(w, pc, rows=range(B))
+    rep, _ = oracle_and_compare(_processed(w, pc), tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(B)))
+    say(f"pre-chain V={V}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+    assert (probs[:, V - 16:] == 0).all()
+
+
 def test_prechain_rejects_other_paths():
     import torch
 
