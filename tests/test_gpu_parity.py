@@ -89,6 +89,43 @@ def _random_batch(rng, B, V, dtype, extras=True):
 
 @pytest.mark.parametrize("path", [None, "rows", "single"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_million_token_rows(dtype, path):
+    """Rows of 2^20 + 7 tokens, far past any workload's vocabulary (513
+    chunked-race items of 2048 tokens per row, the last one ragged; the
+    default path takes one workgroup per row, rows this long being past the
+    split-row limit).  Every token's probability against the oracle."""
+    rng = np.random.default_rng(20 + (dtype == "bf16"))
+    B, V = 3, (1 << 20) + 7
+    w = _random_batch(rng, B, V, dtype)
+    say(f"V={V} {dtype} B={B} path={path}")
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(B), path=path)
+    rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(B)))
+    say(f"V={V} {dtype}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_rows_at_their_limit(dtype):
+    """The split-row path at its longest rows (64 workgroups of 8192 tokens,
+    V = 524288) against the oracle; one token more and the split flag is
+    refused."""
+    rng = np.random.default_rng(64 + (dtype == "bf16"))
+    B, V = 3, 64 * 8192
+    w = _random_batch(rng, B, V, dtype)
+    say(f"split rows V={V} {dtype}")
+    tok, cnt, mk, probs = _gpu(w, want_probs=True, prob_rows=range(B), path="split")
+    rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=list(range(B)))
+    say(f"split rows V={V} {dtype}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+    import nucleus_sampling_amd as ns
+
+    w1 = _random_batch(rng, 2, V + 1, dtype)
+    with pytest.raises(ns.NucleusError):
+        _gpu(w1, path="split")
+
+
+@pytest.mark.parametrize("path", [None, "rows", "single"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [1, 2, 3, 5, 63, 64, 65, 1023, 4097, 9999, 40001])
 def test_small_and_ragged_shapes(V, dtype, path):
     rng = np.random.default_rng(V * 7 + (dtype == "bf16"))
