@@ -98,6 +98,20 @@ def test_rejection_edge_rows(dtype):
     assert rep.ok(), rep.failures
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rejection_million_token_rows(dtype):
+    """Rows of 2^20 + 7 tokens: token and rounds against the oracle, and the
+    main sampler's token on rows off every boundary."""
+    rng = np.random.default_rng(21 + (dtype == "bf16"))
+    w = _random_batch(rng, 3, (1 << 20) + 7, dtype)
+    say(f"rejection V={w['V']} {dtype}")
+    tok, rounds, lg = _rej(w)
+    rep, orows = _check(w, tok, rounds)
+    say(f"rejection V={w['V']} {dtype}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+    assert len(_agree_with_main(tok, _main_tokens(w, lg), orows)) == 0
+
+
 def test_rejection_strided_rows_and_first_race_fallbacks():
     """Unaligned strided rows; rows whose first loaded tokens are all -inf
     (the first round cannot race in the max pass); rows whose max lies far

@@ -69,6 +69,19 @@ def test_spec_ragged_shapes(V):
     assert rep.ok(), rep.failures
 
 
+def test_spec_million_token_rows():
+    """Rows of 2^20 + 7 tokens: 129 chunks of 8192 per row, the last one
+    ragged."""
+    rng = np.random.default_rng(22)
+    w = _random_batch(rng, 3, (1 << 20) + 7, "f32")
+    q, d = workloads.make_draft(w, keep_top=4096, seed=22)
+    say(f"speculative V={w['V']}")
+    tok, acc, cnt, p_at = _run(w, q, d)
+    rep = _check(w, q, d, tok, acc, cnt, p_at)
+    say(f"speculative V={w['V']}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+
+
 def test_spec_edge_rows_and_bad_drafts():
     """Target row errors (p all zero), greedy targets, ties, and draft tokens
     outside [0, V)."""
