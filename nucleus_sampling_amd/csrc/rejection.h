@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void rejection_kernel(Params p, int
             const float shared = __uint_as_float(sh.sstar_bits);
             const float bnd = fmaxf(sstar, shared);
             const float thr = kChainDelta * bnd;  // exact: a power of two
-            const float q = thr > 0.0f ? -__builtin_amdgcn_logf(thr) - 2e-3f : INFINITY;
+            const float q = thr > 0.0f ? -__builtin_amdgcn_logf(thr) + 2e-3f : INFINITY;  // R errs high: see race_groups
             const uint4 w4 = philox4x32_10(make_uint4(i0 >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
             uint32_t pass = 0;
 #pragma unroll

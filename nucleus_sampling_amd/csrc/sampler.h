@@ -352,19 +352,24 @@ __device__ __forceinline__ uint32_t philox_word(const uint4& w4, uint32_t j)
 // The screen.  A token can reach sstar only if e/E >= sstar, i.e.
 // E <= e/sstar; and E = -ln u >= w = 1 - u.  So a token with
 // log2 w > log2 e - log2 sstar cannot reach sstar; the test runs in log2
-// units, with no transcendental per token:
-//  - log2 w from below: w >= n 2^-32 with n = ~word, and for the float nf
-//    of n, log2 nf >= bits(nf) 2^-23 - 127 (log2(1 + f) >= f on [0, 1)), so
-//    L = bits(nf) 2^-23 - 159 - 5e-5 <= log2 w, the 5e-5 covering the
-//    roundings of n, of bits(nf) to a float and of the fused add;
-//  - log2 e - log2 sstar = (x - m) c - log2 sstar, c = log2(e) / T, formed
-//    as fma(x - m, c, -log2 sstar - 2e-3): its roundings, the hardware log2
-//    and the exact scorer's own errors (about 1e-7 relative) stay below
-//    1e-4, far inside the 2e-3 margin.
-// So rejecting when L > R never drops a token that can reach sstar, ties
-// included.  The bound w <= E is loose only when w is large, i.e. only for
-// tokens whose e is a sizeable share of sstar; the many small tokens of a wide
-// nucleus pass only when u is within e/sstar of 1, where w and E agree.
+// units, with no transcendental per token.  Both sides are bounded so that
+// the test can only err towards scoring a token exactly:
+//  - L, a lower bound of log2 w: w >= n 2^-32 with n = ~word, and for the
+//    float nf of n, log2 nf >= bits(nf) 2^-23 - 127 (log2(1 + f) >= f on
+//    [0, 1)), so L = bits(nf) 2^-23 - 159 - 5e-5 <= log2 w, the 5e-5
+//    covering the roundings of n, of bits(nf) to a float and of the fused
+//    add (together below 1.3e-5);
+//  - R, an upper bound of log2 e - log2 sstar = (x - m) c - log2 sstar,
+//    c = log2(e) / T, formed as fma(x - m, c, -log2 sstar + 2e-3): its
+//    roundings and the hardware log2 stay below 1e-4, so R exceeds the
+//    exact value by at least 1.9e-3 (a factor 1.0013 in the score).
+// A token is rejected only when L > R, i.e. when its exact score is below
+// sstar / 1.0013; the exact scorer's own error (about 1e-7 relative) cannot
+// lift such a token to sstar, so no token that can reach sstar is dropped,
+// ties included.  The bound w <= E is loose only when w is large, i.e. only
+// for tokens whose e is a sizeable share of sstar; the many small tokens of
+// a wide nucleus pass only when u is within e/sstar of 1, where w and E
+// agree.
 template <int G>
 __device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool scored, const RowModel& r, float c_log2e,
                                             const uint32_t i0[G], const float x[G][4], const bool keep[G][4],
@@ -402,9 +407,9 @@ __device__ __forceinline__ void race_groups(const Params& p, int64_t b, bool sco
 #pragma unroll
     for (int g = 0; g < G; ++g)
         w4[g] = philox4x32_10(make_uint4(i0[g] >> 2, (uint32_t)b, p.step_lo, p.step_hi), p.seed_lo, p.seed_hi);
-    // q = -log2 sstar - margin; with no score yet (sstar = 0) every kept
-    // token passes.
-    const float q = sstar > 0.0f ? -__builtin_amdgcn_logf(sstar) - 2e-3f : INFINITY;
+    // q = -log2 sstar + margin (R errs high); with no score yet (sstar = 0)
+    // every kept token passes.
+    const float q = sstar > 0.0f ? -__builtin_amdgcn_logf(sstar) + 2e-3f : INFINITY;
     // Computed for every token and masked afterwards: no branches.  Tokens
     // go in from the last, so token 4 g + j's verdict ends at bit 4 g + j.
     uint32_t rej = 0, kall = 0;

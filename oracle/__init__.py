@@ -106,6 +106,8 @@ class Oracle:
         L.oracle_philox4x32_10.restype = None
         L.oracle_noise_word.argtypes = [u64, u64, i64, i64]
         L.oracle_noise_word.restype = ctypes.c_uint32
+        L.oracle_noise_words.argtypes = [u64, u64, i64, i64, vp]
+        L.oracle_noise_words.restype = None
         L.oracle_exp1.argtypes = [ctypes.c_uint32]
         L.oracle_exp1.restype = ctypes.c_double
         L.oracle_topp_levels.argtypes = [vp, vp, i64, ctypes.c_double, vp, vp, vp]
@@ -284,6 +286,12 @@ class Oracle:
     def noise_word(self, seed, step, row, token):
         return int(self.L.oracle_noise_word(ctypes.c_uint64(seed), ctypes.c_uint64(step), int(row), int(token)))
 
+    def noise_words(self, seed, step, row, n):
+        """Words of tokens 0 .. n-1 of one row (oracle_noise_words)."""
+        out = np.zeros(int(n), dtype=np.uint32)
+        self.L.oracle_noise_words(ctypes.c_uint64(seed), ctypes.c_uint64(step), int(row), int(n), _ptr(out))
+        return out
+
     def exp1(self, word):
         return float(self.L.oracle_exp1(int(word)))
 
@@ -347,6 +355,10 @@ def philox4x32_10(*a, **k):
 
 def noise_word(*a, **k):
     return default().noise_word(*a, **k)
+
+
+def noise_words(*a, **k):
+    return default().noise_words(*a, **k)
 
 
 def exp1(*a, **k):

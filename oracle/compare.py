@@ -324,14 +324,16 @@ class SpecReport:
 
 
 def compare_spec(draft_probs, draft_token, gpu_token, gpu_accepted, gpu_keep_count, gpu_p_at_token, orows,
-                 otarget):
+                 otarget, top_p):
     """Speculative verification outputs against oracle_spec_verify's rows.
 
     * row error (oracle status 1): token -1, not accepted.  Nothing to
       resample (status 2): token -1.
-    * the GPU's target kept a different set than the oracle (a row within
-      the mass band of its cut): the output must be valid for the GPU's own p:
-      the draft token if accepted, else a token with p > q.
+    * the GPU's target kept a different set than the oracle: allowed only
+      for a row within the mass band of its cut (the oracle's A* or M* within
+      MASS_BAND of p, the target's own exemption rule); the output must then
+      be valid for the GPU's own p: the draft token if accepted, else a token
+      with p > q.  A different set on any other row is a failure.
     * the acceptance test within SPEC_REL_TOL p(d) of its boundary: valid as
       above.  Otherwise acceptance exactly; an accepted row outputs d.
     * a rejected row outputs the oracle's residual winner, unless another
@@ -359,6 +361,14 @@ def compare_spec(draft_probs, draft_token, gpu_token, gpu_accepted, gpu_keep_cou
                 rep.failures.append((b, f"row error: gpu {g}/{ga}"))
             continue
         if int(gpu_keep_count[b]) != int(otarget["keep_count"][b]):
+            t = otarget[b]
+            p = float(top_p[b])
+            in_band = bool(t["topp_active"]) and (abs(float(t["a_star"]) - p) <= MASS_BAND or
+                                                 abs(float(t["m_star"]) - p) <= MASS_BAND)
+            if not in_band:
+                rep.failures.append((b, f"target keep count {int(gpu_keep_count[b])} vs oracle "
+                                        f"{int(t['keep_count'])} outside the mass band"))
+                continue
             rep.exempt_cut += 1
             if not valid():
                 rep.failures.append((b, f"different cut: gpu output {g}/{ga} not valid"))

@@ -129,6 +129,20 @@ uint32_t oracle_noise_word(uint64_t seed, uint64_t step, int64_t row, int64_t to
     return out[token & 3];
 }
 
+/* The noise words of tokens 0 .. n-1 of one row, word i at out[i]: the same
+ * words oracle_noise_word gives one at a time (tests use it to place tokens
+ * whose noise has a chosen property). */
+void oracle_noise_words(uint64_t seed, uint64_t step, int64_t row, int64_t n, uint32_t* out)
+{
+    for (int64_t i = 0; i < n; i += 4) {
+        uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+        uint32_t ctr[4] = {(uint32_t)(i >> 2), (uint32_t)row, (uint32_t)step, (uint32_t)(step >> 32)};
+        uint32_t w[4];
+        oracle_philox4x32_10(ctr, key, w);
+        for (int j = 0; j < 4 && i + j < n; ++j) out[i + j] = w[j];
+    }
+}
+
 /* Exp(1) variate from a word: u = (r + 1/2) / 2^32 lies strictly inside (0,1)
  * and is exact in double; E = -ln u. */
 double oracle_exp1(uint32_t r)

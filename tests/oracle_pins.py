@@ -758,7 +758,121 @@ def check_chain_order(O):
     assert O.sample(gp, [0.0], [1.0])[0]["token"][0] == 1
 
 
+# --------------------------------------------------------------------------
+# The judges of boundary rows: oracle_eval_cut and oracle_race_score
+# --------------------------------------------------------------------------
+def _levels_numpy(x, T, k, mp):
+    """Survivor levels of a row from the definitions with numpy's sort:
+    (survivor mask, weights e, sorted distinct survivor values descending,
+    mass strictly above each of them, mass at each), masses normalised over
+    the survivors ("Implement batched top-p sampling with temperature", "How
+    to approach it": a token's mass above is that of every strictly more
+    probable token; "What do temperature, top-k and top-p each do ...",
+    reference sampler: min-p and top-k cut the tempered distribution)."""
+    x = np.asarray(x, dtype=np.float64)
+    fin = x > -np.inf
+    m = x[fin].max()
+    e = np.where(fin, np.exp(np.where(fin, x - m, 0.0) / T), 0.0)
+    surv = fin.copy()
+    if mp > 0:
+        surv &= ~(e < min(mp, 1.0))  # p_i < min_p p_max, with p_max the weight 1 of the max
+    if k > 0:
+        vals = np.sort(x[surv])[::-1]
+        if k < vals.size:
+            surv &= x >= vals[k - 1]
+    S = e[surv].sum()
+    lv, inv = np.unique(x[surv], return_inverse=True)
+    at = np.bincount(inv, weights=e[surv] / S, minlength=lv.size)[::-1]
+    lv = lv[::-1]
+    above = np.concatenate([[0.0], np.cumsum(at)[:-1]])
+    return surv, e, lv, above, at
+
+
+def _race_score_numpy(O, x, row, T, seed, step, tok):
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp((x[tok] - x[x > -np.inf].max()) / T)
+    E = -np.log((O.noise_word(seed, step, row, tok) + 0.5) * 2.0 ** -32)
+    return e / E
+
+
+def check_judges(O, batches=150, seed=31):
+    """oracle_eval_cut and oracle_race_score against the definitions.  They
+    judge the rows within 1e-5 of a mass boundary, where the pages say the
+    keep rule itself is ambiguous under floating point ("Implement batched
+    top-p ...", "Why each line is there", closing paragraph), so they get pins
+    of their own.  Per non-greedy row (tiny random rows with and without
+    min-p/top-k, and rows of the small and tie-heavy workloads):
+    - at the oracle's own smallest kept logit, eval_cut gives the oracle's
+      keep count, token and winning score, and (A, M) of that level as
+      computed here (to 1e-13 + 1e-15 V: the same masses summed in another
+      order); at the survivor levels just above and below, and at a
+      value below every survivor, the masses of those levels and the count
+      of survivors at or above them, and (1, 1) with every survivor kept
+      below the lowest survivor and below every finite logit;
+    - race_score of the drawn token is e/E written out from the token's
+      noise word, and equals the oracle's winning score."""
+    import workloads
+
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(batches):
+        V = int(rng.integers(1, 40))
+        L = (rng.integers(-2, 3, (4, V)) if rng.random() < 1 / 3 else rng.normal(0, 2, (4, V))).astype(np.float32)
+        if rng.random() < 0.3:
+            L[:, rng.random(V) < 0.2] = -np.inf
+            L[:, 0] = 0.5
+        T = rng.choice([0.5, 1.0, 2.0], 4).astype(np.float32)
+        P = np.where(rng.random(4) < 0.1, 1.0, rng.uniform(0.05, 1.0, 4)).astype(np.float32)
+        K = np.where(rng.random(4) < 0.5, rng.integers(1, V + 2, 4), 0).astype(np.int32)
+        MP = np.where(rng.random(4) < 0.5, rng.uniform(0.0, 0.6, 4), 0.0).astype(np.float32)
+        cases.append((L, T, P, K, MP, 99))
+    for n, rows in ((1, None), (2, range(6))):
+        w = workloads.make(n, rows=rows)
+        cases.append((w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], w["seed"]))
+    checked = 0
+    for L, T, P, K, MP, sd in cases:
+        out, _ = O.sample(L, T, P, K, MP, seed=sd)
+        for b in range(L.shape[0]):
+            o = out[b]
+            if o["status"] != 0 or o["greedy"]:
+                continue
+            x = L[b].astype(np.float64)
+            tol = 1e-13 + 1e-15 * x.size  # two summation orders of the same masses
+            surv, e, lv, above, at = _levels_numpy(x, float(T[b]), int(K[b]), float(MP[b]))
+            cut = float(o["min_kept_logit"])
+            ev, _ = O.eval_cut(L[b], b, T[b], P[b], K[b], MP[b], sd, 0, cut)
+            j = int(np.nonzero(lv == cut)[0][0])
+            assert ev["status"] == 0
+            assert ev["keep_count"] == o["keep_count"] == int((surv & (x >= cut)).sum())
+            assert ev["token"] == o["token"]
+            assert abs(ev["race_s1"] - o["race_s1"]) <= 1e-12 * o["race_s1"]
+            assert abs(ev["a_cut"] - above[j]) <= tol and abs(ev["m_cut"] - (above[j] + at[j])) <= tol
+            if o["topp_active"]:
+                assert abs(ev["a_cut"] - o["a_star"]) <= tol and abs(ev["m_cut"] - o["m_star"]) <= tol
+            for jj in (j - 1, j + 1):
+                if 0 <= jj < lv.size:
+                    en, _ = O.eval_cut(L[b], b, T[b], P[b], K[b], MP[b], sd, 0, float(lv[jj]))
+                    assert abs(en["a_cut"] - above[jj]) <= tol
+                    assert abs(en["m_cut"] - (above[jj] + at[jj])) <= tol
+                    assert en["keep_count"] == int((surv & (x >= lv[jj])).sum())
+            # Just below the lowest survivor, and below every finite logit
+            # (where min-p or top-k leave non-survivors): every survivor is
+            # above, nothing else counts.
+            for low in (float(np.nextafter(np.float32(lv[-1]), np.float32(-np.inf))), -3.4028234663852886e38):
+                if low > -np.inf:
+                    en, _ = O.eval_cut(L[b], b, T[b], P[b], K[b], MP[b], sd, 0, low)
+                    assert abs(en["a_cut"] - 1.0) <= tol and abs(en["m_cut"] - 1.0) <= tol
+                    assert en["keep_count"] == int(surv.sum())
+            sc = O.race_score(L[b], b, T[b], sd, 0, int(o["token"]))
+            want = _race_score_numpy(O, x, b, float(T[b]), sd, 0, int(o["token"]))
+            assert abs(sc - want) <= 1e-12 * want and abs(sc - o["race_s1"]) <= 1e-12 * want
+            checked += 1
+    assert checked > 400
+    return checked
+
+
 ALL_FAST_CHECKS = [check_worked_examples, check_order_counterexample, check_special_cases, check_invariants,
                    check_exp1, check_race_reproducible, check_logprobs, check_row_seeds, check_rejection_pages,
                    check_rejection_law, check_rejection_is_the_race, check_spec_law, check_spec_special,
-                   check_preprocess_values, check_preprocess_identity_and_invariants, check_chain_order]
+                   check_preprocess_values, check_preprocess_identity_and_invariants, check_chain_order,
+                   check_judges]

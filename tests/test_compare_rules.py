@@ -66,15 +66,23 @@ def test_compare_spec_accepts_the_oracle_and_rejects_mistakes():
     tok, acc = o["token"].copy(), o["accepted"].copy()
     p_at = probs[np.arange(w["B"]), np.clip(tok, 0, w["V"] - 1)]
     cnt = rows["keep_count"]
-    assert compare_spec(q, d, tok, acc, cnt, p_at, o, rows).ok()
+    assert compare_spec(q, d, tok, acc, cnt, p_at, o, rows, w["top_p"]).ok()
     clear = np.nonzero((o["status"] == 0) & (np.abs(o["u"] * o["q_draft"] - o["p_draft"]) > 1e-3))[0]
     b = int(clear[0])
     bad = acc.copy()
     bad[b] = 1 - bad[b]
-    assert not compare_spec(q, d, tok, bad, cnt, p_at, o, rows).ok()     # the other acceptance
+    assert not compare_spec(q, d, tok, bad, cnt, p_at, o, rows, w["top_p"]).ok()     # the other acceptance
     rej = [int(r) for r in clear if o["accepted"][r] == 0 and o["threat"][r] < 0.5 * o["s1_low"][r]]
     if rej:
         r = rej[0]
         bad = tok.copy()
         bad[r] = d[r] if d[r] != tok[r] else (tok[r] + 1) % w["V"]
-        assert not compare_spec(q, d, bad, acc, cnt, p_at, o, rows).ok()  # another residual draw
+        assert not compare_spec(q, d, bad, acc, cnt, p_at, o, rows, w["top_p"]).ok()  # another residual draw
+    # A different target cut on a row far from the mass band is a failure,
+    # even when the output would be valid for that other cut.
+    far = [int(r) for r in np.nonzero((rows["status"] == 0) & (rows["greedy"] == 0) & (rows["topp_active"] == 1))[0]
+           if min(abs(rows["a_star"][r] - w["top_p"][r]), abs(rows["m_star"][r] - w["top_p"][r])) > 1e-3]
+    r = far[0]
+    bad = cnt.copy()
+    bad[r] += 1
+    assert not compare_spec(q, d, tok, acc, bad, p_at, o, rows, w["top_p"]).ok()  # another cut, outside the band

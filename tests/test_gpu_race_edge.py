@@ -1,0 +1,44 @@
+"""Race winners that beat the running best by a hair, on every path.
+
+Rows from tests/race_edge_rows.py: every token but one scores within 5e-5
+below the max token's score, and the planted winner scores 2e-5 above it with
+noise for which the race screen's bound is tight.  Every path of the sampler
+must return the oracle's token (the planted winner) on every row ("What do
+temperature, top-k and top-p each do ...", "A strong answer", last
+paragraph: the race draws exactly from p).
+"""
+import numpy as np
+import pytest
+
+import race_edge_rows
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [None, "single", "split", "rows"]
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_race_edge_rows(path, oracle_lib):
+    import torch
+
+    import nucleus_sampling_amd as ns
+
+    o = oracle_lib.default()
+    B, V = 16, 32768
+    L, T, S, W = race_edge_rows.build(o, B, V, base_seed=901)
+    P = np.ones(B, np.float32)
+    K = np.zeros(B, np.int32)
+    MP = np.zeros(B, np.float32)
+    rows, _ = oracle_lib.sample(L, T, P, K, MP, seed=0, seeds=S)
+    assert np.array_equal(rows["token"], W)
+    say(f"race edge rows B={B} V={V} path={path}")
+    lg = torch.from_numpy(L).to("cuda:0")
+    res = ns.sample(lg, T, P, K, MP, seed=0, step=0, seeds=S, single_workgroup=path == "single",
+                    split_rows=path == "split", row_race=path == "rows")
+    torch.cuda.synchronize()
+    tok = res.token.cpu().numpy()
+    cnt = res.keep_count.cpu().numpy()
+    say(f"path={path}: tokens {tok.tolist()}")
+    assert np.array_equal(tok, W), (tok, W)
+    assert np.array_equal(cnt, rows["keep_count"])

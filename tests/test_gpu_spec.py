@@ -41,7 +41,7 @@ def _check(w, q, d, tok, acc, cnt, p_at, seed=None, step=0, seeds=None):
                                step=step, seeds=seeds, rel_tol=SPEC_REL_TOL, threads=16)
     otarget, _ = oracle.sample(w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], seed=s, step=step,
                                threads=16, seeds=seeds)
-    return compare_spec(q, d, tok, acc, cnt, p_at, orows, otarget)
+    return compare_spec(q, d, tok, acc, cnt, p_at, orows, otarget, w["top_p"])
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])

@@ -3,7 +3,8 @@ build each copy, and require the pins to reject every one of them.  This is
 evidence that the pins constrain each step of the oracle: the boundary
 comparison, the always-kept top level, greedy tie-breaking, the temperature,
 min-p, top-k, renormalisation, validation, Philox, the race, the
-rejection sampler and speculative acceptance."""
+rejection sampler, speculative acceptance, the pre-chain, and the judges of
+boundary rows (oracle_eval_cut, oracle_race_score)."""
 import os
 import shutil
 
@@ -52,6 +53,13 @@ MUTATIONS = [
      "volatile float y = x / rho;"),
     ("duplicates counted once", "if (tok >= 0 && tok < V) count[tok] += 1;", "if (tok >= 0 && tok < V) count[tok] = 1;"),
     ("presence per occurrence", "pen = pen + ap;", "pen = pen + ap * (float)count[i];"),
+    ("judge mass over every finite token", "        if (!r.surv[i]) continue;\n        if (r.x[i] > cut) above += r.e[i];",
+     "        if (!(r.x[i] > -INFINITY)) continue;\n        if (r.x[i] > cut) above += r.e[i];"),
+    ("judge mass above inclusive", "if (r.x[i] > cut) above += r.e[i];", "if (r.x[i] >= cut) above += r.e[i];"),
+    ("judge keeps only above the cut", "if (r.surv[i] && r.x[i] >= cut) { keep[i] = 1;",
+     "if (r.surv[i] && r.x[i] > cut) { keep[i] = 1;"),
+    ("race score without the row max", "double e = exp((x - m) / (double)temperature);",
+     "double e = exp(x / (double)temperature);"),
     ("mask bits reversed", "(allowed[b * words + i / 32] >> (i % 32)) & 1u", "(allowed[b * words + i / 32] >> (31 - i % 32)) & 1u"),
 ]
 
