@@ -17,19 +17,39 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnucleus.so")
 SOURCES = [os.path.join(CSRC, "nucleus.hip")]
+OBJDIR = os.path.join(ROOT, "_build")
+EXTRA = {}  # per-source extra hipcc flags
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, only=None) -> str:
+    """Compile every source to an object (in parallel), then link the
+    library.  ``only`` (a list of source basenames) recompiles just those and
+    relinks with the other objects as they are."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+        objs.append(obj)
+        if only is not None and os.path.basename(src) not in only and os.path.exists(obj):
+            continue
+        cmd = [hipcc, *HIPCC_FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", "-o", obj + ".tmp", src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd), obj))
+    for pr, obj in procs:
+        if pr.wait() != 0:
+            raise subprocess.CalledProcessError(pr.returncode, f"hipcc -c for {obj}")
+        os.replace(obj + ".tmp", obj)
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *SOURCES]
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -38,4 +58,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    only = [a for a in sys.argv[1:] if a.endswith(".hip")] or None
+    build(verbose="-v" in sys.argv, only=only)

@@ -66,9 +66,10 @@ __device__ __forceinline__ int32_t cvt_i32_sat(double x)
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
 // as 1, 2, 3", SC'11): per round, words 0 and 2 are multiplied by the two
 // round multipliers; the new state is (hi1^c1^k0, lo1, hi0^c3^k1, lo0); the
-// key advances by the two Weyl constants between rounds.  The key is
-// wave-uniform at every call, so its schedule lives in scalar registers, and
-// each round's two three-way XORs take one instruction each.
+// key advances by the two Weyl constants between rounds.  philox4x32_10
+// needs a wave-uniform key (its schedule lives in scalar registers, and each
+// round's two three-way XORs take one instruction each);
+// philox4x32_10_lanes takes a key per lane.
 // ---------------------------------------------------------------------------
 
 // a ^ b ^ k for a wave-uniform k: gfx950's three-input bitwise operation with
@@ -82,6 +83,13 @@ __device__ __forceinline__ uint32_t xor3_uniform(uint32_t a, uint32_t b, uint32_
 
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1)
 {
+    // The key schedule is recomputed at every call by scalar adds: left to
+    // itself the compiler hoists the twenty round keys out of the callers'
+    // loops, runs out of scalar registers and reads them back with one VALU
+    // readlane per round key.
+    k0 = (uint32_t)__builtin_amdgcn_readfirstlane(k0);  // wave-uniform by contract
+    k1 = (uint32_t)__builtin_amdgcn_readfirstlane(k1);
+    asm volatile("" : "+s"(k0), "+s"(k1));
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c.x;
@@ -96,6 +104,23 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 }
 
 // ---------------------------------------------------------------------------
+// The same generator for a key that may differ between lanes (one row per
+// lane): plain XORs, no scalar operands.
+__device__ __forceinline__ uint4 philox4x32_10_lanes(uint4 c, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c.x;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
 // Tempered weight e = exp((x - m)/T) in fp32 with the argument carried to
 // about one extra word of precision: x - m is split exactly (TwoSum), the
 // quotient's remainder is exact by fma, and e^(q + lo) = e^q (1 + lo).  The

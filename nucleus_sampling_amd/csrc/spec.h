@@ -74,7 +74,8 @@ __device__ __forceinline__ SpecRow spec_row(const SpecParams& sp, int64_t b)
     r.accepted = false;
     if (!r.bad) {
         const float pd = sp.target[b * sp.V + r.d], qd = sp.draft[b * sp.V + r.d];
-        const uint4 wu = philox4x32_10(make_uint4(0xFFFFFFFFu, r.crow, sp.step_lo, sp.step_hi), r.klo, r.khi);
+        // spec_finish_kernel takes one row per lane: the key may differ between lanes.
+        const uint4 wu = philox4x32_10_lanes(make_uint4(0xFFFFFFFFu, r.crow, sp.step_lo, sp.step_hi), r.klo, r.khi);
         const double u = ((double)wu.x + 0.5) * 0x1p-32;
         r.accepted = u * (double)qd < (double)pd;
     }
