@@ -172,6 +172,31 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
                    const nucleus_options* opt);
 
 /*
+ * nucleus_sample for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and return codes as nucleus_sample, except that the
+ * scratch the chosen path needs (the split-row and row-race paths; the
+ * one-workgroup-per-row path needs none) comes from a static device array of
+ * nucleus_noalloc_scratch_bytes() bytes (32 MiB) that the library holds on
+ * every GPU it runs on until the process ends; opt->workspace and
+ * opt->workspace_bytes are ignored.  Returns NUCLEUS_EWORKSPACE, launching
+ * nothing, when the call's path needs more scratch than that (for example
+ * B = 127 rows of 524288 tokens on the split-row path); NUCLEUS_EDEVICE if
+ * the runtime cannot give the array's address.  Makes no device allocation.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or other threads) race and give undefined
+ * results.  The array needs no initial value: each call tags its
+ * synchronisation words with a value of its own.
+ */
+int nucleus_sample_noalloc(const void* logits, int64_t B, int64_t V, const float* temperature,
+                           const float* top_p, const int32_t* top_k, const float* min_p, uint64_t seed,
+                           uint64_t step, int32_t* out_token, int32_t* out_keep_count, float* out_probs,
+                           const nucleus_options* opt);
+
+/* Size in bytes of nucleus_sample_noalloc's static scratch on each GPU. */
+size_t nucleus_noalloc_scratch_bytes(void);
+
+/*
  * Sample one token per row by sort-free rejection ("Top-p (Nucleus) Sampling,
  * in depth", "Sort-free top-p by rejection sampling"): a second algorithm for
  * the chain above without top-k (temperature -> min-p -> top-p -> sample),

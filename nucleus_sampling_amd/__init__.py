@@ -67,6 +67,10 @@ def lib():
         vp, i64, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64
         L.nucleus_sample.argtypes = [vp, i64, i64, vp, vp, vp, vp, u64, u64, vp, vp, vp, ctypes.POINTER(_Options)]
         L.nucleus_sample.restype = ctypes.c_int
+        L.nucleus_sample_noalloc.argtypes = L.nucleus_sample.argtypes
+        L.nucleus_sample_noalloc.restype = ctypes.c_int
+        L.nucleus_noalloc_scratch_bytes.argtypes = []
+        L.nucleus_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.nucleus_sample_rejection.argtypes = [vp, i64, i64, vp, vp, vp, u64, u64, vp, vp, ctypes.POINTER(_Options)]
         L.nucleus_sample_rejection.restype = ctypes.c_int
         L.nucleus_spec_verify.argtypes = [vp, vp, vp, i64, i64, u64, u64, vp, vp, ctypes.POINTER(_Options)]
@@ -154,7 +158,7 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
            workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
            single_workgroup: bool = False, split_rows: bool = False, row_race: bool = False,
            seeds=None, want_logprobs: bool = False, history=None, repetition_penalty=None,
-           frequency_penalty=None, presence_penalty=None, allowed_mask=None) -> SampleResult:
+           frequency_penalty=None, presence_penalty=None, allowed_mask=None, noalloc: bool = False) -> SampleResult:
     """Sample one token per row of ``logits`` [B, V] (float32 or bfloat16 on a
     gfx950 device; rows may be strided, the last dimension must be dense).
 
@@ -175,6 +179,9 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     / ``presence_penalty`` [B], and ``allowed_mask`` [B, ceil(V/32)] 32-bit
     words (bit i % 32 of word i // 32 allows token i), applied to the raw
     logits before the chain.
+
+    ``noalloc`` calls nucleus_sample_noalloc instead: the library's static
+    per-GPU scratch replaces the workspace (nothing is allocated for it).
     """
     if logits.dim() != 2:
         raise ValueError("logits must be [B, V]")
@@ -213,7 +220,7 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     flags = ((NUCLEUS_FLAG_SINGLE_WORKGROUP if single_workgroup else 0) | (NUCLEUS_FLAG_SPLIT_ROWS if split_rows else 0)
              | (NUCLEUS_FLAG_ROW_RACE if row_race else 0))
-    need = workspace_bytes(B, V, logits.dtype, flags)
+    need = 0 if noalloc else workspace_bytes(B, V, logits.dtype, flags)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = workspace_for(dev, s, need)
     opt = _Options()
@@ -237,10 +244,11 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     def ptr(t):
         return None if t is None else t.data_ptr()
 
-    rc = lib().nucleus_sample(ptr(logits), B, V, ptr(T), ptr(P), ptr(K), ptr(MP), ctypes.c_uint64(seed),
-                              ctypes.c_uint64(step), ptr(out.token), ptr(out.keep_count), ptr(out.probs),
-                              ctypes.byref(opt))
-    _check(rc, "nucleus_sample")
+    entry = lib().nucleus_sample_noalloc if noalloc else lib().nucleus_sample
+    rc = entry(ptr(logits), B, V, ptr(T), ptr(P), ptr(K), ptr(MP), ctypes.c_uint64(seed),
+               ctypes.c_uint64(step), ptr(out.token), ptr(out.keep_count), ptr(out.probs),
+               ctypes.byref(opt))
+    _check(rc, "nucleus_sample_noalloc" if noalloc else "nucleus_sample")
     return out
 
 

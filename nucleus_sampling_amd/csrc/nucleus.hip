@@ -123,11 +123,35 @@ bool has_prechain(const nucleus_options* opt)
                    opt->frequency_penalty || opt->presence_penalty);
 }
 
+// The scratch of nucleus_sample_noalloc: one static array per GPU, never
+// allocated by a call.  In host code the array's name stands for a host-side
+// shadow, not a device address: every use goes through the address
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// The current device's address of `scratch`, looked up once per device;
+// nullptr if the runtime cannot give it.
+void* static_scratch()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    static std::mutex mu;
+    static void* known[64] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!known[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        known[dev] = ptr;
+    }
+    return known[dev];
+}
+
 }  // namespace
 
 extern "C" {
 
-int nucleus_version(void) { return 240; }
+int nucleus_version(void) { return 250; }
 
 const char* nucleus_strerror(int code)
 {
@@ -276,6 +300,30 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     }
     return hipGetLastError() == hipSuccess ? NUCLEUS_OK : NUCLEUS_ELAUNCH;
 }
+
+int nucleus_sample_noalloc(const void* logits, int64_t B, int64_t V, const float* temperature, const float* top_p,
+                           const int32_t* top_k, const float* min_p, uint64_t seed, uint64_t step, int32_t* out_token,
+                           int32_t* out_keep_count, float* out_probs, const nucleus_options* opt)
+{
+    nucleus_options o = {};
+    if (opt) o = *opt;
+    const int32_t dtype = o.dtype;
+    if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16))
+        return NUCLEUS_EINVAL;
+    const int path = has_prechain(&o) ? kPathFused : choose_path(B, V, o.flags);
+    if (path < 0) return NUCLEUS_EINVAL;
+    if (path_workspace(path, B, V) > kStaticScratchBytes) return NUCLEUS_EWORKSPACE;
+    const int dev_rc = check_device();
+    if (dev_rc != NUCLEUS_OK) return dev_rc;
+    void* ws = static_scratch();
+    if (!ws) return NUCLEUS_EDEVICE;
+    o.workspace = ws;
+    o.workspace_bytes = kStaticScratchBytes;
+    return nucleus_sample(logits, B, V, temperature, top_p, top_k, min_p, seed, step, out_token, out_keep_count,
+                          out_probs, &o);
+}
+
+size_t nucleus_noalloc_scratch_bytes(void) { return kStaticScratchBytes; }
 
 int nucleus_sample_rejection(const void* logits, int64_t B, int64_t V, const float* temperature, const float* top_p,
                              const float* min_p, uint64_t seed, uint64_t step, int32_t* out_token,

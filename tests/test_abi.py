@@ -188,3 +188,28 @@ def test_prechain_host_side_argument_errors(L):
     assert _call(L, V=166913, opt=opt(presence_penalty=1 << 26)) == EINVAL
     assert _call_rej(L, opt=opt(allowed_mask=1 << 26)) == EINVAL                # other entry points refuse it
     assert _call_spec(L, opt=opt(repetition_penalty=1 << 26, workspace=1 << 27, workspace_bytes=1 << 20)) == EINVAL
+
+
+def _call_na(L, logits=1 << 20, B=2, V=8, T=1 << 21, P=1 << 22, tok=1 << 23, cnt=1 << 24, opt=None):
+    # Fake, never-dereferenced device addresses, as above.
+    return L.nucleus_sample_noalloc(logits, B, V, T, P, None, None, ctypes.c_uint64(0), ctypes.c_uint64(0), tok, cnt,
+                                    None, opt)
+
+
+def test_noalloc_host_side_checks(L):
+    """nucleus_sample_noalloc: its static scratch is 32 MiB per GPU; a call
+    whose path needs more is refused on the host before any launch, as are
+    bad arguments."""
+    import nucleus_sampling_amd as ns
+
+    assert L.nucleus_noalloc_scratch_bytes() == 32 << 20
+    opt = ns._Options()
+    opt.flags = 2  # split rows: 127 rows of 64 chunks need ~100 MB of per-chunk slots and lists
+    assert L.nucleus_workspace_bytes_for(127, 64 * 8192, 0, 2) > L.nucleus_noalloc_scratch_bytes()
+    assert _call_na(L, B=127, V=64 * 8192, opt=ctypes.byref(opt)) == -2
+    assert _call_na(L, B=-1) == -1
+    assert _call_na(L, V=0) == -1
+    opt = ns._Options()
+    opt.flags = 3  # two flags
+    assert _call_na(L, opt=ctypes.byref(opt)) == -1
+    assert _call_na(L, B=0) in (0, -4)  # no batch: nothing to launch (or no usable device here)
