@@ -137,6 +137,14 @@ typedef struct nucleus_options {
     const uint32_t* allowed_mask;      /* optional device [B, ceil(V/32)] uint32: token i allowed iff
                                           bit (i mod 32) of word i / 32 is set (a grammar / JSON
                                           constraint) */
+    /* Since version 260, for tests of the failure path only ("Top-p (Nucleus)
+     * Sampling, in depth", "Failure modes": a failing request must not hang
+     * the batch): */
+    int64_t split_give_up_row;   /* 0: off.  r + 1 (r >= 0): on the split-row path the workgroups
+                                    of row r give up every wait at once, as if the row's
+                                    workgroups could not meet, so row r reports token -2 and
+                                    every other row is sampled as usual.  Ignored by the other
+                                    paths; negative is NUCLEUS_EINVAL. */
 } nucleus_options;
 
 /*
@@ -155,7 +163,8 @@ typedef struct nucleus_options {
  *                 the draws exactly.
  * out_token       device [B] int32: the sampled id, or -1 on a row error (-2 if, on the
  *                 split-row path, the workgroups of a row could not meet within
- *                 seconds, e.g. because other work held the whole device).
+ *                 seconds, e.g. because other work held the whole device; that row's
+ *                 other outputs are then not written, and the other rows are unaffected).
  * out_keep_count  device [B] int32: size of the kept set (1 for greedy rows,
  *                 0 on a row error).
  * out_probs       device [B, V] float, or NULL: the renormalised kept

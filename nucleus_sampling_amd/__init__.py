@@ -51,6 +51,7 @@ class _Options(ctypes.Structure):
         ("frequency_penalty", ctypes.c_void_p),
         ("presence_penalty", ctypes.c_void_p),
         ("allowed_mask", ctypes.c_void_p),
+        ("split_give_up_row", ctypes.c_int64),
     ]
 
 
@@ -158,7 +159,8 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
            workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None,
            single_workgroup: bool = False, split_rows: bool = False, row_race: bool = False,
            seeds=None, want_logprobs: bool = False, history=None, repetition_penalty=None,
-           frequency_penalty=None, presence_penalty=None, allowed_mask=None, noalloc: bool = False) -> SampleResult:
+           frequency_penalty=None, presence_penalty=None, allowed_mask=None, noalloc: bool = False,
+           split_give_up_row: Optional[int] = None) -> SampleResult:
     """Sample one token per row of ``logits`` [B, V] (float32 or bfloat16 on a
     gfx950 device; rows may be strided, the last dimension must be dense).
 
@@ -182,6 +184,10 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
 
     ``noalloc`` calls nucleus_sample_noalloc instead: the library's static
     per-GPU scratch replaces the workspace (nothing is allocated for it).
+
+    ``split_give_up_row`` (tests of the failure path only): on the split-row
+    path, that row's workgroups give up their waits at once and the row
+    reports token -2.
     """
     if logits.dim() != 2:
         raise ValueError("logits must be [B, V]")
@@ -240,6 +246,7 @@ def sample(logits: torch.Tensor, temperature, top_p, top_k=None, min_p=None, see
     opt.frequency_penalty = FP.data_ptr() if FP is not None else None
     opt.presence_penalty = PP.data_ptr() if PP is not None else None
     opt.allowed_mask = AM.data_ptr() if AM is not None else None
+    opt.split_give_up_row = 0 if split_give_up_row is None else int(split_give_up_row) + 1
 
     def ptr(t):
         return None if t is None else t.data_ptr()

@@ -151,7 +151,7 @@ void* static_scratch()
 
 extern "C" {
 
-int nucleus_version(void) { return 250; }
+int nucleus_version(void) { return 260; }
 
 const char* nucleus_strerror(int code)
 {
@@ -185,6 +185,7 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     const int64_t stride = (opt && opt->row_stride) ? opt->row_stride : V;
     if (B < 0 || V < 1 || V >= (int64_t(1) << 31) || stride < V) return NUCLEUS_EINVAL;
     if (dtype != NUCLEUS_F32 && dtype != NUCLEUS_BF16) return NUCLEUS_EINVAL;
+    if (opt && opt->split_give_up_row < 0) return NUCLEUS_EINVAL;
     const bool pre = has_prechain(opt);
     if (pre) {
         if (opt->history_len < 0 || opt->history_len > kHistMax || (opt->history_len > 0 && !opt->history))
@@ -255,6 +256,7 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
         wk.cand = (uint2*)(ws + L.cand);
         wk.K = K;
         wk.epoch = next_epoch();
+        wk.give_up_row = opt->split_give_up_row - 1;  // opt is set: this path needs its workspace
         const dim3 grid((unsigned)(padded_rows(B) * K)), block(kThreads);
         if (dtype == NUCLEUS_F32)
             hipLaunchKernelGGL(tile_kernel<kF32>, grid, block, 0, s, p, wk);

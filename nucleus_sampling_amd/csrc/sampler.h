@@ -243,12 +243,14 @@ __device__ __forceinline__ void barrier_release(RowCtl* c)
 }
 
 // Every thread of a workgroup that arrived but was not last.  Returns false
-// if the wait timed out.
-__device__ __forceinline__ bool barrier_wait(RowCtl* c, BarrierShared& bs)
+// if the wait timed out; with give_up it gives up at once, without looking
+// (the failure path, driven from the host by tests).
+__device__ __forceinline__ bool barrier_wait(RowCtl* c, BarrierShared& bs, bool give_up)
 {
     if (threadIdx.x == 0) {
         uint32_t n = 0;
-        while (get(&c->gen) == bs.g0) {
+        if (give_up) bs.timeout = 1;
+        while (!give_up && get(&c->gen) == bs.g0) {
             __builtin_amdgcn_s_sleep(1);
             if (++n > kSpinLimit) {
                 bs.timeout = 1;
@@ -863,6 +865,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
     const int64_t base = (int64_t)chunk * kChunk;
     RowCtl* ctl = wk.ctl + b;
     const int64_t wg = b * K + chunk;
+    const bool give_up = b == wk.give_up_row;
     use_row_key(p, b);
     const bool want_probs = wants_dist(p);  // probabilities or log-probabilities
 
@@ -909,7 +912,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
             cstore32(rc, kOffMode, first_mode(e != 0, m, rp.T, rp.P, rp.MP, rp.K, want_probs));
         }
         barrier_release(ctl);
-    } else if (!barrier_wait(ctl, sh.bar)) {
+    } else if (!barrier_wait(ctl, sh.bar, give_up)) {
         timed_out(p, b);
         return;
     }
@@ -1003,7 +1006,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
                 cstore64(rc, kOffStotal, (uint64_t)__double_as_longlong(d.s_total));
             }
             barrier_release(ctl);
-        } else if (!barrier_wait(ctl, sh.bar)) {
+        } else if (!barrier_wait(ctl, sh.bar, give_up)) {
             timed_out(p, b);
             return;
         }
@@ -1153,7 +1156,7 @@ __global__ __launch_bounds__(kThreads, 4) void tile_kernel(Params p, Work wk)
         return;
     }
     if (!want_probs) return;
-    if (!barrier_wait(ctl, sh.bar)) {
+    if (!barrier_wait(ctl, sh.bar, give_up)) {
         timed_out(p, b);
         return;
     }

@@ -53,6 +53,7 @@ struct Work {
     uint2* cand;          // [rows][kCap]: key, index
     int K;                // workgroups per row
     uint64_t epoch;       // this call's tag (56 bits), distinct for every call
+    int64_t give_up_row;  // -1; else the row whose waits give up at once (failure-path tests)
 };
 
 // Per-row state of the row path (row_kernel publishes the decided state and

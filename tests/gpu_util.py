@@ -54,3 +54,50 @@ def oracle_and_compare(w, tok, cnt, mk, step=0, gpu_probs=None, prob_rows=None, 
                   rows, gpu_probs=gpu_probs, oracle_probs=op, prob_rows=prob_rows, seeds=seeds,
                   gpu_logprobs=gpu_logprobs, oracle_logprobs=ol)
     return rep, rows
+
+
+def _merge(total, rep, r0):
+    for f in ("rows", "exact", "errors_ok", "greedy", "exempt_mass", "exempt_mass_exact", "exempt_race",
+              "exempt_minp", "near_1e6", "near_1e7"):
+        setattr(total, f, getattr(total, f) + getattr(rep, f))
+    total.max_prob_ratio = max(total.max_prob_ratio, rep.max_prob_ratio)
+    total.max_logprob_ratio = max(total.max_logprob_ratio, rep.max_logprob_ratio)
+    total.failures.extend((b + r0, why) for b, why in rep.failures)
+
+
+def compare_every_row(w, tok, cnt, mk, probs_dev=None, logprobs_dev=None, step=0, seed=None, seeds=None, chunk=128,
+                      threads=16):
+    """Every row of a batch against the oracle, with its probabilities and
+    log-probabilities when the device tensors are given, a chunk of rows at a
+    time: the oracle's float64 arrays for a whole 1024 x 152064 batch alone
+    would take 2.5 GB of host memory.  Each chunk keeps its rows' own indices
+    (the race counter) and keys.  Returns (Report over the batch, the
+    oracle's rows)."""
+    import oracle
+    from oracle import ROW_DTYPE
+    from oracle.compare import Report, compare
+
+    B = w["B"]
+    s = w["seed"] if seed is None else seed
+    T, P = np.asarray(w["temperature"], np.float32), np.asarray(w["top_p"], np.float32)
+    K = np.zeros(B, np.int32) if w.get("top_k") is None else np.asarray(w["top_k"], np.int32)
+    MP = np.zeros(B, np.float32) if w.get("min_p") is None else np.asarray(w["min_p"], np.float32)
+    total, orows = Report(), np.zeros(B, ROW_DTYPE)
+    want_p, want_l = probs_dev is not None, logprobs_dev is not None
+    for r0 in range(0, B, chunk):
+        r1 = min(B, r0 + chunk)
+        sl = slice(r0, r1)
+        res = oracle.sample(w["logits"], T, P, K, MP, seed=s, step=step, rows=range(r0, r1), want_probs=want_p,
+                            threads=threads, seeds=seeds, want_logprobs=want_l)
+        o, op = res[0], res[1]
+        ol = res[2] if want_l else None
+        orows[sl] = o[sl]
+        gp = probs_dev[r0:r1].cpu().numpy() if want_p else None
+        gl = logprobs_dev[r0:r1].cpu().numpy() if want_l else None
+        rep = compare(w["logits"][sl], T[sl], P[sl], K[sl], MP[sl], s, step, tok[sl], cnt[sl],
+                      None if mk is None else mk[sl], o[sl], gpu_probs=gp, oracle_probs=op,
+                      prob_rows=list(range(r1 - r0)) if (want_p or want_l) else None,
+                      batch_rows=np.arange(r0, r1), seeds=None if seeds is None else seeds[sl], gpu_logprobs=gl,
+                      oracle_logprobs=ol)
+        _merge(total, rep, r0)
+    return total, orows

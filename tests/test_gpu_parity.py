@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import device_logits, oracle_and_compare, say
+from gpu_util import compare_every_row, device_logits, oracle_and_compare, say
 
 pytestmark = pytest.mark.gpu
 
@@ -45,25 +45,51 @@ def _gpu(w, step=0, want_probs=False, prob_rows=None, seed=None, lg=None, path=N
     return out + (logprobs,) if want_logprobs else out
 
 
-PROB_ROWS = {1: list(range(15)), 2: [0, 1, 2, 3, 17, 40, 63], 3: [0, 1, 2, 3, 100, 255], 4: [0, 1, 2, 3, 9, 200],
-             5: [0, 1, 2, 5, 9, 500, 1023]}
+def _gpu_dev(w, step=0, want_probs=False, seed=None, lg=None, path=None, seeds=None, want_logprobs=False):
+    """One call; the result's tensors stay on the device."""
+    import torch
+
+    import nucleus_sampling_amd as ns
+
+    lg = device_logits(w["logits"], w["dtype"]) if lg is None else lg
+    res = ns.sample(lg, w["temperature"], w["top_p"], w["top_k"], w["min_p"],
+                    seed=w["seed"] if seed is None else seed, step=step, want_probs=want_probs, want_min_kept=True,
+                    single_workgroup=path == "single", split_rows=path == "split", row_race=path == "rows",
+                    seeds=seeds, want_logprobs=want_logprobs)
+    torch.cuda.synchronize()
+    return res
+
+
+def _host(res):
+    return res.token.cpu().numpy(), res.keep_count.cpu().numpy(), res.min_kept_logit.cpu().numpy()
+
+
+def _same_bits(a, b):
+    """Two device tensors hold the same bits (NaN included)."""
+    import torch
+
+    return a.shape == b.shape and bool(torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32)))
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_workload_parity(n):
+    """Every row of every workload against the oracle: keep set, token and
+    the renormalised probabilities of all V tokens."""
     say(f"workload {n} ({workloads.NAMES[n]}) shape={workloads.SHAPES[n]} {workloads.DTYPES[n]}: generating")
     w = workloads.make(n)
+    lg = device_logits(w["logits"], w["dtype"])
     say(f"workload {n}: sampling on cuda:0 (no probs: the benchmark's launch)")
-    tok, cnt, mk, _ = _gpu(w)
-    rep, orows = oracle_and_compare(w, tok, cnt, mk)
-    say(f"workload {n}: {rep.summary()}")
-    assert rep.ok(), rep.failures
-    say(f"workload {n}: sampling with probabilities for rows {PROB_ROWS[n]}")
-    tok2, cnt2, mk2, probs = _gpu(w, want_probs=True, prob_rows=PROB_ROWS[n])
+    tok, cnt, mk = _host(_gpu_dev(w, lg=lg))
+    say(f"workload {n}: sampling with probabilities")
+    res = _gpu_dev(w, lg=lg, want_probs=True)
+    tok2, cnt2, mk2 = _host(res)
     assert np.array_equal(tok, tok2) and np.array_equal(cnt, cnt2)
-    rep2, _ = oracle_and_compare(w, tok2, cnt2, mk2, gpu_probs=probs, prob_rows=PROB_ROWS[n])
-    say(f"workload {n} probs: {rep2.summary()}")
-    assert rep2.ok(), rep2.failures
+    assert np.array_equal(mk.view(np.uint32), mk2.view(np.uint32))
+    say(f"workload {n}: every row and its probabilities against the oracle, 128 rows at a time")
+    rep, _ = compare_every_row(w, tok2, cnt2, mk2, probs_dev=res.probs)
+    say(f"workload {n}: {rep.summary()}")
+    assert rep.rows == w["B"]
+    assert rep.ok(), rep.failures
 
 
 def _random_batch(rng, B, V, dtype, extras=True):
@@ -283,20 +309,18 @@ def test_draws_match_oracle_on_worked_example():
 def test_paths_agree_bit_for_bit(n):
     """Every path takes the same decisions with the same arithmetic: the
     split-row path, the single-workgroup path and the chunked-race path give
-    identical outputs, bit for bit, including the probabilities."""
-    rows = PROB_ROWS[n]
-    w = workloads.make(n)
+    identical outputs, bit for bit, including every row's probabilities."""
     import torch
 
+    w = workloads.make(n)
     lg = device_logits(w["logits"], w["dtype"])
     say(f"workload {n}: default path")
-    a = _gpu(w, lg=lg, want_probs=True, prob_rows=rows)
+    a = _gpu_dev(w, lg=lg, want_probs=True)
     for path in PATHS[1:]:
         say(f"workload {n}: path {path}")
-        b = _gpu(w, lg=lg, want_probs=True, prob_rows=rows, path=path)
-        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), path
-        assert np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32)), path
-        assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32)), path
+        b = _gpu_dev(w, lg=lg, want_probs=True, path=path)
+        for f in ("token", "keep_count", "min_kept_logit", "probs"):
+            assert _same_bits(getattr(a, f), getattr(b, f)), (path, f)
     torch.cuda.synchronize()
 
 
@@ -332,33 +356,36 @@ def test_crossing_bin_overflow(dtype):
                    for x, y in zip(a, b)), path
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_logprobs_and_row_seeds(n):
     """Per-request race keys and the processed distribution's
-    log-probabilities (-inf outside the nucleus) against the oracle; every
-    path gives the same bits."""
+    log-probabilities (-inf outside the nucleus) against the oracle on every
+    row; every path gives the same bits."""
+    import torch
+
     w = workloads.make(n)
     B = w["B"]
     seeds = (np.arange(B, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15) + np.uint64(12345)).astype(np.uint64)
-    rows = PROB_ROWS[n]
-    say(f"workload {n}: per-row keys and log-probabilities for rows {rows}")
-    first = _gpu(w, want_probs=True, prob_rows=rows, seeds=seeds, want_logprobs=True)
-    tok, cnt, mk, probs, lps = first
-    rep, _ = oracle_and_compare(w, tok, cnt, mk, gpu_probs=probs, prob_rows=rows, seeds=seeds, gpu_logprobs=lps)
+    lg = device_logits(w["logits"], w["dtype"])
+    say(f"workload {n}: per-row keys and log-probabilities, every row")
+    first = _gpu_dev(w, lg=lg, want_probs=True, seeds=seeds, want_logprobs=True)
+    tok, cnt, mk = _host(first)
+    rep, _ = compare_every_row(w, tok, cnt, mk, probs_dev=first.probs, logprobs_dev=first.logprobs, seeds=seeds)
     say(f"workload {n} keys + logprobs: {rep.summary()}")
+    assert rep.rows == B
     assert rep.ok(), rep.failures
     # The probabilities and the log-probabilities describe one distribution.
-    ok_rows = ~np.isnan(lps).all(axis=1)  # (row errors are NaN throughout)
-    with np.errstate(over="ignore"):
-        d = np.abs(np.exp(lps[ok_rows].astype(np.float64)) - probs[ok_rows])
-        assert np.all(d <= 1e-6 + 1e-5 * probs[ok_rows])
+    lps, probs = first.logprobs, first.probs
+    ok_rows = ~torch.isnan(lps).all(dim=1)  # (row errors are NaN throughout)
+    d = (torch.exp(lps[ok_rows].double()) - probs[ok_rows].double()).abs()
+    assert bool((d <= 1e-6 + 1e-5 * probs[ok_rows].double()).all())
     # The keys matter: sampled rows draw differently from the call's one seed.
-    base = _gpu(w)
+    base = _host(_gpu_dev(w, lg=lg))
     sampled = (w["temperature"] > 0) & (cnt > 1)
     if sampled.sum() >= 8:
         assert (base[0][sampled] != tok[sampled]).any()
     for path in ("single", "split", "rows"):
         say(f"workload {n}: keys + logprobs on path {path}")
-        other = _gpu(w, want_probs=True, prob_rows=rows, seeds=seeds, want_logprobs=True, path=path)
-        assert all(np.array_equal(np.asarray(x).view(np.uint32), np.asarray(y).view(np.uint32))
-                   for x, y in zip(first, other)), path
+        other = _gpu_dev(w, lg=lg, want_probs=True, seeds=seeds, want_logprobs=True, path=path)
+        for f in ("token", "keep_count", "min_kept_logit", "probs", "logprobs"):
+            assert _same_bits(getattr(first, f), getattr(other, f)), (path, f)

@@ -7,13 +7,16 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_util import device_logits, oracle_and_compare, say
+from gpu_util import compare_every_row, device_logits, oracle_and_compare, say
 from test_gpu_parity import _edge_batch, _random_batch
 
 pytestmark = pytest.mark.gpu
 
 
-def _gpu(w, pc, lg=None, rows=None, single=False, want_logprobs=False):
+def _gpu(w, pc, lg=None, rows=None, single=False, want_logprobs=False, dev=False):
+    """Samples with the pre-chain options; with ``dev`` the result object
+    (its tensors on the device), else host arrays with the probabilities of
+    ``rows``."""
     import torch
 
     import nucleus_sampling_amd as ns
@@ -25,6 +28,8 @@ def _gpu(w, pc, lg=None, rows=None, single=False, want_logprobs=False):
                     frequency_penalty=pc["frequency"], presence_penalty=pc["presence"],
                     allowed_mask=pc["allowed"].view(np.int32))
     torch.cuda.synchronize()
+    if dev:
+        return res
     probs = logprobs = None
     if rows is not None:
         idx = torch.as_tensor(list(rows), dtype=torch.long, device=lg.device)
@@ -44,23 +49,28 @@ def _processed(w, pc):
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_prechain_workload_parity(n):
+    """Every row of every workload, its probabilities and log-probabilities
+    included, against the oracle's sampler run on the oracle's processed
+    logits."""
     say(f"pre-chain, workload {n} ({workloads.NAMES[n]}) shape={workloads.SHAPES[n]}: generating")
-    # The flat workload's first 256 rows (V = 152064) keep the host-side inputs quick.
-    w = workloads.make(n, rows=range(256)) if n == 5 else workloads.make(n)
+    w = workloads.make(n)
     pc = workloads.make_prechain(w, hist_len=1024 if n == 3 else 256, seed=n)
-    rows = [0, 1, 2, 3, 4, 5, 9, w["B"] - 1]
     say(f"pre-chain, workload {n}: sampling on cuda:0")
-    tok, cnt, mk, probs, lp = _gpu(w, pc, rows=rows, want_logprobs=True)
+    lg = device_logits(w["logits"], w["dtype"])
+    res = _gpu(w, pc, lg=lg, rows=(), want_logprobs=True, dev=True)
+    tok, cnt, mk = res.token.cpu().numpy(), res.keep_count.cpu().numpy(), res.min_kept_logit.cpu().numpy()
     wp = _processed(w, pc)
-    rep, _ = oracle_and_compare(wp, tok, cnt, mk, gpu_probs=probs, prob_rows=rows, gpu_logprobs=lp)
+    say(f"pre-chain, workload {n}: every row against the oracle, 128 rows at a time")
+    rep, _ = compare_every_row(wp, tok, cnt, mk, probs_dev=res.probs, logprobs_dev=res.logprobs)
     say(f"pre-chain, workload {n}: {rep.summary()}")
+    assert rep.rows == w["B"]
     assert rep.ok(), rep.failures[:10]
     # Never a forbidden token.
     ok = np.nonzero(tok >= 0)[0]
     words = pc["allowed"][ok, tok[ok] // 32]
     assert (((words >> (tok[ok] % 32).astype(np.uint32)) & 1) == 1).all()
     say(f"pre-chain, workload {n}: one workgroup per row on request gives the same bits")
-    tok2, cnt2, mk2, _, _ = _gpu(w, pc, single=True)
+    tok2, cnt2, mk2, _, _ = _gpu(w, pc, lg=lg, single=True)
     assert np.array_equal(tok, tok2) and np.array_equal(cnt, cnt2)
     assert np.array_equal(mk.view(np.uint32), mk2.view(np.uint32))
 
