@@ -12,7 +12,10 @@ the 256 MB last-level cache cannot serve a repeat read.
 Prints one JSON line: rows/s for the whole job, the dominant kernel's
 achieved HBM bandwidth against the 8 TB/s peak (per-launch HIP events on the
 stream the kernel runs on), the same buffers read by a pure streaming kernel
-for comparison, and the float64 oracle timed on the host's cores over a
+for comparison, the same calls writing the probabilities out, the other
+workloads (small, ties, chain in bf16, flat) timed the same way, the
+rejection sampler, speculative verification and the pre-chain on the
+benchmark batch, and the float64 oracle timed on the host's cores over a
 bounded sample of the same rows.
 """
 from __future__ import annotations
@@ -108,12 +111,30 @@ def pmc_summary(fetch_dir: str, write_dir: str, name: str, shape, dtype: str):
     return out
 
 
-def cpu_baseline(w, seconds: float, threads: int):
+def host_cpus():
+    """What the host offers and what the oracle may use: the machine's CPU share
+    for one GPU is OMP_NUM_THREADS (16 there), whatever os.cpu_count() shows."""
+    logical = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = logical
+    try:
+        import psutil
+        physical = psutil.cpu_count(logical=False)
+    except Exception:
+        physical = None
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(share, affinity) if share > 0 else affinity
+    return {"threads": max(1, threads), "host_logical_cpus": logical, "host_physical_cores": physical,
+            "cpus_in_affinity": affinity, "omp_num_threads": share or None}
+
+
+def _oracle_pass_rate(w, seconds: float, threads: int):
     import oracle
 
     t0 = time.perf_counter()
-    rows = 0
-    passes = 0
+    rows = passes = 0
     while True:
         oracle.sample(w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], seed=w["seed"],
                       threads=threads)
@@ -121,16 +142,102 @@ def cpu_baseline(w, seconds: float, threads: int):
         passes += 1
         if time.perf_counter() - t0 >= seconds:
             break
-    dt = time.perf_counter() - t0
+    return rows / (time.perf_counter() - t0), rows, passes
+
+
+def cpu_baseline(w, seconds: float, cpus):
+    """The oracle on the host: three timed runs of whole passes over the
+    benchmark batch, each at least seconds / 3, on cpus["threads"] threads
+    (one row per task); the median run is the value."""
+    import oracle
+
+    threads = cpus["threads"]
+    runs = [_oracle_pass_rate(w, seconds / 3.0, threads) for _ in range(3)]
+    rates = sorted(r[0] for r in runs)
+    total_rows = sum(r[1] for r in runs)
     # One thread on the first 16 rows, for the single-core figure.
     t1 = time.perf_counter()
     oracle.sample(w["logits"], w["temperature"], w["top_p"], w["top_k"], w["min_p"], seed=w["seed"], rows=range(16),
                   threads=1)
     single = 16 / (time.perf_counter() - t1)
-    return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "single_thread_rows_per_s": single,
-            "sample": f"{passes} pass(es) over the {w['B']} rows of the benchmark batch ({rows} rows, {dt:.1f} s, "
-                      f"float64 stable-sort oracle, {threads} threads, one row per task); single thread: 16 rows"}
+    return {"value": rates[1], "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "runs_rows_per_s": [r[0] for r in runs], "single_thread_rows_per_s": single, **cpus,
+            "sample": f"median of 3 runs, each whole passes over the {w['B']} rows of the benchmark batch for at "
+                      f"least {seconds / 3.0:.1f} s ({total_rows} rows in all); float64 stable-sort oracle on "
+                      f"{threads} threads (the host's CPU share for one GPU), one row per task; single thread: "
+                      f"16 rows"}
+
+
+def _rotating_buffers(w, dev, nbuf: int = 0):
+    """Enough device copies of the batch (> 512 MB in all, or nbuf) that the
+    256 MB last-level cache cannot serve a repeat read."""
+    import numpy as np
+    import torch
+
+    esz = 2 if w["dtype"] == "bf16" else 4
+    batch_bytes = w["B"] * w["V"] * esz
+    nbuf = nbuf or max(2, -(-(512 * 2**20 + 1) // batch_bytes) + 1)
+    if w["dtype"] == "bf16":
+        host = torch.from_numpy(w["logits"].view(np.int16)).view(torch.bfloat16)
+    else:
+        host = torch.from_numpy(w["logits"])
+    return [host.to(dev) for _ in range(nbuf)], batch_bytes
+
+
+def _time_launches(fn, steps: int, warmup: int, stream):
+    """Per-launch milliseconds from HIP events recorded on `stream` around each call."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        st[i].record(stream)
+        fn(warmup + i)
+        en[i].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in zip(st, en)], st[0].elapsed_time(en[-1])
+
+
+def workload_object(n: int, steps: int, warmup: int, dev, stream, cpus, cpu_seconds: float):
+    """One workload timed on the library's default path: rows/s, the logits'
+    HBM GB/s and fraction of the 8 TB/s peak, per-launch times, and the oracle's
+    rows/s over a bounded sample of the same rows."""
+    import numpy as np
+    import torch
+
+    import nucleus_sampling_amd as ns
+    import workloads
+
+    w = workloads.make(n)
+    B, V = w["B"], w["V"]
+    bufs, batch_bytes = _rotating_buffers(w, dev)
+    T, P, K, MP = (torch.from_numpy(w[k]).to(dev) for k in ("temperature", "top_p", "top_k", "min_p"))
+    out = ns.SampleResult(torch.empty(B, dtype=torch.int32, device=dev),
+                          torch.empty(B, dtype=torch.int32, device=dev), None, None)
+    need = ns.workspace_bytes(B, V, bufs[0].dtype)
+    ws = ns.workspace_for(dev, stream, need) if need else None
+
+    def step(i):
+        ns.sample(bufs[i % len(bufs)], T, P, K, MP, seed=w["seed"], step=i, out=out, workspace=ws, stream=stream)
+
+    ms, span = _time_launches(step, steps, warmup, stream)
+    avg = float(np.mean(ms))
+    gbps = batch_bytes / (avg * 1e-3) / 1e9
+    res = {"workload": f"{w['name']}: B={B}, V={V} {w['dtype']}", "B": B, "V": V, "logit_dtype": w["dtype"],
+           "kernel": "row_kernel" if B >= 128 else "tile_kernel", "steps": steps,
+           "avg_launch_ms": avg, "median_launch_ms": float(np.median(ms)),
+           "rows_per_s": B / (avg * 1e-3), "rows_per_s_span": B * steps / (span * 1e-3),
+           "algorithmic_bytes_per_launch": batch_bytes, "logits_gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS}
+    if cpu_seconds > 0:
+        rate, rows, _ = _oracle_pass_rate(w, cpu_seconds, cpus["threads"])
+        res["cpu_oracle_rows_per_s"] = rate
+        res["cpu_oracle_sample"] = f"{rows} rows, {cpus['threads']} threads"
+    del bufs
+    torch.cuda.synchronize()
+    return res
 
 
 def main():
@@ -146,7 +253,10 @@ def main():
     ap.add_argument("--no-rejection", action="store_true", help="skip timing the rejection sampler")
     ap.add_argument("--no-spec", action="store_true", help="skip timing speculative verification")
     ap.add_argument("--no-prechain", action="store_true", help="skip timing the pre-chain")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="host seconds for the oracle baseline (three runs of a third each)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip timing the other workloads (small, ties, chain, flat)")
     ap.add_argument("--profile-steps", action="store_true", help="only run the timed loop (for rocprofv3)")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="before the timed loop, run a plain elementwise kernel that reads and writes 256 MiB "
@@ -177,14 +287,9 @@ def main():
     dev = torch.device("cuda:0")
     w = workloads.make(args.workload)
     B, V = w["B"], w["V"]
-    esz = 2 if w["dtype"] == "bf16" else 4
-    batch_bytes = B * V * esz
-    nbuf = args.buffers or max(2, -(-(512 * 2**20 + 1) // batch_bytes) + 1)
-    if w["dtype"] == "bf16":
-        host = torch.from_numpy(w["logits"].view(np.int16)).view(torch.bfloat16)
-    else:
-        host = torch.from_numpy(w["logits"])
-    bufs = [host.to(dev) for _ in range(nbuf)]
+    bufs, batch_bytes = _rotating_buffers(w, dev, args.buffers)
+    nbuf = len(bufs)
+    host = bufs[0]
     T = torch.from_numpy(w["temperature"]).to(dev)
     P = torch.from_numpy(w["top_p"]).to(dev)
     K = torch.from_numpy(w["top_k"]).to(dev)
@@ -341,6 +446,41 @@ def main():
                  "frac_of_hbm_peak": batch_bytes / (pc_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                  "note": "history 256 tokens per row, repetition/frequency/presence penalties, mask ~20% forbidden"}
 
+    # The same calls with the renormalised distribution written out
+    # (out_probs, B x V fp32): the logits read once plus the probabilities
+    # written once.
+    with_probs = None
+    if args.path == "default":
+        pout = ns.SampleResult(torch.empty(B, dtype=torch.int32, device=dev),
+                               torch.empty(B, dtype=torch.int32, device=dev),
+                               torch.empty((B, V), dtype=torch.float32, device=dev), None)
+
+        def prstep(i):
+            ns.sample(bufs[i % nbuf], T, P, K, MP, seed=w["seed"], step=i, out=pout, workspace=ws, stream=stream,
+                      want_probs=True)
+
+        pr_ms, _ = _time_launches(prstep, args.steps, args.warmup, stream)
+        pr_avg = float(np.mean(pr_ms))
+        pr_bytes = batch_bytes + B * V * 4
+        with_probs = {"kernels": "row_kernel (probabilities written by the resolving workgroup)"
+                      if B >= 128 else "tile_kernel", "avg_launch_ms": pr_avg,
+                      "median_launch_ms": float(np.median(pr_ms)), "rows_per_s": B / (pr_avg * 1e-3),
+                      "algorithmic_bytes_per_launch": pr_bytes,
+                      "achieved_gbps": pr_bytes / (pr_avg * 1e-3) / 1e9,
+                      "frac_of_hbm_peak": pr_bytes / (pr_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                      "note": "logits read once (4 B per token) + out_probs written once (4 B per token)"}
+        del pout
+
+    cpus = host_cpus()
+    others = None
+    if not args.no_workloads:
+        others = {}
+        for n in (1, 2, 4, 5):
+            if n == args.workload:
+                continue
+            others[workloads.NAMES[n]] = workload_object(n, args.steps, args.warmup, dev, stream, cpus,
+                                                         0.0 if args.no_cpu_baseline else 2.0)
+
     avg_ms = float(np.mean(per_launch_ms))
     med_ms = float(np.median(per_launch_ms))
     achieved = batch_bytes / (avg_ms * 1e-3) / 1e9
@@ -373,17 +513,21 @@ def main():
                      "median_launch_ms": med_ms, "p10_launch_ms": float(np.percentile(per_launch_ms, 10)),
                      "p90_launch_ms": float(np.percentile(per_launch_ms, 90)),
                      "algorithmic_bytes_per_launch": batch_bytes},
-        "stream_read": {"gbps": stream_gbps, "avg_ms": read_ms, "frac_of_peak": stream_gbps / PEAK_HBM_GBPS,
-                        "sampler_vs_stream": achieved / stream_gbps},
+        "stream_read": {"kernel": "stream_read_kernel", "gbps": stream_gbps, "avg_ms": read_ms,
+                        "frac_of_peak": stream_gbps / PEAK_HBM_GBPS, "sampler_vs_stream": achieved / stream_gbps},
+        "with_probs": with_probs,
+        "workloads": others,
         "rejection": rej,
         "speculative": spec,
         "prechain": prech,
         "wall_s": wall,
         "kernel_hash": kernel_hash(),
     }
+    if others:
+        for o in others.values():
+            o["frac_of_stream_read"] = o["logits_gbps"] / stream_gbps
     if not args.no_cpu_baseline:
-        threads = min(16, os.cpu_count() or 1)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, threads)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, cpus)
     print(json.dumps(res), flush=True)
 
 

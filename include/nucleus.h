@@ -306,12 +306,29 @@ int nucleus_version(void);
 /*
  * Read `bytes` bytes of device memory at `buf` once with 16-byte loads and
  * fold them into device `sink`, an array of 256 uint64 words (XOR-updated,
- * not cleared).  This is the HBM read ceiling the sampler's achieved
+ * not cleared): the XOR of the 256 words changes by the XOR of the buffer's
+ * little-endian 32-bit words, each of the last bytes % 16 bytes XORed in as
+ * a value 0..255.  This is the HBM read ceiling the sampler's achieved
  * bandwidth is compared with.  `buf` must be 16-byte aligned.  Asynchronous
  * on `stream` (a hipStream_t, NULL = null stream).  Returns NUCLEUS_OK or a
  * negative code.
  */
 int nucleus_stream_read(const void* buf, size_t bytes, uint64_t* sink, void* stream);
+
+/*
+ * Phase clocks, for profiling the one-workgroup-per-row path.  Only a library
+ * built with NUCLEUS_PHASE_STAMPS (libnucleus_stamps.so) records them; the
+ * product build returns NUCLEUS_EINVAL and records nothing.  After this call,
+ * every nucleus_sample call with B <= rows that runs one workgroup per row
+ * writes, for row b, the device's 100 MHz constant-rate clock at eight phase
+ * boundaries to buf[8 b + k]: k = 0 start, 1 first pass (max, error flag,
+ * fused histogram), 2 bins ready, 3 bin decision, 4 classification, 5 race
+ * pass, 6 resolver and outputs, 7 probability pass (or its skip).  A phase a
+ * row does not run leaves its word as it was.  buf: device, [rows, 8]
+ * uint64, 8-byte aligned, owned by the caller and valid for every later
+ * call; NULL turns the recording off.  Calls that overlap race on buf.
+ */
+int nucleus_phase_stamps(uint64_t* buf, int64_t rows);
 
 #ifdef __cplusplus
 }

@@ -88,6 +88,8 @@ def lib():
         L.nucleus_version.restype = ctypes.c_int
         L.nucleus_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
         L.nucleus_stream_read.restype = ctypes.c_int
+        L.nucleus_phase_stamps.argtypes = [vp, i64]
+        L.nucleus_phase_stamps.restype = ctypes.c_int
         _lib = L
     return _lib
 

@@ -181,14 +181,101 @@ __device__ __forceinline__ uint64_t uniform(uint64_t v)
 __device__ __forceinline__ double uniform(double v) { return __longlong_as_double((long long)uniform((uint64_t)__double_as_longlong(v))); }
 
 // ---------------------------------------------------------------------------
-// Wave and workgroup reductions (wave64 shuffles; LDS across waves).
+// Wave and workgroup reductions and scans.  Inside a wave they move data
+// with DPP (a lane reads another lane of its 16-lane row as an operand
+// modifier of an ordinary VALU instruction: a few cycles, no LDS round trip)
+// and read the four rows' results with v_readlane; across waves through LDS.
+// Every lane of the wave must be active.
 // ---------------------------------------------------------------------------
+constexpr int kDppQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowRor4 = 0x124;   // row_ror:4: lane (l - 4) mod 16 of the row
+constexpr int kDppRowRor8 = 0x128;   // row_ror:8
+constexpr int kDppRowShr1 = 0x111;   // row_shr:n: lane l - n of the row, 0 below the row's start
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// v of the lane CTRL names (0 bits where it names none), for 4- and 8-byte T.
+template <int CTRL, class T>
+__device__ __forceinline__ T dpp(T v)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "dpp moves 4- and 8-byte values");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const uint64_t r = ((uint64_t)dpp_u32<CTRL>((uint32_t)(u >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)u);
+        return __builtin_bit_cast(T, r);
+    }
+}
+
+template <class T>
+__device__ __forceinline__ T lane_value(T v, int lane)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- and 8-byte values");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, (uint32_t)__builtin_amdgcn_readlane((int)__builtin_bit_cast(uint32_t, v), lane));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+        return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+    }
+}
+
+// f over the 64 lanes (f associative and commutative); every lane receives
+// the result, combined in one fixed order.
 template <class T, class F>
 __device__ __forceinline__ T wave_reduce(T v, F f)
 {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = f(v, __shfl_xor(v, o, kWave));
+    v = f(v, dpp<kDppQuadSwap1>(v));
+    v = f(v, dpp<kDppQuadSwap2>(v));  // every lane: its quad
+    v = f(v, dpp<kDppRowRor4>(v));    // its quad and the one before
+    v = f(v, dpp<kDppRowRor8>(v));    // its row
+    return f(f(lane_value(v, 0), lane_value(v, 16)), f(lane_value(v, 32), lane_value(v, 48)));
+}
+
+// Inclusive prefix sum over the 64 lanes, in one fixed order: within each
+// 16-lane row by doubling steps, then each row adds the rows before it
+// ((r0 + r1) + r2 for the last).  Sets `total` to lane 63's value.
+template <class T>
+__device__ __forceinline__ T wave_inclusive_sum(T v, T& total)
+{
+    v = v + dpp<kDppRowShr1>(v);
+    v = v + dpp<kDppRowShr2>(v);
+    v = v + dpp<kDppRowShr4>(v);
+    v = v + dpp<kDppRowShr8>(v);
+    const T r0 = lane_value(v, 15), r1 = lane_value(v, 31), r2 = lane_value(v, 47);
+    const T r01 = r0 + r1, r012 = r01 + r2;
+    const int row = (int)(threadIdx.x & (kWave - 1)) >> 4;
+    if (row == 1) v = v + r0;
+    if (row == 2) v = v + r01;
+    if (row == 3) v = v + r012;
+    total = lane_value(v, kWave - 1);
     return v;
+}
+
+// The inclusive value of the lane before (T(0) for lane 0), given the
+// inclusive sums `inc` from wave_inclusive_sum.  Moved as an unsigned bit
+// pattern: with the selects written on doubles, the build gave lane 48 the
+// wrong value (twice lane 47's), while the same steps on uint64 are exact.
+template <class T>
+__device__ __forceinline__ T wave_shift_up1(T inc)
+{
+    using U = std::conditional_t<sizeof(T) == 4, uint32_t, uint64_t>;
+    const U u = __builtin_bit_cast(U, inc);
+    const U prev = dpp<kDppRowShr1>(u);
+    const U r15 = lane_value(u, 15), r31 = lane_value(u, 31), r47 = lane_value(u, 47);
+    const int l = (int)(threadIdx.x & (kWave - 1));
+    const U r = l == 16 ? r15 : (l == 32 ? r31 : (l == 48 ? r47 : prev));
+    return __builtin_bit_cast(T, r);
 }
 
 // All threads receive the result.  `scratch` holds one T per wave.
@@ -214,12 +301,8 @@ __device__ __forceinline__ uint64_t block_exclusive_sum(uint64_t v, uint64_t* sc
 {
     constexpr int W = BLOCK / kWave;
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-    uint64_t x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint64_t y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
+    uint64_t wt;
+    const uint64_t x = wave_inclusive_sum(v, wt);
     __syncthreads();
     if (lane == kWave - 1) scratch[w] = x;
     __syncthreads();

@@ -256,9 +256,9 @@ __device__ __forceinline__ double lane_read_f64(double v, int lane)
 // Deterministic whatever the block size: the weight of bin j is
 // exp(-j w) * H[j] * 2^-31, a pure function of j and H[j]; then the first
 // wave alone sums them in one fixed order: lane l adds its 16 bins
-// 16l .. 16l + 15 one by one from 0.0, a fixed six-step wave scan adds the
-// lane totals, and bin j's running weight is (the lanes before l) + (its
-// lane's running value).  Counts are integers, exact in any order.  The
+// 16l .. 16l + 15 one by one from 0.0, a fixed wave scan (wave_inclusive_sum)
+// adds the lane totals, and bin j's running weight is (the lanes before l) +
+// (its lane's running value).  Counts are integers, exact in any order.  The
 // top-p search only stops on non-empty bins, so the cut never lands on an
 // empty one whatever the rounding.
 __device__ __forceinline__ Decision decide(const RowModel& r, uint64_t* H, uint32_t* C, int k, float p)
@@ -281,28 +281,15 @@ __device__ __forceinline__ Decision decide(const RowModel& r, uint64_t* H, uint3
             run += W[PER * lane + i];
             crun += C ? C[PER * lane + i] : 0u;
         }
-        // Inclusive wave scans of the lane totals, then the exclusive parts.
-        double inc = run;
-        uint64_t cinc = crun;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const double y = __shfl_up(inc, o, kWave);
-            const uint64_t cy = __shfl_up(cinc, o, kWave);
-            if (lane >= o) {
-                inc += y;
-                cinc += cy;
-            }
-        }
-        double before = __shfl_up(inc, 1, kWave);
-        uint64_t cbefore = __shfl_up(cinc, 1, kWave);
-        if (lane == 0) {
-            before = 0.0;
-            cbefore = 0;
-        }
-        const double S = lane_read_f64(inc, kWave - 1);
-        const uint64_t total = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cinc >> 32), kWave - 1)
-                                << 32) |
-                               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cinc, kWave - 1);
+        // Inclusive wave scans of the lane totals (a fixed order: doubling
+        // steps in each 16-lane row, then the rows before), and the
+        // inclusive value of the lane before.
+        double S;
+        uint64_t total;
+        const double inc = wave_inclusive_sum(run, S);
+        const uint64_t cinc = wave_inclusive_sum((uint64_t)crun, total);
+        const double before = wave_shift_up1(inc);
+        const uint64_t cbefore = wave_shift_up1(cinc);
         Decision d;
         d.mode = kModeP;
         d.cbin = 0;

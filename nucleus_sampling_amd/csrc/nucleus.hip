@@ -147,11 +147,41 @@ void* static_scratch()
     return known[dev];
 }
 
+// Phase clocks (builds with NUCLEUS_PHASE_STAMPS only): the buffer later
+// calls of the one-workgroup-per-row path write to.
+std::atomic<uint64_t*> g_stamps{nullptr};
+std::atomic<int64_t> g_stamp_rows{0};
+
+uint64_t* stamps_for(int64_t B)
+{
+#ifdef NUCLEUS_PHASE_STAMPS
+    uint64_t* s = g_stamps.load();
+    return (s && B <= g_stamp_rows.load()) ? s : nullptr;
+#else
+    (void)B;
+    return nullptr;
+#endif
+}
+
 }  // namespace
 
 extern "C" {
 
 int nucleus_version(void) { return 260; }
+
+int nucleus_phase_stamps(uint64_t* buf, int64_t rows)
+{
+#ifdef NUCLEUS_PHASE_STAMPS
+    if (rows < 0 || (buf && (uintptr_t)buf % 8)) return NUCLEUS_EINVAL;
+    g_stamp_rows.store(buf ? rows : 0);
+    g_stamps.store(buf);
+    return NUCLEUS_OK;
+#else
+    (void)buf;
+    (void)rows;
+    return NUCLEUS_EINVAL;
+#endif
+}
 
 const char* nucleus_strerror(int code)
 {
@@ -239,6 +269,7 @@ int nucleus_sample(const void* logits, int64_t B, int64_t V, const float* temper
     p.freq_pen = pre ? opt->frequency_penalty : nullptr;
     p.pres_pen = pre ? opt->presence_penalty : nullptr;
     p.allowed = pre ? opt->allowed_mask : nullptr;
+    p.stamps = stamps_for(B);
     const size_t vec_bytes = dtype == NUCLEUS_F32 ? 16 : 8;
     p.vec_in = ((uintptr_t)logits % vec_bytes == 0) && ((size_t)stride * esz) % vec_bytes == 0;
 

@@ -30,6 +30,31 @@ struct Params {
     const float* freq_pen;    // [B] or null (0)
     const float* pres_pen;    // [B] or null (0)
     const uint32_t* allowed;  // [B, ceil(V/32)] bit masks, or null (all allowed)
+    uint64_t* stamps;         // [B, kStamps] phase clocks (builds with NUCLEUS_PHASE_STAMPS), or null
 };
+
+// Phase clocks of the one-workgroup-per-row kernel, compiled in only with
+// NUCLEUS_PHASE_STAMPS: thread 0 of row b's workgroup writes the 100 MHz
+// constant-rate clock at each phase boundary to stamps[b * kStamps + k].
+constexpr int kStamps = 8;
+enum StampPoint {
+    kStampStart = 0,     // the workgroup starts
+    kStampPass1 = 1,     // pass 1 (max, error flag, fused histogram) done
+    kStampHist = 2,      // the row's bins are ready (window folded, or pass 2 done)
+    kStampDecide = 3,    // decide done
+    kStampClassify = 4,  // classify done
+    kStampPass3 = 5,     // pass 3 (race of the surely kept tokens, candidates) done
+    kStampResolve = 6,   // resolver done, outputs written
+    kStampProbs = 7,     // probability pass done (or skipped)
+};
+
+#ifdef NUCLEUS_PHASE_STAMPS
+__device__ __forceinline__ void phase_stamp(const Params& p, int64_t b, int k)
+{
+    if (p.stamps && threadIdx.x == 0) p.stamps[b * kStamps + k] = wall_clock64();
+}
+#else
+__device__ __forceinline__ void phase_stamp(const Params&, int64_t, int) {}
+#endif
 
 }  // namespace nucleus

@@ -490,6 +490,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     const int64_t esz = DT == kF32 ? 4 : 2;
     const void* rowp = (const char*)p.logits + b * p.stride * esz;
     use_row_key(p, b);
+    phase_stamp(p, b, kStampStart);
     const bool want_probs = wants_dist(p);  // probabilities or log-probabilities
     // The pre-chain (penalties, grammar mask) is applied to every buffer of
     // every pass as it arrives.
@@ -561,6 +562,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             win = m1 > -INFINITY && fabs(base) < 0x1p50;
         }, xf);
     block_extremes<kRowThreads>(lmax, bad, sh.redf, sh.redi);
+    phase_stamp(p, b, kStampPass1);
     RowState st;
     st.mode = uniform(first_mode(bad != 0, lmax, rp.T, rp.P, rp.MP, rp.K, want_probs));
     st.m = uniform(lmax);
@@ -630,7 +632,9 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             }
         }
         __syncthreads();
+        phase_stamp(p, b, kStampHist);
         const Decision d = decide(model, H, counts ? C : nullptr, rp.K, rp.P);
+        phase_stamp(p, b, kStampDecide);
         st.mode = uniform(d.mode);
         st.cbin = uniform(d.cbin);
         st.tc = uniform(d.tc);
@@ -640,6 +644,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
 
     const Classes cl = classify(model, st);
     const float keep_lo = cl.keep_lo, cand_lo = cl.cand_lo;
+    phase_stamp(p, b, kStampClassify);
     if (PUBLISH) {
         if (t == 0) publish_row(rw.st + b, st, model, keep_lo, cand_lo);
         return;
@@ -682,6 +687,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     if (qn) wq_drain(rq, qh, qn, lane, qn, race);
     if (lane == 0) sh.wcand[t / kWave] = wn;
     acc = block_race<kRowThreads>(acc, sh.rs);  // (its barriers publish wcand)
+    phase_stamp(p, b, kStampPass3);
     uint32_t most = 0, n = 0;
 #pragma unroll
     for (int w = 0; w < kRowThreads / kWave; ++w) {
@@ -723,7 +729,11 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
                                  sh.rs);
     }
     write_outputs(p, b, st);
-    if (!want_probs) return;
+    phase_stamp(p, b, kStampResolve);
+    if (!want_probs) {
+        phase_stamp(p, b, kStampProbs);
+        return;
+    }
 
     // ---- pass 4: renormalised probabilities and / or log-probabilities
     if (p.out_probs && st.mode != kModeError && st.mode != kModeGreedy)
@@ -745,6 +755,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             store_probs(lrow, i0, V, q);
         }
     }, nofirst, xf);
+    phase_stamp(p, b, kStampProbs);
 }
 
 // The chunk a race_kernel / probs_kernel workgroup covers.  Dispatch is

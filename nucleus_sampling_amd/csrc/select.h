@@ -83,16 +83,13 @@ __device__ __forceinline__ SelectResult select_level(Visit visit, ThrFn thr_of_t
 #pragma unroll
             for (int i = 0; i < 4; ++i) h[i] = sh.hist[kDigitBins - 1 - (4 * t + i)];
             const uint64_t ls = h[0] + h[1] + h[2] + h[3];
+            // Inclusive prefix of the lane sums; minus the lane's own sum, the
+            // weight of the digits above this lane's.
+            uint64_t all;
+            const uint64_t x = wave_inclusive_sum(ls, all);
             if (lvl == first) {
-                total = wave_reduce(ls, SumU64());
+                total = all;
                 thr = thr_of_total(total);
-            }
-            // Exclusive prefix of the lane sums: weight of the digits above this lane's.
-            uint64_t x = ls;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint64_t y = __shfl_up(x, o, kWave);
-                if (t >= o) x += y;
             }
             uint64_t bf = base + x - ls;
             // Lowest non-empty digit whose weight above is < thr (largest rank);

@@ -213,3 +213,10 @@ def test_noalloc_host_side_checks(L):
     opt.flags = 3  # two flags
     assert _call_na(L, opt=ctypes.byref(opt)) == -1
     assert _call_na(L, B=0) in (0, -4)  # no batch: nothing to launch (or no usable device here)
+
+
+def test_phase_stamps_are_off_in_the_product_build(L):
+    """The product library has no phase clocks compiled in: registering a
+    buffer is refused and nothing is recorded."""
+    assert L.nucleus_phase_stamps(1 << 20, 4) == -1
+    assert L.nucleus_phase_stamps(None, 0) == -1
