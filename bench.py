@@ -227,7 +227,7 @@ def workload_object(n: int, steps: int, warmup: int, dev, stream, cpus, cpu_seco
     avg = float(np.mean(ms))
     gbps = batch_bytes / (avg * 1e-3) / 1e9
     res = {"workload": f"{w['name']}: B={B}, V={V} {w['dtype']}", "B": B, "V": V, "logit_dtype": w["dtype"],
-           "kernel": "row_kernel" if B >= 128 else "tile_kernel", "steps": steps,
+           "kernel": "tile_kernel" if need else "row_kernel", "steps": steps,
            "avg_launch_ms": avg, "median_launch_ms": float(np.median(ms)),
            "rows_per_s": B / (avg * 1e-3), "rows_per_s_span": B * steps / (span * 1e-3),
            "algorithmic_bytes_per_launch": batch_bytes, "logits_gbps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS}
@@ -301,7 +301,7 @@ def main():
              "rows": ns.NUCLEUS_FLAG_ROW_RACE}[args.path]
     need = ns.workspace_bytes(B, V, host.dtype, flags)
     ws = ns.workspace_for(dev, stream, need) if need else None
-    kernel = {"default": "row_kernel" if B >= 128 else "tile_kernel", "single": "row_kernel",
+    kernel = {"default": "tile_kernel" if ns.workspace_bytes(B, V, host.dtype) else "row_kernel", "single": "row_kernel",
               "split": "tile_kernel", "rows": "row_kernel+race_kernel"}[args.path]
 
     def step(i):
@@ -462,8 +462,7 @@ def main():
         pr_ms, _ = _time_launches(prstep, args.steps, args.warmup, stream)
         pr_avg = float(np.mean(pr_ms))
         pr_bytes = batch_bytes + B * V * 4
-        with_probs = {"kernels": "row_kernel (probabilities written by the resolving workgroup)"
-                      if B >= 128 else "tile_kernel", "avg_launch_ms": pr_avg,
+        with_probs = {"kernels": kernel + " (probabilities written in the same launch)", "avg_launch_ms": pr_avg,
                       "median_launch_ms": float(np.median(pr_ms)), "rows_per_s": B / (pr_avg * 1e-3),
                       "algorithmic_bytes_per_launch": pr_bytes,
                       "achieved_gbps": pr_bytes / (pr_avg * 1e-3) / 1e9,

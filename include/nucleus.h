@@ -69,12 +69,15 @@ extern "C" {
 /* Option flags. */
 #define NUCLEUS_FLAG_SINGLE_WORKGROUP 1 /* run every row, every phase, on one workgroup that
                                            streams the row from memory once per phase (the path
-                                           batches of 128 rows or more take by default); no
+                                           every batch takes by default but small batches of
+                                           long rows, below); no
                                            workspace needed.  Same results, bit for bit.  For
                                            verification and for callers that cannot provide a
                                            workspace. */
 #define NUCLEUS_FLAG_SPLIT_ROWS 2       /* split every row over register-resident workgroups
-                                           (the path batches under 128 rows take by default)
+                                           (the path taken by default by batches of B < 128
+                                           rows of V > 32768 tokens with B * ceil(V / 8192)
+                                           <= 1536)
                                            whatever the batch size; rows longer than 64 * 8192
                                            tokens are then NUCLEUS_EINVAL.  Same results, bit
                                            for bit.  For verification. */
@@ -286,10 +289,11 @@ int nucleus_spec_verify(const float* target_probs, const float* draft_probs, con
 size_t nucleus_spec_workspace_bytes(int64_t B, int64_t V);
 
 /* Device workspace, in bytes, that nucleus_sample needs for a batch of this
- * shape and dtype with no flags: batches under 128 rows of at most
- * 64 * 8192 tokens need the split-row path's (per row: a 128-byte control
- * block, 12.3 KB per 8192-token chunk and a 64 KB candidate list); other
- * batches need none.  Returns 0 for B == 0 and for invalid shapes. */
+ * shape and dtype with no flags: batches that split their rows by default
+ * (B < 128, 32768 < V <= 64 * 8192, B * ceil(V / 8192) <= 1536) need the
+ * split-row path's (per row: a 128-byte control block, 12.3 KB per
+ * 8192-token chunk and a 64 KB candidate list); other batches need none.
+ * Returns 0 for B == 0 and for invalid shapes. */
 size_t nucleus_workspace_bytes(int64_t B, int64_t V, int32_t dtype);
 
 /* The same for a call with the given option flags (0 for
@@ -321,12 +325,14 @@ int nucleus_stream_read(const void* buf, size_t bytes, uint64_t* sink, void* str
  * product build returns NUCLEUS_EINVAL and records nothing.  After this call,
  * every nucleus_sample call with B <= rows that runs one workgroup per row
  * writes, for row b, the device's 100 MHz constant-rate clock at eight phase
- * boundaries to buf[8 b + k]: k = 0 start, 1 first pass (max, error flag,
+ * boundaries to buf[16 b + k]: k = 0 start, 1 first pass (max, error flag,
  * fused histogram), 2 bins ready, 3 bin decision, 4 classification, 5 race
- * pass, 6 resolver and outputs, 7 probability pass (or its skip).  A phase a
- * row does not run leaves its word as it was.  buf: device, [rows, 8]
- * uint64, 8-byte aligned, owned by the caller and valid for every later
- * call; NULL turns the recording off.  Calls that overlap race on buf.
+ * pass, 6 resolver and outputs, 7 probability pass (or its skip); and facts
+ * about the row: buf[16 b + 8] its mode after the bin decision, + 9 the
+ * crossing-bin candidates the race pass found, + 10 the most any wave found.
+ * A phase a row does not run leaves its word as it was.  buf: device,
+ * [rows, 16] uint64, 8-byte aligned, owned by the caller and valid for every
+ * later call; NULL turns the recording off.  Calls that overlap race on buf.
  */
 int nucleus_phase_stamps(uint64_t* buf, int64_t rows);
 

@@ -40,12 +40,19 @@ int check_device()
     return known[dev] == 1 ? NUCLEUS_OK : NUCLEUS_EDEVICE;
 }
 
-// Batches with at least this many rows give each row a CU of its own
-// (row_kernel, every phase in one workgroup).  Smaller batches split each row
-// over ceil(V / kChunk) register-resident workgroups (tile_kernel).  The
+// By default a row runs on one workgroup of its own (row_kernel, every
+// phase).  Small batches of long rows split each row over ceil(V / kChunk)
+// register-resident workgroups instead (tile_kernel): fewer than 128 rows of
+// more than 32768 tokens, and at most 1536 workgroups in all.  Measured on
+// MI355X (Normal logits, T = 1): with rows of 8192 or 32000 tokens one
+// workgroup per row is as fast or faster at every batch size; with 128256
+// tokens splitting wins up to ~64-96 rows (45 against 67 us at B = 1, 62
+// against 80 us at B = 64) and loses at 127 (108 against 84 us).  The
 // chunked-race path (row_kernel's histogram passes, then race_kernel spread
 // over the device) is taken on request.
 constexpr int64_t kSplitBelowRows = 128;
+constexpr int64_t kSplitAboveTokens = 32768;
+constexpr int64_t kSplitMaxWorkgroups = 1536;
 
 enum Path { kPathTile, kPathRows, kPathFused };
 
@@ -64,7 +71,9 @@ int choose_path(int64_t B, int64_t V, int32_t flags)
     if (flags & NUCLEUS_FLAG_SINGLE_WORKGROUP) return kPathFused;
     if (flags & NUCLEUS_FLAG_ROW_RACE) return kPathRows;
     if (flags & NUCLEUS_FLAG_SPLIT_ROWS) return tile_chunks(V) ? kPathTile : -1;
-    return (B < kSplitBelowRows && tile_chunks(V)) ? kPathTile : kPathFused;
+    const int64_t K = tile_chunks(V);
+    return (B < kSplitBelowRows && V > kSplitAboveTokens && K && B * K <= kSplitMaxWorkgroups) ? kPathTile
+                                                                                               : kPathFused;
 }
 
 size_t path_workspace(int path, int64_t B, int64_t V)

@@ -35,8 +35,9 @@ struct Params {
 
 // Phase clocks of the one-workgroup-per-row kernel, compiled in only with
 // NUCLEUS_PHASE_STAMPS: thread 0 of row b's workgroup writes the 100 MHz
-// constant-rate clock at each phase boundary to stamps[b * kStamps + k].
-constexpr int kStamps = 8;
+// constant-rate clock at each phase boundary to stamps[b * kStamps + k]
+// (k < 8), and a few facts about the row after them.
+constexpr int kStamps = 16;
 enum StampPoint {
     kStampStart = 0,     // the workgroup starts
     kStampPass1 = 1,     // pass 1 (max, error flag, fused histogram) done
@@ -46,6 +47,9 @@ enum StampPoint {
     kStampPass3 = 5,     // pass 3 (race of the surely kept tokens, candidates) done
     kStampResolve = 6,   // resolver done, outputs written
     kStampProbs = 7,     // probability pass done (or skipped)
+    kStampMode = 8,      // (facts) the row's mode after decide
+    kStampCands = 9,     // crossing-bin candidates found in pass 3
+    kStampMostWave = 10, // the most any wave found
 };
 
 #ifdef NUCLEUS_PHASE_STAMPS
@@ -53,8 +57,13 @@ __device__ __forceinline__ void phase_stamp(const Params& p, int64_t b, int k)
 {
     if (p.stamps && threadIdx.x == 0) p.stamps[b * kStamps + k] = wall_clock64();
 }
+__device__ __forceinline__ void phase_fact(const Params& p, int64_t b, int k, uint64_t v)
+{
+    if (p.stamps && threadIdx.x == 0) p.stamps[b * kStamps + k] = v;
+}
 #else
 __device__ __forceinline__ void phase_stamp(const Params&, int64_t, int) {}
+__device__ __forceinline__ void phase_fact(const Params&, int64_t, int, uint64_t) {}
 #endif
 
 }  // namespace nucleus

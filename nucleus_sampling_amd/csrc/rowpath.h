@@ -38,8 +38,11 @@ namespace nucleus {
 
 constexpr int kRowThreads = 1024;  // 16 waves: one workgroup per CU
 constexpr int kRowUnroll = 8;      // 4-token groups per thread whose loads are in flight together
-constexpr int kRowCand = 6144;     // crossing-bin candidates held in LDS
-constexpr int kWaveCand = kRowCand / (kRowThreads / kWave);  // each wave's segment of them
+// Crossing-bin candidates held in LDS during the race pass, in one segment
+// per wave: 9728 (608 a wave) in the plain kernel, 6144 (384 a wave) beside
+// the pre-chain's LDS tables.
+constexpr int kRowCand = 9728;
+constexpr int kRowCandPre = 6144;
 constexpr int kWin = 4096;         // cells of the fused pass's LDS histogram window
 constexpr int kWinHead = kWin - kBins;  // cells the window reaches above the provisional max
 constexpr int kRaceQueue = 256;    // per-wave ring of 4-token groups waiting for the race
@@ -247,7 +250,7 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
 // LDS list (CAP entries); n, the same in every lane, counts the
 // wave's appends, those past the segment (dropped) included.  No atomics:
 // positions come from the lanes' ranks.
-template <uint32_t CAP = kWaveCand>
+template <uint32_t CAP>
 __device__ __forceinline__ void wave_append(u32x2v* seg, uint32_t& n, bool pred, uint32_t key, uint32_t idx)
 {
     const uint64_t mask = __ballot(pred);
@@ -392,14 +395,17 @@ __device__ __forceinline__ void stage_flush(u32x2v* stage, uint32_t& sn, uint32_
     sn = 0;
 }
 
-struct RowShared {
+template <int CANDS>
+struct RowSharedT {
+    static constexpr int kCands = CANDS;                          // candidates in the race pass
+    static constexpr int kWaveCands = CANDS / (kRowThreads / kWave);  // each wave's segment of them
     union {
         struct {  // histogram: a window of lattice cells (bins from decide on)
             uint64_t hm[kWin + kRowThreads];  // the window, then one slot per thread
             uint32_t hc[kWin + kRowThreads];
         } h;
         struct {  // race pass
-            u32x2v cand[kRowCand];
+            u32x2v cand[CANDS];
             RaceQueue rq[kRowThreads / kWave];
         } r;
         float factor[kBins];  // probability pass
@@ -410,11 +416,43 @@ struct RowShared {
     uint32_t wcand[kMaxWaves];  // candidates each wave found (past its segment too)
     uint32_t wpre[kMaxWaves];   // candidates of the waves before
     uint32_t sstar_bits;  // best exact race score found so far in the workgroup (bits of a float >= 0)
+    uint32_t gather_n;    // candidates gathered by the second look at the row
+    // After the race pass the whole race-pass area holds one candidate list.
+    static constexpr int kGatherCands = (int)(sizeof(decltype(u.r)) / sizeof(u32x2v));
 };
 
-struct RowSharedPre : RowShared {
+using RowShared = RowSharedT<kRowCand>;
+
+struct RowSharedPre : RowSharedT<kRowCandPre> {
     PreShared pre;
 };
+
+static_assert(sizeof(RowShared) <= 160 * 1024 && sizeof(RowSharedPre) <= 160 * 1024, "LDS of one workgroup");
+
+// wave_append into a list shared by the workgroup: one LDS atomic per wave
+// step reserves the places of the lanes with pred set.  Entries past cap are
+// dropped (the caller knows the count in advance).
+__device__ __forceinline__ void block_append(u32x2v* list, uint32_t* counter, uint32_t cap, bool pred, uint32_t key,
+                                             uint32_t idx)
+{
+    const uint64_t mask = __ballot(pred);
+    if (mask == 0) return;
+    const int leader = (int)__builtin_ctzll(mask);
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    uint32_t base = 0;
+    if ((int)lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+    if (pred) {
+        const uint32_t off =
+            base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (off < cap) {
+            u32x2v e;
+            e.x = key;
+            e.y = idx;
+            list[off] = e;
+        }
+    }
+}
 
 // Row max and error flag over the workgroup: wave reductions, then one
 // exchange through LDS.
@@ -662,7 +700,9 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     RaceQueue& rq = sh.u.r.rq[t / kWave];
     const uint32_t lane = (uint32_t)t & (kWave - 1);
     uint32_t qh = 0, qn = 0;  // ring head and fill, the same in every lane of the wave
-    u32x2v* const seg = sh.u.r.cand + (t / kWave) * kWaveCand;
+    using Sh = std::remove_reference_t<decltype(sh)>;
+    constexpr uint32_t kWaveC = Sh::kWaveCands;
+    u32x2v* const seg = sh.u.r.cand + (t / kWave) * kWaveC;
     uint32_t wn = 0;          // the wave's candidates, the same in every lane
     auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
         race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits, !has_cand);
@@ -680,7 +720,7 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             }
             if (__ballot(anyc)) {  // uniform: most of a row's groups hold no crossing-bin token
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wave_append(seg, wn, c[j], order_key(xs[j]), i0 + j);
+                for (int j = 0; j < 4; ++j) wave_append<kWaveC>(seg, wn, c[j], order_key(xs[j]), i0 + j);
             }
         }
     }, nofirst, xf);
@@ -698,14 +738,17 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     }
     most = uniform(most);
     n = uniform(n);
-    if (most <= (uint32_t)kWaveCand) {
+    phase_fact(p, b, kStampMode, st.mode);
+    phase_fact(p, b, kStampCands, n);
+    phase_fact(p, b, kStampMostWave, most);
+    if (most <= kWaveC) {
         // Pack the waves' segments into one list, in the race queues' space
         // (the race is over): every later visit then reads n entries.
         u32x2v* const list = (u32x2v*)sh.u.r.rq;
-        static_assert(sizeof(sh.u.r.rq) >= sizeof(u32x2v) * kRowCand, "packed list fits the race queues");
+        static_assert(sizeof(sh.u.r.rq) >= sizeof(u32x2v) * Sh::kCands, "packed list fits the race queues");
         __syncthreads();
-        for (uint32_t i = t; i < (uint32_t)kRowCand; i += kRowThreads) {
-            const uint32_t w = i / kWaveCand, k = i - w * kWaveCand;
+        for (uint32_t i = t; i < (uint32_t)Sh::kCands; i += kRowThreads) {
+            const uint32_t w = i / kWaveC, k = i - w * kWaveC;
             if (k < sh.wcand[w]) list[sh.wpre[w] + k] = sh.u.r.cand[i];
         }
         __syncthreads();
@@ -717,7 +760,41 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
                                      }
                                  },
                                  sh.rs);
-    } else {  // more candidates than a wave's segment holds: visit the row in global memory
+    } else if (n <= (uint32_t)Sh::kGatherCands) {
+        // Some wave found more candidates than its segment holds, but the
+        // whole race-pass area (segments and queues, free now) holds them
+        // all: one more read of the row gathers them there, and every later
+        // visit reads LDS.  The order of the list is the atomics' order; the
+        // resolver's sums, counts and maxima do not depend on it.
+        u32x2v* const list = (u32x2v*)&sh.u.r;
+        __syncthreads();
+        if (t == 0) sh.gather_n = 0;
+        __syncthreads();
+        stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
+            bool c[4];
+            bool anyc = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = xs[j] >= cand_lo && xs[j] < keep_lo;
+                anyc |= c[j];
+            }
+            if (__ballot(anyc)) {  // uniform
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    block_append(list, &sh.gather_n, (uint32_t)Sh::kGatherCands, c[j], order_key(xs[j]), i0 + j);
+            }
+        }, nofirst, xf);
+        __syncthreads();
+        const uint32_t ng = min(sh.gather_n, (uint32_t)Sh::kGatherCands);
+        resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
+                                 [&](auto&& fn) {
+                                     for (uint32_t i = t; i < ng; i += kRowThreads) {
+                                         const u32x2v c = list[i];
+                                         fn(c.x, c.y);
+                                     }
+                                 },
+                                 sh.rs);
+    } else {  // more candidates than LDS holds: visit the row in global memory
         resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
                                  [&](auto&& fn) {
                                      stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {

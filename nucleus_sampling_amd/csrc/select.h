@@ -73,10 +73,39 @@ __device__ __forceinline__ SelectResult select_level(Visit visit, ThrFn thr_of_t
     __syncthreads();
     for (int lvl = first; lvl < 4; ++lvl) {
         const int shift = 24 - 8 * lvl;
+        // Each thread sums a run of tokens with one digit in registers and
+        // adds it to the histogram when the digit changes; the last runs of
+        // a wave go in with one atomic when they share a digit.  Tied keys
+        // (a whole level in the crossing bin) would otherwise send every
+        // token's atomic to one LDS address.
+        uint32_t rd = 0;
+        uint64_t racc = 0;
         visit([&](uint32_t key, uint64_t w) {
-            if ((key & mask) == prefix)
-                atomicAdd((unsigned long long*)&sh.hist[(key >> shift) & 0xFFu], (unsigned long long)w);
+            if ((key & mask) == prefix) {
+                const uint32_t d = (key >> shift) & 0xFFu;
+                if (d != rd && racc) {
+                    atomicAdd((unsigned long long*)&sh.hist[rd], (unsigned long long)racc);
+                    racc = 0;
+                }
+                rd = d;
+                racc += w;
+            }
         });
+        {
+            const bool has = racc != 0;
+            const uint64_t hm = __ballot(has);
+            if (hm) {  // uniform
+                const int leader = (int)__builtin_ctzll(hm);
+                const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)rd, leader);
+                if (__ballot(has && rd != dl) == 0) {  // uniform: one digit for the whole wave
+                    const uint64_t tot = wave_reduce(racc, SumU64());
+                    if ((int)(t & (kWave - 1)) == leader)
+                        atomicAdd((unsigned long long*)&sh.hist[dl], (unsigned long long)tot);
+                } else if (has) {
+                    atomicAdd((unsigned long long*)&sh.hist[rd], (unsigned long long)racc);
+                }
+            }
+        }
         __syncthreads();
         if (t < kWave) {
             uint64_t h[4];

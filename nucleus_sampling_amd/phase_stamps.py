@@ -70,7 +70,7 @@ def main():
             else torch.from_numpy(w["logits"]))
     nbuf = max(2, -(-(512 * 2**20 + 1) // (host.numel() * host.element_size())) + 1)
     bufs = [host.to(dev) for _ in range(nbuf)]
-    stamps = torch.zeros((B, 8), dtype=torch.int64, device=dev)
+    stamps = torch.zeros((B, 16), dtype=torch.int64, device=dev)
     rc = L.nucleus_phase_stamps(stamps.data_ptr(), B)
     if rc != 0:
         raise SystemExit(f"nucleus_phase_stamps: {ns.strerror(rc)}")
@@ -83,7 +83,8 @@ def main():
                       want_probs=args.probs)
     torch.cuda.synchronize()
     L.nucleus_phase_stamps(None, 0)
-    st = stamps.cpu().numpy().view(np.uint64)
+    full = stamps.cpu().numpy().view(np.uint64)
+    st = full[:, :8]
     kept = r.keep_count.cpu().numpy()
     ph = row_phases(st)
     dense = kept > 8192
@@ -96,9 +97,15 @@ def main():
                      "median_dense_us": float(np.nanmedian(v[dense])) if np.isfinite(v[dense]).any() else None,
                      "max_us": float(np.nanmax(v)) if np.isfinite(v).any() else None,
                      "last_row_us": float(v[last]) if np.isfinite(v[last]) else None})
+    res_us = ph["resolver + outputs"]
+    slow = [int(i) for i in np.argsort(-np.nan_to_num(res_us, nan=-1.0))[:5]]
     res = {"workload": f"{w['name']}: B={B}, V={V} {w['dtype']}", "calls": args.calls, "probs": args.probs,
            "launch_span_us": span, "rows_keeping_more_than_8192": int(dense.sum()),
-           "last_row": {"row": last, "keep_count": int(kept[last])}, "phases": rows}
+           "last_row": {"row": last, "keep_count": int(kept[last])}, "phases": rows,
+           "slowest_resolvers": [{"row": i, "us": float(res_us[i]), "mode": int(full[i, 8]),
+                                  "candidates": int(full[i, 9]), "most_in_a_wave": int(full[i, 10]),
+                                  "keep_count": int(kept[i]), "T": float(w["temperature"][i]),
+                                  "p": float(w["top_p"][i])} for i in slow]}
     if args.json:
         print(json.dumps(res))
         return
@@ -112,6 +119,9 @@ def main():
     for r_ in rows:
         print(f"{r_['phase']:34s} {f(r_['median_us'])} {f(r_['median_dense_us'])} {f(r_['max_us'])} "
               f"{f(r_['last_row_us'])} ")
+    print("slowest resolvers: " + "; ".join(
+        f"row {s['row']} {s['us']:.1f} us (mode {s['mode']}, {s['candidates']} candidates, {s['most_in_a_wave']} in "
+        f"one wave, keeps {s['keep_count']}, T {s['T']:.2f}, p {s['p']:.4f})" for s in res["slowest_resolvers"]))
 
 
 if __name__ == "__main__":

@@ -51,10 +51,13 @@ def test_workspace_query(L):
     assert L.nucleus_workspace_bytes(4, 0, 0) == 0
     assert L.nucleus_workspace_bytes(4, 1 << 31, 0) == 0
     assert L.nucleus_workspace_bytes(4, 10, 7) == 0
-    # Small batches split rows (per-chunk slots); large ones run a workgroup
-    # per row and need nothing; the chunked-race flag needs per-row state and
-    # a candidate list.
-    assert L.nucleus_workspace_bytes(2, 8, 0) > 0
+    # Small batches of long rows split rows (per-chunk slots); others run a
+    # workgroup per row and need nothing; the chunked-race flag needs per-row
+    # state and a candidate list.
+    assert L.nucleus_workspace_bytes(2, 40000, 0) > 0
+    assert L.nucleus_workspace_bytes(2, 32768, 0) == 0 and L.nucleus_workspace_bytes(2, 8, 0) == 0
+    assert L.nucleus_workspace_bytes(96, 128256, 0) > 0 and L.nucleus_workspace_bytes(97, 128256, 0) == 0
+    assert L.nucleus_workspace_bytes(127, 40000, 0) > 0 and L.nucleus_workspace_bytes(128, 40000, 0) == 0
     assert L.nucleus_workspace_bytes(256, 128256, 0) == 0
     assert L.nucleus_workspace_bytes_for(256, 128256, 0, 1) == 0
     assert L.nucleus_workspace_bytes_for(256, 128256, 0, 4) >= 256 * (256 + 8192 * 8)
@@ -103,7 +106,7 @@ def test_host_side_argument_errors(L):
     assert _call(L, V=64 * 8192 + 1, opt=ctypes.byref(opt)) == EINVAL  # too long to split
     # The default path needs a workspace for these shapes.
     opt = ns._Options()
-    assert _call(L, opt=ctypes.byref(opt)) == -2
+    assert _call(L, V=40000, opt=ctypes.byref(opt)) == -2
 
 
 def test_empty_batch_launches_nothing(L):

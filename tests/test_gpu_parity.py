@@ -150,7 +150,7 @@ def test_split_rows_at_their_limit(dtype):
         _gpu(w1, path="split")
 
 
-@pytest.mark.parametrize("path", [None, "rows", "single"])
+@pytest.mark.parametrize("path", [None, "rows", "single", "split"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [1, 2, 3, 5, 63, 64, 65, 1023, 4097, 9999, 40001])
 def test_small_and_ragged_shapes(V, dtype, path):
@@ -164,7 +164,7 @@ def test_small_and_ragged_shapes(V, dtype, path):
     assert rep.ok(), rep.failures
 
 
-@pytest.mark.parametrize("path", [None, "rows", "single"])
+@pytest.mark.parametrize("path", [None, "rows", "single", "split"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_strided_unaligned_rows(dtype, path):
     """Rows whose starts are not 16-byte aligned take the scalar-load path."""
@@ -230,7 +230,7 @@ def _edge_batch():
         np.asarray(MP, np.float32)
 
 
-@pytest.mark.parametrize("path", [None, "rows", "single"])
+@pytest.mark.parametrize("path", [None, "rows", "single", "split"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_edge_rows(dtype, path):
     L, T, P, K, MP = _edge_batch()
@@ -328,10 +328,13 @@ def test_paths_agree_bit_for_bit(n):
 def test_crossing_bin_overflow(dtype):
     """Rows whose crossing bin holds more tokens than the resolver's list (one
     or two tied levels over 40,001 tokens) are resolved by re-reading the row;
-    results still match the oracle and the single-workgroup path."""
+    rows whose crossing bin overflows a wave's share of the race pass's list
+    but not the whole list (12,000 tied tokens; 15,000 distinct values inside
+    one bin) are gathered by one more read; results still match the oracle
+    and the single-workgroup path."""
     V = 40001
     rng = np.random.default_rng(5)
-    L = np.zeros((7, V), np.float32)
+    L = np.zeros((9, V), np.float32)
     L[1, rng.random(V) < 0.5] = 1.0            # two levels, ~20K tokens each
     L[2] = rng.integers(-1, 2, V)              # three levels
     L[3, :] = 0.25                             # one level
@@ -339,8 +342,12 @@ def test_crossing_bin_overflow(dtype):
     L[5, ::3] = -np.inf
     L[6] = rng.normal(0, 1, V)                 # 5000 tokens tied above the rest: a crossing bin
     L[6, rng.choice(V, 5000, replace=False)] = 2.5  # larger than LDS staging, within the list
-    T = np.asarray([1.0, 1.0, 0.5, 2.0, 1.0, 1.0, 1.0], np.float32)
-    P = np.asarray([0.5, 0.6, 0.95, 0.1, 0.5, 0.99, 0.3], np.float32)
+    L[7] = rng.normal(0, 1, V)
+    L[7, rng.choice(V, 12000, replace=False)] = 2.5  # one tied level: ~750 candidates a wave
+    L[8] = rng.normal(0, 1, V)
+    L[8, rng.choice(V, 15000, replace=False)] = 2.5 + rng.uniform(0, 1e-3, 15000)  # many levels in one bin
+    T = np.asarray([1.0, 1.0, 0.5, 2.0, 1.0, 1.0, 1.0, 1.0, 1.0], np.float32)
+    P = np.asarray([0.5, 0.6, 0.95, 0.1, 0.5, 0.99, 0.3, 0.3, 0.4], np.float32)
     B = len(T)
     w = dict(logits=workloads.f32_to_bf16_bits(L) if dtype == "bf16" else L, dtype=dtype, temperature=T, top_p=P,
              top_k=np.zeros(B, np.int32), min_p=np.zeros(B, np.float32), seed=77, B=B, V=V)
