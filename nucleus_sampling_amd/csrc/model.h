@@ -61,6 +61,7 @@ struct Lattice {
     double s;   // cells per logit unit: cell of x = floor(x * s); 0 when T = +inf
     double w;   // cell width in d units, 1/(s T); 0 when every token weighs the same
     double q;   // exp(-w), the weight ratio of neighbouring bin edges
+    double q32; // q^32 by five squarings
     float c0, c1, c2, c3;  // 2^31 * Taylor coefficients of exp(-f w)
 };
 
@@ -84,6 +85,10 @@ __device__ __forceinline__ Lattice make_lattice(float T)
     const double w = (T == INFINITY) ? 0.0 : 1.0 / (L.s * (double)T);
     L.w = w;
     L.q = exp(-w);
+    double q32 = L.q;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) q32 *= q32;
+    L.q32 = q32;
     L.c0 = (float)kFx;
     L.c1 = (float)(-w * kFx);
     L.c2 = (float)(w * w * 0.5 * kFx);
@@ -150,6 +155,7 @@ __device__ __forceinline__ Lattice uniform(const Lattice& a)
     L.s = uniform(a.s);
     L.w = uniform(a.w);
     L.q = uniform(a.q);
+    L.q32 = uniform(a.q32);
     L.c0 = uniform(a.c0);
     L.c1 = uniform(a.c1);
     L.c2 = uniform(a.c2);
@@ -202,18 +208,23 @@ __device__ __forceinline__ uint32_t bin_fx(const RowModel& r, float x)
     return cell_fx(r.L, f);
 }
 
-// Weight of bin j's upper edge, exp(-w)^j by binary powering (a fixed
-// sequence of at most 20 products, so every path computes the same double;
-// relative error below 1e-13).
+// Weight of bin j's upper edge (0 <= j < 1024), exp(-w)^j as
+// q^(j mod 32) * (q^32)^(j / 32) with q = exp(-w): two
+// independent five-step binary powerings (a fixed sequence of products, so
+// every path computes the same double; relative error below 1e-13).
+static_assert(kBins <= 1024, "edge_weight covers ten bits of bin index");
 __device__ __forceinline__ double edge_weight(const RowModel& r, int j)
 {
 #pragma clang fp contract(off)
-    double acc = 1.0, sq = r.L.q;
-    for (int k = j; k; k >>= 1) {
-        if (k & 1) acc *= sq;
-        sq *= sq;
+    double lo = 1.0, hi = 1.0, sl = r.L.q, sh = r.L.q32;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        lo = ((j >> k) & 1) ? lo * sl : lo;
+        hi = ((j >> (5 + k)) & 1) ? hi * sh : hi;
+        sl *= sl;
+        sh *= sh;
     }
-    return acc;
+    return hi * lo;
 }
 
 // Weight of a token at the common 2^-40 scale used when several bins meet
@@ -250,7 +261,7 @@ __device__ __forceinline__ double lane_read_f64(double v, int lane)
 
 // Decide how a row's cut is found from its merged histogram H (integer
 // weights) and C (counts of survivors per bin, only when k > 0).  H is
-// overwritten with the bin weights (doubles).  Must be called by all threads
+// overwritten (with the bin weights, as doubles, transposed).  Must be called by all threads
 // of one workgroup.
 //
 // Deterministic whatever the block size: the weight of bin j is
@@ -267,20 +278,38 @@ __device__ __forceinline__ Decision decide(const RowModel& r, uint64_t* H, uint3
     constexpr int PER = kBins / kWave;  // bins per lane
     __shared__ Decision dec;
     const int t = threadIdx.x;
+    // Bin weights, stored transposed over H's space: bin PER l + i (lane l's
+    // i-th) at W[i kWave + l], so that the first wave reads them without bank
+    // conflicts.  (Blocks of 256 or more threads: four bins a thread at most.)
     double* W = (double*)H;
-    for (int j = t; j < kBins; j += blockDim.x) W[j] = bin_weight(r, j, H[j]);
+    double wt[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = t + q * (int)blockDim.x;
+        wt[q] = j < kBins ? bin_weight(r, j, H[j]) : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = t + q * (int)blockDim.x;
+        if (j < kBins) W[(j % PER) * kWave + j / PER] = wt[q];
+    }
     __syncthreads();
     if (t < kWave) {
         const int lane = t;
-        // Lane totals (the searches below redo these sums bin by bin, in the
-        // same order, so they see the same values).
-        double run = 0.0;
+        // The lane's bins in registers, and its total (the searches below
+        // redo these sums bin by bin, in the same order, so they see the same
+        // values).
+        double wv[PER], pre[PER + 1];  // pre[i]: the lane's bins before its i-th, summed in order
         uint32_t crun = 0;
-#pragma unroll 4
+        pre[0] = 0.0;
+#pragma unroll
         for (int i = 0; i < PER; ++i) {
-            run += W[PER * lane + i];
+            wv[i] = W[i * kWave + lane];
+            pre[i + 1] = pre[i] + wv[i];
             crun += C ? C[PER * lane + i] : 0u;
         }
+        const double run = pre[PER];
         // Inclusive wave scans of the lane totals (a fixed order: doubling
         // steps in each 16-lane row, then the rows before), and the
         // inclusive value of the lane before.
@@ -317,23 +346,25 @@ __device__ __forceinline__ Decision decide(const RowModel& r, uint64_t* H, uint3
         } else {
             // top-p: the first non-empty bin whose running weight reaches
             // p * S (the last non-empty bin when rounding leaves none).
+            // Bin i of the lane has weight before + pre[i] above it and
+            // reaches the threshold with before + pre[i + 1]; the tests are
+            // independent, so they run side by side.
             const double thr = (double)p * S;
-            int first = PER, last = -1;
-            double above_first = 0.0, above_last = 0.0, acc = 0.0;
-#pragma unroll 4
+            uint32_t reach = 0, nonempty = 0;
+#pragma unroll
             for (int i = 0; i < PER; ++i) {
-                const double wi = W[PER * lane + i];
-                const double ab = i > 0 ? before + acc : before;  // weight of the bins before
-                acc += wi;
-                const bool nonempty = wi > 0.0;
-                if (first == PER && nonempty && before + acc >= thr) {
-                    first = i;
-                    above_first = ab;
-                }
-                if (nonempty) {
-                    last = i;
-                    above_last = ab;
-                }
+                const bool ne = wv[i] > 0.0;
+                nonempty |= ne ? 1u << i : 0u;
+                reach |= (ne && before + pre[i + 1] >= thr) ? 1u << i : 0u;
+            }
+            const int first = reach ? (int)__builtin_ctz(reach) : PER;
+            const int last = nonempty ? 31 - (int)__builtin_clz(nonempty) : -1;
+            double above_first = 0.0, above_last = 0.0;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const double ab = i > 0 ? before + pre[i] : before;  // weight of the bins before
+                above_first = i == first ? ab : above_first;
+                above_last = i == last ? ab : above_last;
             }
             const uint64_t mf = __ballot(first < PER);
             int L, i;
