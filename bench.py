@@ -255,6 +255,8 @@ def main():
     ap.add_argument("--no-prechain", action="store_true", help="skip timing the pre-chain")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="host seconds for the oracle baseline (three runs of a third each)")
+    ap.add_argument("--no-with-probs", action="store_true",
+                    help="skip timing the benchmark calls with the probabilities written out")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip timing the other workloads (small, ties, chain, flat)")
     ap.add_argument("--profile-steps", action="store_true", help="only run the timed loop (for rocprofv3)")
@@ -450,7 +452,7 @@ def main():
     # (out_probs, B x V fp32): the logits read once plus the probabilities
     # written once.
     with_probs = None
-    if args.path == "default":
+    if args.path == "default" and not args.no_with_probs:
         pout = ns.SampleResult(torch.empty(B, dtype=torch.int32, device=dev),
                                torch.empty(B, dtype=torch.int32, device=dev),
                                torch.empty((B, V), dtype=torch.float32, device=dev), None)
