@@ -246,26 +246,42 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
     stream_row<DT, NTL, NT>(p, rowp, f, [](float) {});
 }
 
-// Appends (key, idx) for the lanes with pred to the wave's own segment of an
-// LDS list (CAP entries); n, the same in every lane, counts the
-// wave's appends, those past the segment (dropped) included.  No atomics:
-// positions come from the lanes' ranks.
-template <uint32_t CAP>
-__device__ __forceinline__ void wave_append(u32x2v* seg, uint32_t& n, bool pred, uint32_t key, uint32_t idx)
+
+// Appends of the crossing-bin tokens of one 4-token group per lane to the
+// wave's own segment of an LDS list (CAP entries): one wave scan of the
+// lanes' counts gives every lane its places, lane by lane in order.  No
+// atomics.  wave_count4 returns the wave's total and the lane's offset;
+// wave_put4 writes from base + offset, dropping entries past CAP (the caller
+// counts them).
+template <int N>
+__device__ __forceinline__ uint32_t wave_count(const bool c[N], uint32_t& excl)
 {
-    const uint64_t mask = __ballot(pred);
-    if (mask == 0) return;
-    if (pred) {
-        const uint32_t off =
-            n + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        if (off < CAP) {
-            u32x2v e;
-            e.x = key;
-            e.y = idx;
-            seg[off] = e;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) cnt += (uint32_t)c[k];
+    uint32_t total;
+    const uint32_t incl = wave_inclusive_sum(cnt, total);
+    excl = incl - cnt;
+    return total;
+}
+
+__device__ __forceinline__ uint32_t wave_count4(const bool c[4], uint32_t& excl) { return wave_count<4>(c, excl); }
+
+template <uint32_t CAP>
+__device__ __forceinline__ void wave_put4(u32x2v* seg, uint32_t off, const bool c[4], const float xs[4], uint32_t i0)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (c[j]) {
+            if (off < CAP) {
+                u32x2v e;
+                e.x = order_key(xs[j]);
+                e.y = i0 + (uint32_t)j;
+                seg[off] = e;
+            }
+            ++off;
         }
     }
-    n += (uint32_t)__popcll(mask);
 }
 
 // Per-wave ring of 4-token groups holding at least one kept token: the race
@@ -376,10 +392,11 @@ __device__ __forceinline__ void race_queued(const Params& p, int64_t b, bool sco
 }
 
 // A wave's staging area for candidates bound for a row's list in global
-// memory: appends go to LDS (wave_append) and are flushed with one atomic
+// memory: appends go to LDS (wave_put4) and are flushed with one atomic
 // on the row's counter per kStage entries, instead of one per appending
 // group (a returning device atomic stalls the wave for a microsecond).
 constexpr int kStage = 256;
+static_assert(kStage >= 4 * kWave, "one wave step's candidates fit an emptied stage");
 
 __device__ __forceinline__ void stage_flush(u32x2v* stage, uint32_t& sn, uint32_t* counter,
                                             __amdgpu_buffer_rsrc_t list, uint32_t cap, uint32_t lane)
@@ -429,7 +446,7 @@ struct RowSharedPre : RowSharedT<kRowCandPre> {
 
 static_assert(sizeof(RowShared) <= 160 * 1024 && sizeof(RowSharedPre) <= 160 * 1024, "LDS of one workgroup");
 
-// wave_append into a list shared by the workgroup: one LDS atomic per wave
+// Appends into a list shared by the workgroup: one LDS atomic per wave
 // step reserves the places of the lanes with pred set.  Entries past cap are
 // dropped (the caller knows the count in advance).
 __device__ __forceinline__ void block_append(u32x2v* list, uint32_t* counter, uint32_t cap, bool pred, uint32_t key,
@@ -704,25 +721,42 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     constexpr uint32_t kWaveC = Sh::kWaveCands;
     u32x2v* const seg = sh.u.r.cand + (t / kWave) * kWaveC;
     uint32_t wn = 0;          // the wave's candidates, the same in every lane
+    // A group joins its wave's ring if it holds a surely kept token or a
+    // candidate; each drain races the kept tokens of its groups and appends
+    // their candidates with one wave scan for the two groups a lane holds
+    // (in a dense row nearly every wave step holds a candidate, and one scan
+    // a drain costs less than one per step).
+    const float push_lo = has_cand ? cand_lo : keep_lo;
     auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
         race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits, !has_cand);
+        if (has_cand) {  // uniform
+            bool c[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float x = xs[k >> 2][k & 3];
+                c[k] = active[k >> 2] && x >= cand_lo && x < keep_lo;
+            }
+            uint32_t excl;
+            const uint32_t tot = wave_count<8>(c, excl);
+            uint32_t off = wn + excl;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (c[k]) {
+                    if (off < kWaveC) {
+                        u32x2v e;
+                        e.x = order_key(xs[k >> 2][k & 3]);
+                        e.y = i0[k >> 2] + (uint32_t)(k & 3);
+                        seg[off] = e;
+                    }
+                    ++off;
+                }
+            }
+            wn += tot;
+        }
     };
     stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
-        const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
+        const bool any = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])) >= push_lo;
         wq_push(rq, qh, qn, lane, any, i0, xs, race);
-        if (has_cand) {
-            bool c[4];
-            bool anyc = false;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c[j] = xs[j] >= cand_lo && xs[j] < keep_lo;
-                anyc |= c[j];
-            }
-            if (__ballot(anyc)) {  // uniform: most of a row's groups hold no crossing-bin token
-#pragma unroll
-                for (int j = 0; j < 4; ++j) wave_append<kWaveC>(seg, wn, c[j], order_key(xs[j]), i0 + j);
-            }
-        }
     }, nofirst, xf);
     if (qn) wq_drain(rq, qh, qn, lane, qn, race);
     if (lane == 0) sh.wcand[t / kWave] = wn;
@@ -951,10 +985,19 @@ __global__ __launch_bounds__(kRaceThreads, 4) void race_kernel(Params p, RowWork
         const bool any = (xs[0] >= keep_lo) | (xs[1] >= keep_lo) | (xs[2] >= keep_lo) | (xs[3] >= keep_lo);
         wq_push(rq, qh, qn, lane, any, i0, xs, race);
         if (has_cand) {
+            bool c[4];
+            bool anyc = false;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (sn + kWave > (uint32_t)kStage) stage_flush(stage, sn, &ps->cand_n, rk, kCap, lane);
-                wave_append<kStage>(stage, sn, xs[j] >= cand_lo && xs[j] < keep_lo, order_key(xs[j]), i0 + j);
+                c[j] = xs[j] >= cand_lo && xs[j] < keep_lo;
+                anyc |= c[j];
+            }
+            if (__ballot(anyc)) {  // uniform: most groups hold no crossing-bin token
+                uint32_t excl;
+                const uint32_t tot = wave_count4(c, excl);  // at most 4 kWave = kStage
+                if (sn + tot > (uint32_t)kStage) stage_flush(stage, sn, &ps->cand_n, rk, kCap, lane);
+                wave_put4<kStage>(stage, sn + excl, c, xs, i0);
+                sn += tot;
             }
         }
     };
