@@ -571,51 +571,58 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             sh.u.h.hm[i] = 0;
             sh.u.h.hc[i] = 0;
         }
+    // lmax takes the IEEE maximum, which propagates NaN, so one test of each
+    // thread's max after the pass finds NaN and +inf: no per-token flag.
     float lmax = -INFINITY;
-    int bad = 0;
     bool win = false;     // uniform: the window is placed
     double base = 0.0;    // uniform: cell held by window slot 0 (slot k holds cell base - k)
     uint64_t tail_w = 0;  // the second pass: tokens of the last bin, summed in registers
     uint32_t tail_c = 0;
-    stream_row_x<DT, false, kRowThreads>(
-        p, rowp,
-        [&](uint32_t, const float* xs) {
+    // The pass, for rows with (COUNTS) and without top-k counts: the test
+    // stays out of the per-token code.
+    auto pass1 = [&](auto counts_tag) __attribute__((always_inline)) {
+        constexpr bool COUNTS = decltype(counts_tag)::value;
+        stream_row_x<DT, false, kRowThreads>(
+            p, rowp,
+            [&](uint32_t, const float* xs) {
+                lmax = __builtin_elementwise_maximum(
+                    lmax, __builtin_elementwise_maximum(__builtin_elementwise_maximum(xs[0], xs[1]),
+                                                        __builtin_elementwise_maximum(xs[2], xs[3])));
+                if (win) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float v = xs[j];
-                bad |= !(v < INFINITY);  // NaN or +inf
-                lmax = fmaxf(lmax, v);
-            }
-            if (win) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    // Branch-free.  A token in the window goes to its cell's
-                    // slot; every other value goes to this thread's own slot
-                    // past the window, which folds into the last bin: the
-                    // tail below the window (all of it in the last bin), a
-                    // token above the window (the row is then redone, bins
-                    // straight from the model), and NaN / -inf, which are no
-                    // tokens and add zero (cell_fx gives them 0; any slot
-                    // the saturating conversion picks for them is in range).
-                    const float v = xs[j];
-                    float f;
-                    const double k = base - lattice_cell(lat, v, f);
-                    const uint32_t fx = cell_fx(lat, f);
-                    const uint32_t ki = (uint32_t)cvt_i32_sat(k);  // k is a whole number
-                    const uint32_t slot = ki < (uint32_t)kWin ? ki : (uint32_t)(kWin + t);
-                    atomicAdd((unsigned long long*)&sh.u.h.hm[slot], (unsigned long long)fx);
-                    if (counts) atomicAdd(&sh.u.h.hc[slot], v > -INFINITY ? 1u : 0u);
+                    for (int j = 0; j < 4; ++j) {
+                        // Branch-free.  A token in the window goes to its
+                        // cell's slot; every other value goes to this
+                        // thread's own slot past the window, which folds
+                        // into the last bin: the tail below the window (all
+                        // of it in the last bin), a token above the window
+                        // (the row is then redone, bins straight from the
+                        // model), and NaN / -inf, which are no tokens and add
+                        // zero (cell_fx gives them 0; any slot the saturating
+                        // conversion picks for them is in range).
+                        const float v = xs[j];
+                        float f;
+                        const double k = base - lattice_cell(lat, v, f);
+                        const uint32_t fx = cell_fx(lat, f);
+                        const uint32_t ki = (uint32_t)cvt_i32_sat(k);  // k is a whole number
+                        const uint32_t slot = ki < (uint32_t)kWin ? ki : (uint32_t)(kWin + t);
+                        atomicAdd((unsigned long long*)&sh.u.h.hm[slot], (unsigned long long)fx);
+                        if constexpr (COUNTS) atomicAdd(&sh.u.h.hc[slot], v > -INFINITY ? 1u : 0u);
+                    }
                 }
-            }
-        },
-        [&](float mx) {
-            if (!fused) return;
-            const float m1 = block_reduce<kRowThreads>(mx, MaxF(), sh.redf);
-            base = uniform(floor((double)m1 * lat.s) + (double)kWinHead);
-            // Cells are exact integers in double below 2^53; a provisional
-            // max of -inf or +inf leaves the window unplaced.
-            win = m1 > -INFINITY && fabs(base) < 0x1p50;
-        }, xf);
+            },
+            [&](float mx) {
+                if (!fused) return;
+                const float m1 = block_reduce<kRowThreads>(mx, MaxF(), sh.redf);
+                base = uniform(floor((double)m1 * lat.s) + (double)kWinHead);
+                // Cells are exact integers in double below 2^53; a provisional
+                // max of -inf or +inf leaves the window unplaced.
+                win = m1 > -INFINITY && fabs(base) < 0x1p50;
+            }, xf);
+    };
+    if (counts) pass1(std::true_type());
+    else pass1(std::false_type());
+    int bad = !(lmax < INFINITY);  // NaN or +inf
     block_extremes<kRowThreads>(lmax, bad, sh.redf, sh.redi);
     phase_stamp(p, b, kStampPass1);
     RowState st;
