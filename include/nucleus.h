@@ -329,7 +329,9 @@ int nucleus_stream_read(const void* buf, size_t bytes, uint64_t* sink, void* str
  * fused histogram), 2 bins ready, 3 bin decision, 4 classification, 5 race
  * pass, 6 resolver and outputs, 7 probability pass (or its skip); and facts
  * about the row: buf[16 b + 8] its mode after the bin decision, + 9 the
- * crossing-bin candidates the race pass found, + 10 the most any wave found.
+ * crossing-bin candidates listed after the race pass, + 10 the marked runs
+ * of 4-token groups that hold them (a run is one group in rows of up to
+ * 2^18 groups).
  * A phase a row does not run leaves its word as it was.  buf: device,
  * [rows, 16] uint64, 8-byte aligned, owned by the caller and valid for every
  * later call; NULL turns the recording off.  Calls that overlap race on buf.

@@ -48,8 +48,8 @@ enum StampPoint {
     kStampResolve = 6,   // resolver done, outputs written
     kStampProbs = 7,     // probability pass done (or skipped)
     kStampMode = 8,      // (facts) the row's mode after decide
-    kStampCands = 9,     // crossing-bin candidates found in pass 3
-    kStampMostWave = 10, // the most any wave found
+    kStampCands = 9,     // crossing-bin candidates listed after pass 3
+    kStampMarked = 10,   // marked runs of groups holding them
 };
 
 #ifdef NUCLEUS_PHASE_STAMPS

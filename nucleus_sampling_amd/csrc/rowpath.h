@@ -9,8 +9,9 @@
 //     2  only for min-p rows (whose survivors depend on the max), or when
 //        the histogram window missed the max: the histogram again
 //   then either finishes the row itself (one more pass racing the surely kept
-//   tokens and gathering the crossing bin's tokens into LDS, the resolver,
-//   and an optional probability pass), or publishes the row's state for
+//   tokens and marking the 4-token groups that hold a crossing-bin token,
+//   whose tokens are then read again into an LDS list; the resolver; an
+//   optional probability pass), or publishes the row's state for
 //   race_kernel.
 //
 // race_kernel: the race pass split into items of 2048 tokens, each raced by
@@ -38,11 +39,14 @@ namespace nucleus {
 
 constexpr int kRowThreads = 1024;  // 16 waves: one workgroup per CU
 constexpr int kRowUnroll = 8;      // 4-token groups per thread whose loads are in flight together
-// Crossing-bin candidates held in LDS during the race pass, in one segment
-// per wave: 9728 (608 a wave) in the plain kernel, 6144 (384 a wave) beside
-// the pre-chain's LDS tables.
-constexpr int kRowCand = 9728;
-constexpr int kRowCandPre = 6144;
+// Crossing-bin candidates.  The race pass only marks, in an LDS bitmap, the
+// 4-token groups (or runs of 2^k groups in rows of more than 2^18 groups)
+// that hold one; after the race the marked groups are listed (up to
+// kRowMarked of them), read again and their candidates listed in LDS.
+constexpr int kMarkWords = 2048;             // bitmap words: 65536 bits
+constexpr int kMarkBits = kMarkWords * 32;
+constexpr int kRowMarked = 8192;             // marked groups listed in LDS
+constexpr int kRelist = 4;                   // marked groups a thread reads at once
 constexpr int kWin = 4096;         // cells of the fused pass's LDS histogram window
 constexpr int kWinHead = kWin - kBins;  // cells the window reaches above the provisional max
 constexpr int kRaceQueue = 256;    // per-wave ring of 4-token groups waiting for the race
@@ -247,12 +251,11 @@ __device__ __forceinline__ void stream_row(const Params& p, const void* rowp, F&
 }
 
 
-// Appends of the crossing-bin tokens of one 4-token group per lane to the
-// wave's own segment of an LDS list (CAP entries): one wave scan of the
-// lanes' counts gives every lane its places, lane by lane in order.  No
-// atomics.  wave_count4 returns the wave's total and the lane's offset;
-// wave_put4 writes from base + offset, dropping entries past CAP (the caller
-// counts them).
+// Appends of the crossing-bin tokens of one 4-token group per lane to a
+// wave's own LDS area (CAP entries): one wave scan of the lanes' counts gives
+// every lane its places, lane by lane in order.  No atomics.  wave_count4
+// returns the wave's total and the lane's offset; wave_put4 writes from
+// base + offset, dropping entries past CAP (the caller counts them).
 template <int N>
 __device__ __forceinline__ uint32_t wave_count(const bool c[N], uint32_t& excl)
 {
@@ -412,64 +415,35 @@ __device__ __forceinline__ void stage_flush(u32x2v* stage, uint32_t& sn, uint32_
     sn = 0;
 }
 
-template <int CANDS>
-struct RowSharedT {
-    static constexpr int kCands = CANDS;                          // candidates in the race pass
-    static constexpr int kWaveCands = CANDS / (kRowThreads / kWave);  // each wave's segment of them
+struct RowShared {
     union {
         struct {  // histogram: a window of lattice cells (bins from decide on)
             uint64_t hm[kWin + kRowThreads];  // the window, then one slot per thread
             uint32_t hc[kWin + kRowThreads];
         } h;
-        struct {  // race pass
-            u32x2v cand[CANDS];
+        struct {  // race pass; afterwards the candidate list takes the queues' space
             RaceQueue rq[kRowThreads / kWave];
+            uint32_t marks[kMarkWords];       // groups holding a crossing-bin token
+            uint32_t marked[kRowMarked];      // the marked groups, listed
         } r;
         float factor[kBins];  // probability pass
     } u;
     ResolveShared rs;
     float redf[kMaxWaves];
     int redi[kMaxWaves];
-    uint32_t wcand[kMaxWaves];  // candidates each wave found (past its segment too)
-    uint32_t wpre[kMaxWaves];   // candidates of the waves before
+    uint64_t scan[kMaxWaves];
     uint32_t sstar_bits;  // best exact race score found so far in the workgroup (bits of a float >= 0)
-    uint32_t gather_n;    // candidates gathered by the second look at the row
-    // After the race pass the whole race-pass area holds one candidate list.
-    static constexpr int kGatherCands = (int)(sizeof(decltype(u.r)) / sizeof(u32x2v));
+    uint32_t cand_n;      // candidates listed
 };
 
-using RowShared = RowSharedT<kRowCand>;
+// Candidates the LDS list holds after the race (in the race queues' space).
+constexpr int kRowCands = (int)(sizeof(RaceQueue) * (kRowThreads / kWave) / sizeof(u32x2v));
 
-struct RowSharedPre : RowSharedT<kRowCandPre> {
+struct RowSharedPre : RowShared {
     PreShared pre;
 };
 
 static_assert(sizeof(RowShared) <= 160 * 1024 && sizeof(RowSharedPre) <= 160 * 1024, "LDS of one workgroup");
-
-// Appends into a list shared by the workgroup: one LDS atomic per wave
-// step reserves the places of the lanes with pred set.  Entries past cap are
-// dropped (the caller knows the count in advance).
-__device__ __forceinline__ void block_append(u32x2v* list, uint32_t* counter, uint32_t cap, bool pred, uint32_t key,
-                                             uint32_t idx)
-{
-    const uint64_t mask = __ballot(pred);
-    if (mask == 0) return;
-    const int leader = (int)__builtin_ctzll(mask);
-    const uint32_t lane = threadIdx.x & (kWave - 1);
-    uint32_t base = 0;
-    if ((int)lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-    base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
-    if (pred) {
-        const uint32_t off =
-            base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        if (off < cap) {
-            u32x2v e;
-            e.x = key;
-            e.y = idx;
-            list[off] = e;
-        }
-    }
-}
 
 // Row max and error flag over the workgroup: wave reductions, then one
 // exchange through LDS.
@@ -712,11 +686,23 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
         return;
     }
 
-    // ---- pass 3: race the surely kept tokens; the crossing bin's tokens go to LDS
+    // ---- pass 3: race the surely kept tokens; mark the groups that hold a
+    // crossing-bin token
     const bool scored = st.mode != kModeGreedy;
     const bool has_cand = cand_lo < keep_lo;
     const float c_log2e = model.invT * 1.4426950408889634f;
-    if (t == 0) sh.sstar_bits = 0;
+    const uint32_t V = (uint32_t)p.V;
+    const uint32_t ngroups = (V + 3) >> 2;
+    // Groups per mark: 1, or the power of two that fits the row in kMarkBits.
+    uint32_t mshift = 0;
+    while ((ngroups - 1) >> mshift >= (uint32_t)kMarkBits) ++mshift;
+    const uint32_t nmarks = ((ngroups - 1) >> mshift) + 1;
+    __syncthreads();  // every thread is past decide: the histogram's space is free
+    for (uint32_t i = t; i < (uint32_t)kMarkWords; i += kRowThreads) sh.u.r.marks[i] = 0;
+    if (t == 0) {
+        sh.sstar_bits = 0;
+        sh.cand_n = 0;
+    }
     __syncthreads();
     RaceAcc acc;
     acc.init();
@@ -724,41 +710,25 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     RaceQueue& rq = sh.u.r.rq[t / kWave];
     const uint32_t lane = (uint32_t)t & (kWave - 1);
     uint32_t qh = 0, qn = 0;  // ring head and fill, the same in every lane of the wave
-    using Sh = std::remove_reference_t<decltype(sh)>;
-    constexpr uint32_t kWaveC = Sh::kWaveCands;
-    u32x2v* const seg = sh.u.r.cand + (t / kWave) * kWaveC;
-    uint32_t wn = 0;          // the wave's candidates, the same in every lane
     // A group joins its wave's ring if it holds a surely kept token or a
-    // candidate; each drain races the kept tokens of its groups and appends
-    // their candidates with one wave scan for the two groups a lane holds
-    // (in a dense row nearly every wave step holds a candidate, and one scan
-    // a drain costs less than one per step).
+    // candidate; each drain races the kept tokens of its groups and marks
+    // those holding a candidate (one LDS or per such group: in a dense row
+    // nearly every drain holds a candidate, and a mark costs far less than
+    // placing each candidate in a list).
     const float push_lo = has_cand ? cand_lo : keep_lo;
     auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
         race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits, !has_cand);
         if (has_cand) {  // uniform
-            bool c[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float x = xs[k >> 2][k & 3];
-                c[k] = active[k >> 2] && x >= cand_lo && x < keep_lo;
-            }
-            uint32_t excl;
-            const uint32_t tot = wave_count<8>(c, excl);
-            uint32_t off = wn + excl;
+            for (int h = 0; h < 2; ++h) {
+                bool c = false;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                if (c[k]) {
-                    if (off < kWaveC) {
-                        u32x2v e;
-                        e.x = order_key(xs[k >> 2][k & 3]);
-                        e.y = i0[k >> 2] + (uint32_t)(k & 3);
-                        seg[off] = e;
-                    }
-                    ++off;
+                for (int j = 0; j < 4; ++j) c |= (xs[h][j] >= cand_lo) & (xs[h][j] < keep_lo);
+                if (active[h] && c) {
+                    const uint32_t m = (i0[h] >> 2) >> mshift;
+                    atomicOr(&sh.u.r.marks[m >> 5], 1u << (m & 31));
                 }
             }
-            wn += tot;
         }
     };
     stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
@@ -766,76 +736,105 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
         wq_push(rq, qh, qn, lane, any, i0, xs, race);
     }, nofirst, xf);
     if (qn) wq_drain(rq, qh, qn, lane, qn, race);
-    if (lane == 0) sh.wcand[t / kWave] = wn;
-    acc = block_race<kRowThreads>(acc, sh.rs);  // (its barriers publish wcand)
+    acc = block_race<kRowThreads>(acc, sh.rs);  // (its barriers publish the marks)
     phase_stamp(p, b, kStampPass3);
-    uint32_t most = 0, n = 0;
+
+    // The marked groups, listed in order by one scan of the marks' counts.
+    uint32_t nmarked = 0;
+    if (has_cand) {  // uniform
+        constexpr int kWordsPerThread = kMarkWords / kRowThreads;
+        uint32_t words[kWordsPerThread];
+        uint32_t cnt = 0;
 #pragma unroll
-    for (int w = 0; w < kRowThreads / kWave; ++w) {
-        const uint32_t c = sh.wcand[w];
-        if (t == w) sh.wpre[w] = n;
-        most = max(most, c);
-        n += c;
-    }
-    most = uniform(most);
-    n = uniform(n);
-    phase_fact(p, b, kStampMode, st.mode);
-    phase_fact(p, b, kStampCands, n);
-    phase_fact(p, b, kStampMostWave, most);
-    if (most <= kWaveC) {
-        // Pack the waves' segments into one list, in the race queues' space
-        // (the race is over): every later visit then reads n entries.
-        u32x2v* const list = (u32x2v*)sh.u.r.rq;
-        static_assert(sizeof(sh.u.r.rq) >= sizeof(u32x2v) * Sh::kCands, "packed list fits the race queues");
-        __syncthreads();
-        for (uint32_t i = t; i < (uint32_t)Sh::kCands; i += kRowThreads) {
-            const uint32_t w = i / kWaveC, k = i - w * kWaveC;
-            if (k < sh.wcand[w]) list[sh.wpre[w] + k] = sh.u.r.cand[i];
+        for (int k = 0; k < kWordsPerThread; ++k) {
+            const uint32_t wi = (uint32_t)t * kWordsPerThread + k;
+            words[k] = wi * 32 < nmarks ? sh.u.r.marks[wi] : 0u;
+            cnt += (uint32_t)__builtin_popcount(words[k]);
+        }
+        uint32_t off = (uint32_t)block_exclusive_sum<kRowThreads>(cnt, sh.scan);
+#pragma unroll
+        for (int w = 0; w < kRowThreads / kWave; ++w) nmarked += (uint32_t)sh.scan[w];  // the waves' totals
+        nmarked = uniform(nmarked);
+#pragma unroll
+        for (int k = 0; k < kWordsPerThread; ++k) {
+            uint32_t w = words[k];
+            while (w) {
+                const uint32_t m = ((uint32_t)t * kWordsPerThread + k) * 32 + (uint32_t)__builtin_ctz(w);
+                w &= w - 1u;
+                if (off < (uint32_t)kRowMarked) sh.u.r.marked[off] = m;
+                ++off;
+            }
         }
         __syncthreads();
-        resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
-                                 [&](auto&& fn) {
-                                     for (uint32_t i = t; i < n; i += kRowThreads) {
-                                         const u32x2v c = list[i];
-                                         fn(c.x, c.y);
-                                     }
-                                 },
-                                 sh.rs);
-    } else if (n <= (uint32_t)Sh::kGatherCands) {
-        // Some wave found more candidates than its segment holds, but the
-        // whole race-pass area (segments and queues, free now) holds them
-        // all: one more read of the row gathers them there, and every later
-        // visit reads LDS.  The order of the list is the atomics' order; the
-        // resolver's sums, counts and maxima do not depend on it.
-        u32x2v* const list = (u32x2v*)&sh.u.r;
-        __syncthreads();
-        if (t == 0) sh.gather_n = 0;
-        __syncthreads();
-        stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
-            bool c[4];
-            bool anyc = false;
+    }
+    phase_fact(p, b, kStampMode, st.mode);
+    phase_fact(p, b, kStampMarked, nmarked);
+    const uint32_t per_mark = 1u << mshift;
+    u32x2v* const list = (u32x2v*)sh.u.r.rq;
+    bool listed = false;  // uniform: the candidates fit the LDS list
+    if (nmarked <= (uint32_t)kRowMarked && nmarked * per_mark <= (uint32_t)(4 * kRowCands)) {
+        // Read the marked groups again (kRelist loads in flight per thread) and
+        // list their candidates; every lane runs the same number of steps,
+        // so the placing may use wave operations.
+        const uint32_t total = nmarked * per_mark;
+        for (uint32_t base = 0; base < total; base += kRelist * kRowThreads) {
+            float x[kRelist][4];
+            uint32_t g[kRelist];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                c[j] = xs[j] >= cand_lo && xs[j] < keep_lo;
-                anyc |= c[j];
+            for (int u = 0; u < kRelist; ++u) {
+                const uint32_t k = base + (uint32_t)u * kRowThreads + (uint32_t)t;
+                g[u] = k < total ? (sh.u.r.marked[k >> mshift] << mshift) + (k & (per_mark - 1)) : ngroups;
+                load4<DT>(rowp, (int64_t)min(g[u], ngroups) << 2, V, p.vec_in, x[u]);  // -inf past V
             }
-            if (__ballot(anyc)) {  // uniform
+            // One wave scan of the lanes' counts and one LDS atomic a wave
+            // place the candidates.
+            bool c[kRelist][4];
+            uint32_t cnt = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    block_append(list, &sh.gather_n, (uint32_t)Sh::kGatherCands, c[j], order_key(xs[j]), i0 + j);
+            for (int u = 0; u < kRelist; ++u) {
+                xf(g[u] << 2, x[u]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    c[u][j] = g[u] < ngroups && x[u][j] >= cand_lo && x[u][j] < keep_lo;
+                    cnt += (uint32_t)c[u][j];
+                }
             }
-        }, nofirst, xf);
+            uint32_t tot;
+            const uint32_t incl = wave_inclusive_sum(cnt, tot);
+            uint32_t at = 0;
+            if (lane == 0 && tot) at = atomicAdd(&sh.cand_n, tot);
+            uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)at, 0) + incl - cnt;
+#pragma unroll
+            for (int u = 0; u < kRelist; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (c[u][j]) {
+                        if (off < (uint32_t)kRowCands) {
+                            u32x2v e;
+                            e.x = order_key(x[u][j]);
+                            e.y = (g[u] << 2) + (uint32_t)j;
+                            list[off] = e;
+                        }
+                        ++off;
+                    }
+                }
+        }
         __syncthreads();
-        const uint32_t ng = min(sh.gather_n, (uint32_t)Sh::kGatherCands);
-        resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
-                                 [&](auto&& fn) {
-                                     for (uint32_t i = t; i < ng; i += kRowThreads) {
-                                         const u32x2v c = list[i];
-                                         fn(c.x, c.y);
-                                     }
-                                 },
-                                 sh.rs);
-    } else {  // more candidates than LDS holds: visit the row in global memory
+        const uint32_t n = uniform(sh.cand_n);
+        phase_fact(p, b, kStampCands, n);
+        if (n <= (uint32_t)kRowCands) {
+            resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
+                                     [&](auto&& fn) {
+                                         for (uint32_t i = t; i < n; i += kRowThreads) {
+                                             const u32x2v c = list[i];
+                                             fn(c.x, c.y);
+                                         }
+                                     },
+                                     sh.rs);
+            listed = true;
+        }
+    }
+    if (!listed) {  // more candidates than LDS holds: visit the row in global memory
         resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
                                  [&](auto&& fn) {
                                      stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
@@ -859,7 +858,6 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     const LogNorm ln = log_norm(model, st);
     float* prow = p.out_probs ? p.out_probs + b * p.V : nullptr;
     float* lrow = p.out_logprobs ? p.out_logprobs + b * p.V : nullptr;
-    const uint32_t V = (uint32_t)p.V;
     stream_row_x<DT, true, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
         float q[4];
         if (prow) {

@@ -103,7 +103,7 @@ def main():
            "launch_span_us": span, "rows_keeping_more_than_8192": int(dense.sum()),
            "last_row": {"row": last, "keep_count": int(kept[last])}, "phases": rows,
            "slowest_resolvers": [{"row": i, "us": float(res_us[i]), "mode": int(full[i, 8]),
-                                  "candidates": int(full[i, 9]), "most_in_a_wave": int(full[i, 10]),
+                                  "candidates": int(full[i, 9]), "marked_groups": int(full[i, 10]),
                                   "keep_count": int(kept[i]), "T": float(w["temperature"][i]),
                                   "p": float(w["top_p"][i])} for i in slow]}
     if args.json:
@@ -120,8 +120,8 @@ def main():
         print(f"{r_['phase']:34s} {f(r_['median_us'])} {f(r_['median_dense_us'])} {f(r_['max_us'])} "
               f"{f(r_['last_row_us'])} ")
     print("slowest resolvers: " + "; ".join(
-        f"row {s['row']} {s['us']:.1f} us (mode {s['mode']}, {s['candidates']} candidates, {s['most_in_a_wave']} in "
-        f"one wave, keeps {s['keep_count']}, T {s['T']:.2f}, p {s['p']:.4f})" for s in res["slowest_resolvers"]))
+        f"row {s['row']} {s['us']:.1f} us (mode {s['mode']}, {s['candidates']} candidates in {s['marked_groups']} "
+        f"marked groups, keeps {s['keep_count']}, T {s['T']:.2f}, p {s['p']:.4f})" for s in res["slowest_resolvers"]))
 
 
 if __name__ == "__main__":

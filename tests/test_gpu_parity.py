@@ -326,12 +326,13 @@ def test_paths_agree_bit_for_bit(n):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_crossing_bin_overflow(dtype):
-    """Rows whose crossing bin holds more tokens than the resolver's list (one
-    or two tied levels over 40,001 tokens) are resolved by re-reading the row;
-    rows whose crossing bin overflows a wave's share of the race pass's list
-    but not the whole list (12,000 tied tokens; 15,000 distinct values inside
-    one bin) are gathered by one more read; results still match the oracle
-    and the single-workgroup path."""
+    """Rows whose crossing bin holds more tokens than the resolver's LDS list
+    (one or two tied levels over 40,001 tokens; 12,000 tied tokens in ~7,600
+    marked groups) or whose marked groups outnumber the list of marked groups
+    (15,000 distinct values inside one bin, ~8,500 groups) are resolved by
+    visiting the row in global memory; a 5,000-token crossing bin (~4,100
+    marked groups) is listed from the marks; results still match the oracle
+    and the single-workgroup and chunked-race paths bit for bit."""
     V = 40001
     rng = np.random.default_rng(5)
     L = np.zeros((9, V), np.float32)
