@@ -47,6 +47,10 @@ constexpr int kMarkWords = 2048;             // bitmap words: 65536 bits
 constexpr int kMarkBits = kMarkWords * 32;
 constexpr int kRowMarked = 8192;             // marked groups listed in LDS
 constexpr int kRelist = 4;                   // marked groups a thread reads at once
+// Min-p rows: the first pass keeps every token within T ln(1/min_p) of the
+// max of the first tokens loaded, in per-wave LDS segments of kMinpSeg.
+constexpr int kMinpSeg = 256;
+constexpr int kMinpCands = kRowMarked / 2;   // their candidates, listed in the marked-group list's space
 constexpr int kWin = 4096;         // cells of the fused pass's LDS histogram window
 constexpr int kWinHead = kWin - kBins;  // cells the window reaches above the provisional max
 constexpr int kRaceQueue = 256;    // per-wave ring of 4-token groups waiting for the race
@@ -434,6 +438,7 @@ struct RowShared {
     uint64_t scan[kMaxWaves];
     uint32_t sstar_bits;  // best exact race score found so far in the workgroup (bits of a float >= 0)
     uint32_t cand_n;      // candidates listed
+    uint32_t mcnt[kMaxWaves];  // min-p rows: tokens each wave kept in the first pass
 };
 
 // Candidates the LDS list holds after the race (in the race queues' space).
@@ -444,6 +449,8 @@ struct RowSharedPre : RowShared {
 };
 
 static_assert(sizeof(RowShared) <= 160 * 1024 && sizeof(RowSharedPre) <= 160 * 1024, "LDS of one workgroup");
+static_assert((kWin + kRowThreads - kBins) * sizeof(uint64_t) >= (size_t)kMinpSeg * (kRowThreads / kWave) * sizeof(u32x2v),
+              "min-p segments fit the histogram window past the bins");
 
 // Row max and error flag over the workgroup: wave reductions, then one
 // exchange through LDS.
@@ -539,6 +546,20 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     const RowParams rp = row_params(p, b);
     const bool counts = rp.K > 0;
     const bool fused = hist_before_max(rp, want_probs);
+    // Min-p rows (their survivors depend on the max, so they cannot bin in
+    // the first pass) keep, in per-wave LDS segments past the bins, every
+    // token at or above list_lo = (max of the first tokens loaded) + T ln(min_p)
+    // rounded down: the survivors are among them, since the row max is at
+    // least that first max.  Greedy rows (T <= 0) keep every token at or
+    // above that first max: the row max's ties are among them.  When every
+    // segment holds its tokens, the histogram and the race pass read the
+    // segments instead of the row.
+    const bool greedy_row = rp.T <= 0.0f;
+    const bool minp_list =
+        !PUBLISH && !fused && (greedy_row || (rp.T > 0.0f && rp.T < INFINITY && rp.MP > 0.0f));  // uniform
+    float list_lo = INFINITY;  // uniform
+    uint32_t mn = 0;           // tokens this wave kept, the same in every lane
+    u32x2v* const mseg = (u32x2v*)&sh.u.h.hm[kBins] + (t / kWave) * kMinpSeg;
     const Lattice lat = uniform(make_lattice(fused ? rp.T : 1.0f));
     if (fused)
         for (int i = t; i < kWin + kRowThreads; i += kRowThreads) {
@@ -558,10 +579,37 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
         constexpr bool COUNTS = decltype(counts_tag)::value;
         stream_row_x<DT, false, kRowThreads>(
             p, rowp,
-            [&](uint32_t, const float* xs) {
+            [&](uint32_t i0, const float* xs) {
                 lmax = __builtin_elementwise_maximum(
                     lmax, __builtin_elementwise_maximum(__builtin_elementwise_maximum(xs[0], xs[1]),
                                                         __builtin_elementwise_maximum(xs[2], xs[3])));
+                if (minp_list) {  // uniform
+                    bool c[4];
+                    bool any = false;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        c[j] = xs[j] >= list_lo;
+                        any |= c[j];
+                    }
+                    if (__ballot(any)) {  // uniform
+                        uint32_t excl;
+                        const uint32_t tot = wave_count<4>(c, excl);
+                        uint32_t off = mn + excl;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            if (c[j]) {
+                                if (off < (uint32_t)kMinpSeg) {
+                                    u32x2v e;
+                                    e.x = __float_as_uint(xs[j]);
+                                    e.y = i0 + (uint32_t)j;
+                                    mseg[off] = e;
+                                }
+                                ++off;
+                            }
+                        }
+                        mn += tot;
+                    }
+                }
                 if (win) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -586,8 +634,20 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
                 }
             },
             [&](float mx) {
-                if (!fused) return;
+                if (!fused && !minp_list) return;
                 const float m1 = block_reduce<kRowThreads>(mx, MaxF(), sh.redf);
+                if (minp_list) {
+                    if (greedy_row) {
+                        list_lo = uniform(m1);
+                        return;
+                    }
+                    const float mpc = rp.MP > 1.0f ? 1.0f : rp.MP;
+                    const double c = (double)m1 + (double)rp.T * log((double)mpc);
+                    float lo = (float)c;
+                    if ((double)lo > c) lo = nextafterf(lo, -INFINITY);
+                    list_lo = uniform(lo);
+                    return;
+                }
                 base = uniform(floor((double)m1 * lat.s) + (double)kWinHead);
                 // Cells are exact integers in double below 2^53; a provisional
                 // max of -inf or +inf leaves the window unplaced.
@@ -597,7 +657,15 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
     if (counts) pass1(std::true_type());
     else pass1(std::false_type());
     int bad = !(lmax < INFINITY);  // NaN or +inf
-    block_extremes<kRowThreads>(lmax, bad, sh.redf, sh.redi);
+    if (minp_list && (t & (kWave - 1)) == 0) sh.mcnt[t / kWave] = mn;
+    block_extremes<kRowThreads>(lmax, bad, sh.redf, sh.redi);  // (its barriers publish mcnt)
+    bool use_list = false;  // uniform: the min-p segments hold every token at or above list_lo
+    if (minp_list) {
+        uint32_t most = 0;
+#pragma unroll
+        for (int w = 0; w < kRowThreads / kWave; ++w) most = max(most, sh.mcnt[w]);
+        use_list = uniform(most) <= (uint32_t)kMinpSeg;
+    }
     phase_stamp(p, b, kStampPass1);
     RowState st;
     st.mode = uniform(first_mode(bad != 0, lmax, rp.T, rp.P, rp.MP, rp.K, want_probs));
@@ -645,21 +713,26 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
             // registers and added once per wave instead of by LDS atomics.
             tail_w = 0;
             tail_c = 0;
-            stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t, const float* xs) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (survives(model, xs[j])) {
-                        const Binned bt = bin_token(model, xs[j]);
-                        if (bt.j == (uint32_t)(kBins - 1)) {
-                            tail_w += bt.fx;
-                            tail_c += 1;
-                        } else {
-                            atomicAdd((unsigned long long*)&H[bt.j], (unsigned long long)bt.fx);
-                            if (counts) atomicAdd(&C[bt.j], 1u);
-                        }
+            auto bin_one = [&](float x) __attribute__((always_inline)) {
+                if (survives(model, x)) {
+                    const Binned bt = bin_token(model, x);
+                    if (bt.j == (uint32_t)(kBins - 1)) {
+                        tail_w += bt.fx;
+                        tail_c += 1;
+                    } else {
+                        atomicAdd((unsigned long long*)&H[bt.j], (unsigned long long)bt.fx);
+                        if (counts) atomicAdd(&C[bt.j], 1u);
                     }
                 }
-            }, nofirst, xf);
+            };
+            if (use_list) {  // uniform: every survivor is in the waves' segments
+                for (uint32_t i = (uint32_t)lane; i < mn; i += kWave) bin_one(__uint_as_float(mseg[i].x));
+            } else {
+                stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t, const float* xs) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bin_one(xs[j]);
+                }, nofirst, xf);
+            }
             tail_w = wave_reduce(tail_w, SumU64());
             tail_c = wave_reduce(tail_c, SumU32());
             if (lane == 0 && tail_c) {
@@ -686,164 +759,237 @@ __global__ __launch_bounds__(kRowThreads, 1) void row_kernel(Params p, RowWork r
         return;
     }
 
-    // ---- pass 3: race the surely kept tokens; mark the groups that hold a
-    // crossing-bin token
-    const bool scored = st.mode != kModeGreedy;
-    const bool has_cand = cand_lo < keep_lo;
-    const float c_log2e = model.invT * 1.4426950408889634f;
     const uint32_t V = (uint32_t)p.V;
-    const uint32_t ngroups = (V + 3) >> 2;
-    // Groups per mark: 1, or the power of two that fits the row in kMarkBits.
-    uint32_t mshift = 0;
-    while ((ngroups - 1) >> mshift >= (uint32_t)kMarkBits) ++mshift;
-    const uint32_t nmarks = ((ngroups - 1) >> mshift) + 1;
-    __syncthreads();  // every thread is past decide: the histogram's space is free
-    for (uint32_t i = t; i < (uint32_t)kMarkWords; i += kRowThreads) sh.u.r.marks[i] = 0;
-    if (t == 0) {
-        sh.sstar_bits = 0;
-        sh.cand_n = 0;
-    }
-    __syncthreads();
-    RaceAcc acc;
-    acc.init();
-    float sstar = 0.0f;
-    RaceQueue& rq = sh.u.r.rq[t / kWave];
-    const uint32_t lane = (uint32_t)t & (kWave - 1);
-    uint32_t qh = 0, qn = 0;  // ring head and fill, the same in every lane of the wave
-    // A group joins its wave's ring if it holds a surely kept token or a
-    // candidate; each drain races the kept tokens of its groups and marks
-    // those holding a candidate (one LDS or per such group: in a dense row
-    // nearly every drain holds a candidate, and a mark costs far less than
-    // placing each candidate in a list).
-    const float push_lo = has_cand ? cand_lo : keep_lo;
-    auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
-        race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits, !has_cand);
-        if (has_cand) {  // uniform
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                bool c = false;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) c |= (xs[h][j] >= cand_lo) & (xs[h][j] < keep_lo);
-                if (active[h] && c) {
-                    const uint32_t m = (i0[h] >> 2) >> mshift;
-                    atomicOr(&sh.u.r.marks[m >> 5], 1u << (m & 31));
-                }
-            }
-        }
-    };
-    stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
-        const bool any = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])) >= push_lo;
-        wq_push(rq, qh, qn, lane, any, i0, xs, race);
-    }, nofirst, xf);
-    if (qn) wq_drain(rq, qh, qn, lane, qn, race);
-    acc = block_race<kRowThreads>(acc, sh.rs);  // (its barriers publish the marks)
-    phase_stamp(p, b, kStampPass3);
-
-    // The marked groups, listed in order by one scan of the marks' counts.
-    uint32_t nmarked = 0;
-    if (has_cand) {  // uniform
-        constexpr int kWordsPerThread = kMarkWords / kRowThreads;
-        uint32_t words[kWordsPerThread];
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int k = 0; k < kWordsPerThread; ++k) {
-            const uint32_t wi = (uint32_t)t * kWordsPerThread + k;
-            words[k] = wi * 32 < nmarks ? sh.u.r.marks[wi] : 0u;
-            cnt += (uint32_t)__builtin_popcount(words[k]);
-        }
-        uint32_t off = (uint32_t)block_exclusive_sum<kRowThreads>(cnt, sh.scan);
-#pragma unroll
-        for (int w = 0; w < kRowThreads / kWave; ++w) nmarked += (uint32_t)sh.scan[w];  // the waves' totals
-        nmarked = uniform(nmarked);
-#pragma unroll
-        for (int k = 0; k < kWordsPerThread; ++k) {
-            uint32_t w = words[k];
-            while (w) {
-                const uint32_t m = ((uint32_t)t * kWordsPerThread + k) * 32 + (uint32_t)__builtin_ctz(w);
-                w &= w - 1u;
-                if (off < (uint32_t)kRowMarked) sh.u.r.marked[off] = m;
-                ++off;
-            }
-        }
+    if (use_list) {  // uniform
+        // ---- pass 3 of a min-p or greedy row from its segments: every kept
+        // token and every candidate is there.  Kept tokens are raced one by one; the
+        // candidates are placed in one list (one wave scan and one LDS atomic
+        // per wave step) in the marked-group list's space, which neither the
+        // segments nor the bins use.
+        const uint32_t lane = (uint32_t)t & (kWave - 1);
+        u32x2v* const clist = (u32x2v*)sh.u.r.marked;
+        static_assert(sizeof(sh.u.r.marked) >= sizeof(u32x2v) * kMinpCands, "candidate list fits");
+        if (t == 0) sh.cand_n = 0;
         __syncthreads();
-    }
-    phase_fact(p, b, kStampMode, st.mode);
-    phase_fact(p, b, kStampMarked, nmarked);
-    const uint32_t per_mark = 1u << mshift;
-    u32x2v* const list = (u32x2v*)sh.u.r.rq;
-    bool listed = false;  // uniform: the candidates fit the LDS list
-    if (nmarked <= (uint32_t)kRowMarked && nmarked * per_mark <= (uint32_t)(4 * kRowCands)) {
-        // Read the marked groups again (kRelist loads in flight per thread) and
-        // list their candidates; every lane runs the same number of steps,
-        // so the placing may use wave operations.
-        const uint32_t total = nmarked * per_mark;
-        for (uint32_t base = 0; base < total; base += kRelist * kRowThreads) {
-            float x[kRelist][4];
-            uint32_t g[kRelist];
-#pragma unroll
-            for (int u = 0; u < kRelist; ++u) {
-                const uint32_t k = base + (uint32_t)u * kRowThreads + (uint32_t)t;
-                g[u] = k < total ? (sh.u.r.marked[k >> mshift] << mshift) + (k & (per_mark - 1)) : ngroups;
-                load4<DT>(rowp, (int64_t)min(g[u], ngroups) << 2, V, p.vec_in, x[u]);  // -inf past V
-            }
-            // One wave scan of the lanes' counts and one LDS atomic a wave
-            // place the candidates.
-            bool c[kRelist][4];
-            uint32_t cnt = 0;
-#pragma unroll
-            for (int u = 0; u < kRelist; ++u) {
-                xf(g[u] << 2, x[u]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    c[u][j] = g[u] < ngroups && x[u][j] >= cand_lo && x[u][j] < keep_lo;
-                    cnt += (uint32_t)c[u][j];
-                }
-            }
-            uint32_t tot;
-            const uint32_t incl = wave_inclusive_sum(cnt, tot);
-            uint32_t at = 0;
-            if (lane == 0 && tot) at = atomicAdd(&sh.cand_n, tot);
-            uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)at, 0) + incl - cnt;
-#pragma unroll
-            for (int u = 0; u < kRelist; ++u)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (c[u][j]) {
-                        if (off < (uint32_t)kRowCands) {
-                            u32x2v e;
-                            e.x = order_key(x[u][j]);
-                            e.y = (g[u] << 2) + (uint32_t)j;
-                            list[off] = e;
-                        }
-                        ++off;
+        RaceAcc acc;
+        acc.init();
+        for (uint32_t base = 0; base < mn; base += kWave) {  // uniform in the wave
+            const uint32_t i = base + lane;
+            bool c = false;
+            uint32_t key = 0, idx = 0;
+            if (i < mn) {
+                const u32x2v e = mseg[i];
+                const float x = __uint_as_float(e.x);
+                key = order_key(x);
+                idx = e.y;
+                if (x >= keep_lo) {
+                    if (greedy_row) {  // uniform: every kept token scores 1, so the lowest index wins
+                        const uint64_t pk = race_pack(1.0f, idx);
+                        acc.best = pk > acc.best ? pk : acc.best;
+                        acc.count += 1;
+                        acc.minkey = key < acc.minkey ? key : acc.minkey;
+                    } else {
+                        race_one(p, b, model, key, idx, acc);
                     }
                 }
+                c = x >= cand_lo && x < keep_lo;
+            }
+            uint32_t tot;
+            const uint32_t incl = wave_inclusive_sum((uint32_t)c, tot);
+            uint32_t at = 0;
+            if (lane == 0 && tot) at = atomicAdd(&sh.cand_n, tot);
+            const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)at, 0) + incl - (uint32_t)c;
+            if (c && off < (uint32_t)kMinpCands) {
+                u32x2v e;
+                e.x = key;
+                e.y = idx;
+                clist[off] = e;
+            }
         }
-        __syncthreads();
+        acc = block_race<kRowThreads>(acc, sh.rs);  // (its barriers publish the list)
+        phase_stamp(p, b, kStampPass3);
         const uint32_t n = uniform(sh.cand_n);
+        phase_fact(p, b, kStampMode, st.mode);
         phase_fact(p, b, kStampCands, n);
-        if (n <= (uint32_t)kRowCands) {
+        if (n <= (uint32_t)kMinpCands) {
             resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
                                      [&](auto&& fn) {
-                                         for (uint32_t i = t; i < n; i += kRowThreads) {
-                                             const u32x2v c = list[i];
-                                             fn(c.x, c.y);
+                                         for (uint32_t k = t; k < n; k += kRowThreads) {
+                                             const u32x2v e = clist[k];
+                                             fn(e.x, e.y);
                                          }
                                      },
                                      sh.rs);
-            listed = true;
-        }
-    }
-    if (!listed) {  // more candidates than LDS holds: visit the row in global memory
-        resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
-                                 [&](auto&& fn) {
-                                     stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
+        } else {  // more candidates than the list holds: visit the row in global memory
+            resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
+                                     [&](auto&& fn) {
+                                         stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
 #pragma unroll
-                                         for (int j = 0; j < 4; ++j)
-                                             if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), i0 + j);
-                                     }, nofirst, xf);
-                                 },
-                                 sh.rs);
+                                             for (int j = 0; j < 4; ++j)
+                                                 if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), i0 + j);
+                                         }, nofirst, xf);
+                                     },
+                                     sh.rs);
+        }
+    } else {
+        // ---- pass 3: race the surely kept tokens; mark the groups that hold a
+        // crossing-bin token
+        const bool scored = st.mode != kModeGreedy;
+        const bool has_cand = cand_lo < keep_lo;
+        const float c_log2e = model.invT * 1.4426950408889634f;
+        const uint32_t ngroups = (V + 3) >> 2;
+        // Groups per mark: 1, or the power of two that fits the row in kMarkBits.
+        uint32_t mshift = 0;
+        while ((ngroups - 1) >> mshift >= (uint32_t)kMarkBits) ++mshift;
+        const uint32_t nmarks = ((ngroups - 1) >> mshift) + 1;
+        __syncthreads();  // every thread is past decide: the histogram's space is free
+        for (uint32_t i = t; i < (uint32_t)kMarkWords; i += kRowThreads) sh.u.r.marks[i] = 0;
+        if (t == 0) {
+            sh.sstar_bits = 0;
+            sh.cand_n = 0;
+        }
+        __syncthreads();
+        RaceAcc acc;
+        acc.init();
+        float sstar = 0.0f;
+        RaceQueue& rq = sh.u.r.rq[t / kWave];
+        const uint32_t lane = (uint32_t)t & (kWave - 1);
+        uint32_t qh = 0, qn = 0;  // ring head and fill, the same in every lane of the wave
+        // A group joins its wave's ring if it holds a surely kept token or a
+        // candidate; each drain races the kept tokens of its groups and marks
+        // those holding a candidate (one LDS or per such group: in a dense row
+        // nearly every drain holds a candidate, and a mark costs far less than
+        // placing each candidate in a list).
+        const float push_lo = has_cand ? cand_lo : keep_lo;
+        auto race = [&](const uint32_t* i0, const float (*xs)[4], const bool* active) __attribute__((always_inline)) {
+            race_queued(p, b, scored, model, c_log2e, keep_lo, i0, xs, active, acc, sstar, &sh.sstar_bits, !has_cand);
+            if (has_cand) {  // uniform
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    bool c = false;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) c |= (xs[h][j] >= cand_lo) & (xs[h][j] < keep_lo);
+                    if (active[h] && c) {
+                        const uint32_t m = (i0[h] >> 2) >> mshift;
+                        atomicOr(&sh.u.r.marks[m >> 5], 1u << (m & 31));
+                    }
+                }
+            }
+        };
+        stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
+            const bool any = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])) >= push_lo;
+            wq_push(rq, qh, qn, lane, any, i0, xs, race);
+        }, nofirst, xf);
+        if (qn) wq_drain(rq, qh, qn, lane, qn, race);
+        acc = block_race<kRowThreads>(acc, sh.rs);  // (its barriers publish the marks)
+        phase_stamp(p, b, kStampPass3);
+
+        // The marked groups, listed in order by one scan of the marks' counts.
+        uint32_t nmarked = 0;
+        if (has_cand) {  // uniform
+            constexpr int kWordsPerThread = kMarkWords / kRowThreads;
+            uint32_t words[kWordsPerThread];
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int k = 0; k < kWordsPerThread; ++k) {
+                const uint32_t wi = (uint32_t)t * kWordsPerThread + k;
+                words[k] = wi * 32 < nmarks ? sh.u.r.marks[wi] : 0u;
+                cnt += (uint32_t)__builtin_popcount(words[k]);
+            }
+            uint32_t off = (uint32_t)block_exclusive_sum<kRowThreads>(cnt, sh.scan);
+#pragma unroll
+            for (int w = 0; w < kRowThreads / kWave; ++w) nmarked += (uint32_t)sh.scan[w];  // the waves' totals
+            nmarked = uniform(nmarked);
+#pragma unroll
+            for (int k = 0; k < kWordsPerThread; ++k) {
+                uint32_t w = words[k];
+                while (w) {
+                    const uint32_t m = ((uint32_t)t * kWordsPerThread + k) * 32 + (uint32_t)__builtin_ctz(w);
+                    w &= w - 1u;
+                    if (off < (uint32_t)kRowMarked) sh.u.r.marked[off] = m;
+                    ++off;
+                }
+            }
+            __syncthreads();
+        }
+        phase_fact(p, b, kStampMode, st.mode);
+        phase_fact(p, b, kStampMarked, nmarked);
+        const uint32_t per_mark = 1u << mshift;
+        u32x2v* const list = (u32x2v*)sh.u.r.rq;
+        bool listed = false;  // uniform: the candidates fit the LDS list
+        if (nmarked <= (uint32_t)kRowMarked && nmarked * per_mark <= (uint32_t)(4 * kRowCands)) {
+            // Read the marked groups again (kRelist loads in flight per thread) and
+            // list their candidates; every lane runs the same number of steps,
+            // so the placing may use wave operations.
+            const uint32_t total = nmarked * per_mark;
+            for (uint32_t base = 0; base < total; base += kRelist * kRowThreads) {
+                float x[kRelist][4];
+                uint32_t g[kRelist];
+#pragma unroll
+                for (int u = 0; u < kRelist; ++u) {
+                    const uint32_t k = base + (uint32_t)u * kRowThreads + (uint32_t)t;
+                    g[u] = k < total ? (sh.u.r.marked[k >> mshift] << mshift) + (k & (per_mark - 1)) : ngroups;
+                    load4<DT>(rowp, (int64_t)min(g[u], ngroups) << 2, V, p.vec_in, x[u]);  // -inf past V
+                }
+                // One wave scan of the lanes' counts and one LDS atomic a wave
+                // place the candidates.
+                bool c[kRelist][4];
+                uint32_t cnt = 0;
+#pragma unroll
+                for (int u = 0; u < kRelist; ++u) {
+                    xf(g[u] << 2, x[u]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        c[u][j] = g[u] < ngroups && x[u][j] >= cand_lo && x[u][j] < keep_lo;
+                        cnt += (uint32_t)c[u][j];
+                    }
+                }
+                uint32_t tot;
+                const uint32_t incl = wave_inclusive_sum(cnt, tot);
+                uint32_t at = 0;
+                if (lane == 0 && tot) at = atomicAdd(&sh.cand_n, tot);
+                uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)at, 0) + incl - cnt;
+#pragma unroll
+                for (int u = 0; u < kRelist; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (c[u][j]) {
+                            if (off < (uint32_t)kRowCands) {
+                                u32x2v e;
+                                e.x = order_key(x[u][j]);
+                                e.y = (g[u] << 2) + (uint32_t)j;
+                                list[off] = e;
+                            }
+                            ++off;
+                        }
+                    }
+            }
+            __syncthreads();
+            const uint32_t n = uniform(sh.cand_n);
+            phase_fact(p, b, kStampCands, n);
+            if (n <= (uint32_t)kRowCands) {
+                resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
+                                         [&](auto&& fn) {
+                                             for (uint32_t i = t; i < n; i += kRowThreads) {
+                                                 const u32x2v c = list[i];
+                                                 fn(c.x, c.y);
+                                             }
+                                         },
+                                         sh.rs);
+                listed = true;
+            }
+        }
+        if (!listed) {  // more candidates than LDS holds: visit the row in global memory
+            resolve_row<kRowThreads>(p, b, model, rp, st, acc, cl,
+                                     [&](auto&& fn) {
+                                         stream_row_x<DT, false, kRowThreads>(p, rowp, [&](uint32_t i0, const float* xs) {
+#pragma unroll
+                                             for (int j = 0; j < 4; ++j)
+                                                 if (xs[j] >= cand_lo && xs[j] < keep_lo) fn(order_key(xs[j]), i0 + j);
+                                         }, nofirst, xf);
+                                     },
+                                     sh.rs);
+        }
     }
     write_outputs(p, b, st);
     phase_stamp(p, b, kStampResolve);
