@@ -397,3 +397,62 @@ def test_logprobs_and_row_seeds(n):
         other = _gpu_dev(w, lg=lg, want_probs=True, seeds=seeds, want_logprobs=True, path=path)
         for f in ("token", "keep_count", "min_kept_logit", "probs", "logprobs"):
             assert _same_bits(getattr(first, f), getattr(other, f)), (path, f)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_minp_and_greedy_row_lists(dtype):
+    """Min-p and greedy rows read their tokens near the max from LDS lists
+    the first pass keeps (every token at or above the first tokens' max plus
+    T ln(min_p); greedy: that max), and fall back to reading the row again
+    when some wave's list overflows.  Rows for both: peaked rows whose max
+    lies early or late in the row; near-flat rows where most tokens are
+    within T ln(1/min_p) of the max (overflow); a greedy row of one level
+    (every token tied at the max: overflow) and greedy rows whose max sits in
+    the last token or ties between the first and last.  Every row against
+    the oracle, probabilities included, and bit for bit against the
+    single-workgroup and chunked-race paths."""
+    rng = np.random.default_rng(31)
+    V = 65536 + 12
+    rows, T, P, K, MP = [], [], [], [], []
+
+    def add(x, t=1.0, p=0.9, k=0, mp=0.05):
+        rows.append(np.asarray(x, np.float32))
+        T.append(t)
+        P.append(p)
+        K.append(k)
+        MP.append(mp)
+
+    base = rng.normal(0, 3, V).astype(np.float32)
+    add(base)                                             # list
+    late = base.copy()
+    late[-3] = 40.0
+    add(late)                                             # max in the last tile: first max far below it
+    early = base.copy()
+    early[5] = 40.0
+    add(early, mp=0.5)
+    add(base, t=0.7, k=50)
+    add(base, t=2.0, p=1.0, mp=0.01)                      # every survivor kept
+    add(rng.normal(0, 0.01, V), mp=0.05)                  # near flat: overflow, row read again
+    add(np.linspace(1.0, 0.0, V), t=1.0, mp=0.001)        # overflow
+    add(base, t=0.0)                                      # greedy
+    add(np.ones(V), t=0.0)                                # greedy, one level: overflow
+    g = base.copy()
+    g[-1] = 50.0
+    add(g, t=-1.0)                                        # greedy, max at the last token
+    g2 = base.copy()
+    g2[0] = g2[-1] = 50.0
+    add(g2, t=0.0)                                        # greedy tie: lowest index wins
+    L = np.stack(rows)
+    w = dict(logits=workloads.f32_to_bf16_bits(L) if dtype == "bf16" else L, dtype=dtype,
+             temperature=np.asarray(T, np.float32), top_p=np.asarray(P, np.float32),
+             top_k=np.asarray(K, np.int32), min_p=np.asarray(MP, np.float32), seed=5, B=len(T), V=V)
+    B = len(T)
+    say(f"min-p and greedy row lists {dtype} B={B} V={V}")
+    a = _gpu(w, want_probs=True, prob_rows=range(B))
+    rep, _ = oracle_and_compare(w, *a[:3], gpu_probs=a[3], prob_rows=list(range(B)))
+    say(f"min-p and greedy row lists {dtype}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+    for path in ("single", "rows"):
+        b = _gpu(w, want_probs=True, prob_rows=range(B), path=path)
+        assert all(np.array_equal(np.asarray(x).view(np.uint32), np.asarray(y).view(np.uint32))
+                   for x, y in zip(a, b)), path
